@@ -1,0 +1,63 @@
+"""The oracle pins must catch plausible mistakes: each case below plants one
+mistake in a copy of oracle/pisa_oracle.c (never in the original), builds the
+copy with gcc and runs tests/test_oracle_pins.py against it, which must fail."""
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "pisa_oracle.c")
+
+# (name, text in the original, replacement)
+MUTANTS = [
+    ("eligibility_strict", "if (A[k] * span <= t)", "if (A[k] * span < t)"),
+    ("leaf_mean_over_C", "lev1[i * d + e] = s / (double)(hi - lo);", "lev1[i * d + e] = s / (double)C;"),
+    ("node_mean_over_g", "dst[i * d + e] = s / (double)(hi - lo);", "dst[i * d + e] = s / (double)g;"),
+    ("no_scale", "double scale = 1.0 / sqrt((double)P->d);\n    if (l == 1)",
+     "double scale = 1.0;\n    if (l == 1)"),
+    ("lse_is_max", "return m + log(s);", "return m;"),
+    ("tie_higher_index", "return (x->i < y->i) ? -1 : (x->i > y->i);",
+     "return (x->i > y->i) ? -1 : (x->i < y->i);"),
+    ("no_previous_block", "if (c >= 1) cand[nc++] = (c - 1) / den;", ""),
+    ("group_mean", "u += orc_lse_score(P, P->item_b[item], h, q, l, i);",
+     "u += orc_lse_score(P, P->item_b[item], h, q, l, i) / G;"),
+    ("drop_last_child", "int64_t lo = i * P->g, hi = i * P->g + P->g < P->M[l - 1] ? i * P->g + P->g : P->M[l - 1];",
+     "int64_t lo = i * P->g, hi = i * P->g + P->g - 1 < P->M[l - 1] ? i * P->g + P->g - 1 : P->M[l - 1];"),
+    ("forced_outside_budget", "int keep = Kt - nF;\n            nI = 0;", "int keep = Kt;\n            nI = 0;"),
+    ("keep_all_strict", "if (nA <= Kt) {", "if (nA < Kt) {"),
+    ("bsa_unnormalised", "S[k].u += exp(z[k] - lz);", "S[k].u += z[k];"),
+    ("attn_mask_self", "if (P->causal && j > t) continue;", "if (P->causal && j >= t) continue;"),
+    ("wrong_children", "int64_t lo = I[k] * P->g;", "int64_t lo = I[k] * P->g + 1;"),
+    ("transposed_operand", "for (int e = 0; e < d; e++) s += (double)q[e] * k[e];",
+     "for (int e = 0; e < d; e++) s += (double)q[e] * k[d - 1 - e];"),
+    ("ascending_scores", "if (x->u > y->u) return -1;\n    if (x->u < y->u) return 1;",
+     "if (x->u < y->u) return -1;\n    if (x->u > y->u) return 1;"),
+]
+
+
+def _run(m, tmp):
+    name, old, new = m
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    path = os.path.join(tmp, name + ".c")
+    lib = os.path.join(tmp, name + ".so")
+    open(path, "w").write(src.replace(old, new))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
+                    path, "-o", lib, "-lm"], check=True)
+    env = dict(os.environ, PISA_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+def test_every_planted_mistake_is_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        with ThreadPoolExecutor(max_workers=4) as ex:
+            results = list(ex.map(lambda m: _run(m, tmp), MUTANTS))
+    survivors = [n for n, rc in results if rc == 0]
+    assert not survivors, "mutants not caught by the pins: %s" % survivors

@@ -1,0 +1,441 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle (oracle/pisa_oracle.c) against one of:
+  * closed forms worked by hand from the definitions (tests/golden/hand_examples.json);
+  * special cases that reduce to a library routine (scipy logsumexp / softmax,
+    torch scaled_dot_product_attention, numpy means over raw keys);
+  * invariants the method guarantees (bounds of eq 19-20, forced set of
+    appendix B, the Jensen sandwich of appendix A.1, causality).
+All citations refer to "Block Sparse Attention with Log-Linear Complexity".
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp, softmax
+
+import oracle
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))
+e = math.e
+
+
+def ev(expr):
+    return float(eval(expr, {"math": math, "e": e}))
+
+
+def _w1_pyr():
+    w = GOLD["w1"]
+    K = np.array(w["keys"], np.float32).reshape(1, w["N"], 1, w["d"])
+    return oracle.Pyramid(K, w["N"], w["C"], w["g"]), np.array(w["q"], np.float32)
+
+
+# --------------------------------------------------------------------------
+# Hand-worked closed forms (section 3.2, section 3.1, appendix B, appendix A.1)
+# --------------------------------------------------------------------------
+
+def test_w1_levels_and_summaries():
+    w = GOLD["w1"]
+    pyr, _ = _w1_pyr()
+    assert pyr.M == w["levels"]
+    for l, vals in w["summaries"].items():
+        got = pyr.level(int(l)).ravel()
+        np.testing.assert_allclose(got, [ev(v) for v in vals], rtol=0, atol=1e-15)
+
+
+def test_w1_scores():
+    pyr, q = _w1_pyr()
+    for s in GOLD["w1"]["scores"]:
+        got = oracle.score(pyr, q, 0, 0, s["level"], s["node"])
+        assert got == pytest.approx(ev(s["value"]), abs=1e-13)
+
+
+def test_w1_noncausal_routes_and_exhaustive_miss():
+    pyr, q = _w1_pyr()
+    for case in GOLD["w1"]["noncausal_routes"]:
+        r = oracle.route(pyr, q.reshape(1, 1, 1), [0], [case["t"]], case["K_top"], causal=False)
+        assert r["idx"][0, 0].tolist() == case["idx"]
+        np.testing.assert_allclose(r["score"][0, 0], [ev(x) for x in case["score"]], atol=1e-13)
+    b = oracle.bsa(pyr, q.reshape(1, 1, 1), [0], [7], 1, causal=False)
+    assert b["idx"][0, 0].tolist() == GOLD["w1"]["exhaustive_k1"]
+
+
+def test_w2_forced_policy():
+    w = GOLD["w2"]
+    K = np.array(w["keys"], np.float32).reshape(1, w["N"], 1, w["d"])
+    pyr = oracle.Pyramid(K, w["N"], w["C"], w["g"])
+    q = np.array(w["q"], np.float32).reshape(1, 1, 1)
+    for case in w["causal_routes"]:
+        r = oracle.route(pyr, q, [0], [case["t"]], case["K_top"], causal=True)
+        assert r["idx"][0, 0].tolist() == case["idx"], case["note"]
+        kept = [s for i, s in zip(r["idx"][0, 0], r["score"][0, 0]) if i >= 0]
+        assert all(math.isinf(s) and s > 0 for s in kept)
+
+
+def test_w3_jensen_equality_case():
+    pyr, q = _w1_pyr()
+    for n in GOLD["w3"]["nodes"]:
+        s = oracle.score(pyr, q, 0, 0, n["level"], n["node"])
+        F_hat = s - math.log(2)
+        assert F_hat == pytest.approx(ev(n["F_hat"]), abs=1e-13)
+        assert ev(n["mean_logit"]) <= F_hat + 1e-13 <= ev(n["F_q"]) + 2e-13
+
+
+@pytest.mark.parametrize("case", GOLD["walks"]["cases"], ids=lambda c: "N%d" % c["N"])
+def test_structural_walk(case):
+    rng = np.random.default_rng(7)
+    N, C, g, Kt = case["N"], case["C"], case["g"], case["K_top"]
+    d, H = 16, 1
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    Q = rng.standard_normal((1, H, d)).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    r = oracle.route(pyr, Q, [0], [case["t"]], Kt, causal=True, trace=True)
+    for l, (nA, ns) in case["per_level"].items():
+        assert r["trace"][0, 0, int(l)].tolist() == [nA, ns], "level %s" % l
+
+
+# --------------------------------------------------------------------------
+# Pyramid: closed forms on perfect trees, the unweighted tail rule (eq 15)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("C,g,k", [(4, 2, 5), (16, 4, 3), (8, 3, 3)])
+def test_perfect_tree_summaries_are_raw_means(C, g, k):
+    rng = np.random.default_rng(1)
+    N, H, d = C * g ** k, 2, 5
+    K = rng.standard_normal((2, N, H, d)).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    assert pyr.L == k + 1
+    for l in range(1, pyr.L + 1):
+        span = C * g ** (l - 1)
+        lev = pyr.level(l)
+        for i in range(pyr.M[l]):
+            want = K[:, i * span:(i + 1) * span].astype(np.float64).mean(axis=1)  # [B][H][d]
+            np.testing.assert_allclose(lev[:, :, i], want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_imperfect_tree_tail_is_unweighted(g):
+    rng = np.random.default_rng(2)
+    N, C, d = 1000, 16, 3
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    Kd = K[0, :, 0].astype(np.float64)
+    pyr = oracle.Pyramid(K, N, C, g)
+    M = pyr.M
+    assert M[1] == 63  # leaf 62 holds tokens 992..999
+    leaf = lambda i: Kd[i * C:min(i * C + C, N)].mean(axis=0)
+    np.testing.assert_allclose(pyr.level(1)[0, 0, 62], leaf(62), atol=1e-14)
+    # the last level-2 node: unweighted mean of its existing children
+    last2 = M[2] - 1
+    kids = [leaf(r) for r in range(last2 * g, min(last2 * g + g, M[1]))]
+    np.testing.assert_allclose(pyr.level(2)[0, 0, last2], np.mean(kids, axis=0), atol=1e-14)
+    # ... which is not the token-weighted mean of its span when children differ in size
+    tok_mean = Kd[last2 * g * C:N].mean(axis=0)
+    if len(kids) > 1:
+        assert np.abs(pyr.level(2)[0, 0, last2] - tok_mean).max() > 1e-3
+    # the level-3 tail node: mean of level-2 children, each already a mean of leaves
+    last3 = M[3] - 1
+    l2 = [pyr.level(2)[0, 0, r] for r in range(last3 * g, min(last3 * g + g, M[2]))]
+    full2 = [np.mean([leaf(x) for x in range(r * g, min(r * g + g, M[1]))], axis=0)
+             for r in range(last3 * g, min(last3 * g + g, M[2]))]
+    np.testing.assert_allclose(l2, full2, atol=1e-14)
+    np.testing.assert_allclose(pyr.level(3)[0, 0, last3], np.mean(full2, axis=0), atol=1e-14)
+
+
+def test_level_sizes():
+    for N, C, g in [(1, 16, 2), (16, 16, 2), (17, 16, 2), (1000, 16, 4), (262144, 64, 4),
+                    (262145, 64, 4), (5, 2, 3)]:
+        M = oracle.levels(N, C, g)
+        assert M[0] == N and M[1] == -(-N // C) and M[-1] == 1
+        for l in range(1, len(M) - 1):
+            assert M[l + 1] == -(-M[l] // g) and M[l] > 1
+    assert oracle.levels(262144, 64, 4) == [262144, 4096, 1024, 256, 64, 16, 4, 1]
+    assert len(oracle.levels(262145, 64, 4)) - 1 == 8
+
+
+# --------------------------------------------------------------------------
+# Scores reduce to scipy's logsumexp (eq 21) and sum over heads (eq 22)
+# --------------------------------------------------------------------------
+
+def test_scores_match_library_logsumexp():
+    rng = np.random.default_rng(3)
+    N, C, g, d, H = 300, 16, 4, 8, 2
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    q = rng.standard_normal(d).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    for h in range(H):
+        Kh = K[0, :, h].astype(np.float64)
+        for i in range(pyr.M[1]):
+            z = Kh[i * C:min(i * C + C, N)] @ q.astype(np.float64) / math.sqrt(d)
+            assert oracle.score(pyr, q, 0, h, 1, i) == pytest.approx(logsumexp(z), abs=1e-12)
+        for l in range(2, pyr.L + 1):
+            for i in range(pyr.M[l]):
+                kids = pyr.level(l - 1)[0, h, i * g:min(i * g + g, pyr.M[l - 1])]
+                z = kids @ q.astype(np.float64) / math.sqrt(d)
+                assert oracle.score(pyr, q, 0, h, l, i) == pytest.approx(logsumexp(z), abs=1e-12)
+
+
+def test_group_scores_are_sums_of_head_scores():
+    rng = np.random.default_rng(4)
+    N, C, g, d, Hq = 512, 16, 2, 8, 3
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    Q = rng.standard_normal((5, Hq, d)).astype(np.float32)
+    t = np.array([511, 400, 300, 200, 100])
+    pyr = oracle.Pyramid(K, N, C, g)
+    r = oracle.route(pyr, Q, [0] * 5, t, 4, causal=True)
+    checked = 0
+    for n in range(5):
+        for i, s in zip(r["idx"][n, 0], r["score"][n, 0]):
+            if i >= 0 and np.isfinite(s):
+                want = sum(oracle.score(pyr, Q[n, j], 0, 0, 1, int(i)) for j in range(Hq))
+                assert s == pytest.approx(want, abs=1e-12)
+                checked += 1
+    assert checked > 0
+
+
+# --------------------------------------------------------------------------
+# Reductions to brute force (section 3.2: a level with at most K candidates is
+# kept whole, so K_top >= M_2 turns PISA into exhaustive leaf LSE selection)
+# --------------------------------------------------------------------------
+
+def exhaustive_lse(K, Q, t, C, Kt, causal=True):
+    """Brute force: score every eligible non-forced leaf by summed raw-key LSE."""
+    N, H, d = K.shape[1], K.shape[2], K.shape[3]
+    Hq = Q.shape[1]
+    G = Hq // H
+    M1 = -(-N // C)
+    out = []
+    for n, tt in enumerate(t):
+        c = tt // C
+        row = []
+        for h in range(H):
+            elig = list(range(c + 1)) if causal else list(range(M1))
+            F = sorted({0, c} | ({c - 1} if c >= 1 else set())) if causal else []
+            if len(elig) <= Kt:
+                row.append(sorted(elig))
+                continue
+            S = [i for i in elig if i not in F]
+            u = []
+            for i in S:
+                Kb = K[0, i * C:min(i * C + C, N), h].astype(np.float64)
+                u.append(sum(logsumexp(Kb @ Q[n, h * G + j].astype(np.float64) / math.sqrt(d))
+                             for j in range(G)))
+            order = sorted(range(len(S)), key=lambda k: (-u[k], S[k]))
+            row.append(sorted(F + [S[k] for k in order[:Kt - len(F)]]))
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("Kt", [32, 64])
+def test_reduction_to_exhaustive_on_tiny(Kt):
+    rng = np.random.default_rng(5)
+    N, C, g, d = 1024, 16, 2, 64
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    Q = rng.standard_normal((N, 1, d)).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    t = np.arange(0, N, 7)
+    r = oracle.route(pyr, Q[t], [0] * len(t), t, Kt, causal=True, trace=True)
+    want = exhaustive_lse(K, Q[t], t, C, Kt)
+    for n in range(len(t)):
+        got = [int(x) for x in r["idx"][n, 0] if x >= 0]
+        assert got == want[n][0], "t=%d" % t[n]
+        assert len(got) == min(Kt, t[n] // C + 1)
+    if Kt == 64:
+        assert r["trace"][..., 1].sum() == 0  # nothing is ever scored
+    else:
+        assert r["trace"][:, 0, 2:, 1].sum() == 0 and r["trace"][-1, 0, 1].tolist() == [64, 61]
+
+
+def test_reduction_to_exhaustive_grouped_noncausal():
+    rng = np.random.default_rng(6)
+    N, C, g, d, H, Hq = 200, 8, 4, 8, 2, 4
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    Q = rng.standard_normal((10, Hq, d)).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    Kt = pyr.M[2]  # every level above the leaves is kept whole
+    t = np.arange(10) * 19
+    r = oracle.route(pyr, Q, [0] * 10, t, Kt, causal=False)
+    want = exhaustive_lse(K, Q, t, C, Kt, causal=False)
+    for n in range(10):
+        for h in range(H):
+            assert [int(x) for x in r["idx"][n, h] if x >= 0] == want[n][h]
+
+
+# --------------------------------------------------------------------------
+# Invariants: budget and candidate bounds (eq 19-20), forced set and causality
+# (appendix B), the Jensen sandwich (appendix A.1 eq 39)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,C,g,Kt", [(1000, 16, 2, 4), (1000, 16, 4, 4), (4096, 16, 4, 8)])
+def test_budget_forced_and_causal(N, C, g, Kt):
+    rng = np.random.default_rng(8)
+    d = 16
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    t = np.arange(N)
+    Q = rng.standard_normal((N, 1, d)).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    r = oracle.route(pyr, Q, [0] * N, t, Kt, causal=True, trace=True)
+    for n in range(N):
+        c = t[n] // C
+        got = [int(x) for x in r["idx"][n, 0] if x >= 0]
+        assert len(got) == min(Kt, c + 1) and len(set(got)) == len(got)
+        assert got == sorted(got) and all(x <= c for x in got)
+        assert {0, c} | ({c - 1} if c >= 1 else set()) <= set(got)
+        assert (r["idx"][n, 0][len(got):] == -1).all()
+    assert (r["trace"][..., 0] <= g * Kt).all()
+
+
+def test_jensen_sandwich_on_random_perfect_tree():
+    rng = np.random.default_rng(9)
+    C, g, k, d = 4, 2, 6, 8
+    N = C * g ** k
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    Kd = K[0, :, 0].astype(np.float64)
+    pyr = oracle.Pyramid(K, N, C, g)
+    for trial in range(4):
+        q = rng.standard_normal(d).astype(np.float32)
+        qd = q.astype(np.float64)
+        for l in range(2, pyr.L + 1):
+            span, cspan = C * g ** (l - 1), C * g ** (l - 2)
+            for i in range(pyr.M[l]):
+                m = [Kd[(i * g + j) * cspan:(i * g + j + 1) * cspan].mean(0) @ qd / math.sqrt(d)
+                     for j in range(g)]
+                F_hat = oracle.score(pyr, q, 0, 0, l, i) - math.log(g)
+                F_q = logsumexp(Kd[i * span:(i + 1) * span] @ qd / math.sqrt(d)) - math.log(span)
+                assert np.mean(m) <= F_hat + 1e-12
+                assert F_hat <= F_q + 1e-12
+                assert F_hat == pytest.approx(logsumexp(m) - math.log(g), abs=1e-12)
+
+
+def test_planted_block_is_found():
+    """A past leaf whose keys all equal beta * q / |q| with beta |q| / sqrt(d) = 40 wins
+    at every level (its share of each ancestor summary stays far above the noise)."""
+    rng = np.random.default_rng(10)
+    N, C, g, d, Kt = 1024, 16, 2, 64, 4
+    for t, j in [(1023, 5), (900, 30), (700, 1), (500, 17)]:
+        K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+        q = rng.standard_normal(d).astype(np.float32)
+        for sign in (+1, -1):
+            Kp = K.copy()
+            beta = 40 * math.sqrt(d) / np.linalg.norm(q)
+            Kp[0, j * C:(j + 1) * C, 0] = sign * beta * q / np.linalg.norm(q)
+            pyr = oracle.Pyramid(Kp, N, C, g)
+            r = oracle.route(pyr, q.reshape(1, 1, d), [0], [t], Kt, causal=True)
+            assert (j in r["idx"][0, 0]) == (sign > 0 or j == 0)
+
+
+def test_decode_route_equals_prefix_route():
+    """Routing the last token of a length-n prefix equals routing position n-1 inside a
+    longer sequence: every node the query ranks lies in its past (appendix B)."""
+    rng = np.random.default_rng(11)
+    N, C, g, d, Hq = 2048, 16, 4, 16, 2
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    Q = rng.standard_normal((N, Hq, d)).astype(np.float32)
+    full = oracle.Pyramid(K, N, C, g)
+    ns = [1, 2, 16, 17, 63, 64, 65, 255, 256, 257, 1024, 1025, 2000, 2048]
+    r_full = oracle.route(full, Q[np.array(ns) - 1], [0] * len(ns), np.array(ns) - 1, 8, causal=True)
+    for k, n in enumerate(ns):
+        pre = oracle.Pyramid(K[:, :n].copy(), n, C, g)
+        r = oracle.route(pre, Q[n - 1:n], [0], [n - 1], 8, causal=True)
+        assert r["idx"][0].tolist() == r_full["idx"][k].tolist(), "n=%d" % n
+
+
+def test_head_permutation_symmetry():
+    rng = np.random.default_rng(12)
+    N, C, g, d = 1024, 16, 2, 16
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    Q = rng.standard_normal((64, 4, d)).astype(np.float32)
+    t = np.arange(64) * 16
+    pyr = oracle.Pyramid(K, N, C, g)
+    a = oracle.route(pyr, Q, [0] * 64, t, 4)
+    b = oracle.route(pyr, Q[:, [2, 0, 3, 1]], [0] * 64, t, 4)
+    assert (a["idx"] == b["idx"]).all()
+    np.testing.assert_allclose(a["score"], b["score"], atol=1e-12)
+
+
+def test_single_head_groups_route_independently():
+    rng = np.random.default_rng(13)
+    N, C, g, d = 512, 16, 2, 16
+    K = rng.standard_normal((1, N, 2, d)).astype(np.float32)
+    Q = rng.standard_normal((32, 2, d)).astype(np.float32)
+    t = np.arange(32) * 16 + 3
+    both = oracle.route(oracle.Pyramid(K, N, C, g), Q, [0] * 32, t, 4)
+    for h in range(2):
+        one = oracle.route(oracle.Pyramid(K[:, :, h:h + 1].copy(), N, C, g), Q[:, h:h + 1],
+                           [0] * 32, t, 4)
+        assert (one["idx"][:, 0] == both["idx"][:, h]).all()
+
+
+# --------------------------------------------------------------------------
+# Exhaustive selector against scipy softmax (section 3.1, appendix C's per-head
+# normalisation), attention against torch SDPA (eq 6)
+# --------------------------------------------------------------------------
+
+def test_bsa_matches_library_softmax():
+    rng = np.random.default_rng(14)
+    N, C, g, d, H, Hq, Kt = 640, 16, 2, 16, 2, 4, 5
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    Q = rng.standard_normal((40, Hq, d)).astype(np.float32)
+    t = np.arange(40) * 16 + 5
+    pyr = oracle.Pyramid(K, N, C, g)
+    r = oracle.bsa(pyr, Q, [0] * 40, t, Kt)
+    G = Hq // H
+    for n in range(40):
+        c = t[n] // C
+        for h in range(H):
+            means = np.stack([K[0, i * C:(i + 1) * C, h].astype(np.float64).mean(0)
+                              for i in range(c + 1)])
+            F = sorted({0, c} | ({c - 1} if c >= 1 else set()))
+            if c + 1 <= Kt:
+                want = list(range(c + 1))
+            else:
+                S = [i for i in range(c + 1) if i not in F]
+                u = sum(softmax(means[S] @ Q[n, h * G + j].astype(np.float64) / math.sqrt(d))
+                        for j in range(G))
+                order = sorted(range(len(S)), key=lambda k: (-u[k], S[k]))
+                want = sorted(F + [S[k] for k in order[:Kt - len(F)]])
+                np.testing.assert_allclose(np.sort(u)[::-1][:Kt - len(F)],
+                                           np.sort(r["score"][n, h][np.isfinite(r["score"][n, h])])[::-1],
+                                           atol=1e-12)
+            assert [int(x) for x in r["idx"][n, h] if x >= 0] == want
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_matches_sdpa(causal):
+    rng = np.random.default_rng(15)
+    N, C, d, H, Hq = 200, 16, 32, 2, 4
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    V = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    Q = rng.standard_normal((N, Hq, d)).astype(np.float32)
+    M1 = -(-N // C)
+    t = np.arange(N)
+    for sel_kind in ("all", "subset"):
+        if sel_kind == "all":
+            sel = np.tile(np.arange(M1, dtype=np.int32), (N, H, 1))
+        else:
+            sel = np.full((N, H, 4), -1, np.int32)
+            for n in range(N):
+                for h in range(H):
+                    pick = rng.choice(M1, size=3, replace=False)
+                    sel[n, h, :3] = np.sort(pick)
+        r = oracle.sparse_attn(Q, [0] * N, t, K, V, N, C, sel, causal=causal)
+        mask = torch.zeros(Hq, N, N, dtype=torch.bool)
+        for n in range(N):
+            for hq in range(Hq):
+                for i in sel[n, hq // (Hq // H)]:
+                    if i >= 0:
+                        mask[hq, n, i * C:min(i * C + C, N)] = True
+        if causal:
+            mask &= torch.ones(N, N, dtype=torch.bool).tril()
+        empty = ~mask.any(-1)
+        mask[empty] = True  # keep SDPA finite; such rows are checked separately
+        q = torch.from_numpy(Q).double().permute(1, 0, 2)
+        k = torch.from_numpy(K[0]).double().permute(1, 0, 2).repeat_interleave(Hq // H, 0)
+        v = torch.from_numpy(V[0]).double().permute(1, 0, 2).repeat_interleave(Hq // H, 0)
+        want = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+        want = want.permute(1, 0, 2).numpy()
+        emp = empty.permute(1, 0).numpy()
+        np.testing.assert_allclose(r["out"][~emp], want[~emp], atol=1e-10)
+        assert (r["out"][emp] == 0).all() and np.isneginf(r["lse"][emp]).all()
