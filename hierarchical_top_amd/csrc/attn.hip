@@ -1,0 +1,267 @@
+// attn.hip -- block-sparse attention forward ("Block Sparse Attention with
+// Log-Linear Complexity", section 3.1 eq 6; appendix B: future tokens inside
+// a selected block are masked).
+//
+// One wave per (sequence, query row, KV head); four waves per workgroup.
+// Per selected block of C keys (C < 32 is padded to 32 with masked keys):
+//   S^T = K_blk Q^T on MFMA: A = 16 keys x d, B = d x 16 columns holding the
+//     G_Q query heads (and, for fp32 queries, their low halves). Tile rt's
+//     row r holds key 32*(rt/2) + 8*(r/4) + 4*(rt%2) + r%4, so that after the
+//     product every lane holds, for its head, the 8 consecutive keys that the
+//     P V product needs from it: P is used straight from registers.
+//   online softmax in base 2 per head (fp32);
+//   O += P V on MFMA with V staged transposed in LDS (V^T[d][key]).
+#include "pisa_device.hpp"
+#include "pisa_internal.hpp"
+
+namespace pisa {
+
+template <int D, typename T, int G>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
+{
+    constexpr int TA = Src<T>::TERMS;  // query terms (columns per head)
+    constexpr int TB = Src<T>::TERMS;  // key / value / probability terms
+    constexpr int KS = D / 32;
+    constexpr int CT = D / 16;          // output column tiles
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ldv = Cp + 8;  // V^T row stride (bf16)
+    bf16* s_vt = reinterpret_cast<bf16*>(s_raw) + (size_t)wave * TB * D * ldv;
+
+    const int64_t total = (int64_t)a.B * a.H_kv * a.N_q;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= total) return;
+    const int64_t r = item % a.N_q;
+    const int h = (int)((item / a.N_q) % a.H_kv);
+    const int b = (int)(item / ((int64_t)a.N_q * a.H_kv));
+    const int64_t nb = a.kv_len ? a.kv_len[b] : a.N_kv;
+    const int64_t pos = nb - a.N_q + r;
+    const int C = a.C;
+
+    // B operand: column j = lane % 16 -> (term, head); k chunk = lane / 16
+    bf16x8 qb[KS];
+    {
+        const int j = lane & 15;
+        const int term = j / G, head = j % G;
+        const bool ok = j < G * TA && pos >= 0;
+        const T* qp = (const T*)a.Q + (((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head) * D + 8 * (lane >> 4);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 vh, vl;
+            Src<T>::load(qp + 32 * s, ok, vh, vl);
+            qb[s] = term == 0 ? vh : vl;
+        }
+    }
+    const float scale = kLog2e * rsqrtf((float)D);
+    const int col = lane & 15;          // this lane's head column in S^T
+    const bool head_col = col < G;       // a combined (high + low) head lives here
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int32_t* sel = a.idx + (((int64_t)b * a.H_kv + h) * a.N_q + r) * a.K_top;
+    const T* kbase = (const T*)a.K + ((int64_t)b * a.N_alloc * a.H_kv + h) * D;
+    const T* vbase = (const T*)a.V + ((int64_t)b * a.N_alloc * a.H_kv + h) * D;
+    const int64_t kstride = (int64_t)a.H_kv * D;
+    const int nrt = Cp / 16;
+
+    for (int k = 0; k < a.K_top; ++k) {
+        const int blk = sel[k];
+        if (blk < 0) continue;
+        const int64_t k0 = (int64_t)blk * C;
+        int64_t kend = k0 + C < nb ? k0 + C : nb;
+        if (a.causal && kend > pos + 1) kend = pos + 1;
+        if (kend <= k0) continue;  // no visible key in this block (uniform across the wave)
+
+        // Stage V^T: lane = key (lanes >= Cp idle); pairs of lanes write packed dwords.
+        {
+            const int key = lane;
+            const bool kok = key < Cp && k0 + key < kend;
+            const T* vp = vbase + (kok ? (k0 + key) : 0) * kstride;
+#pragma unroll
+            for (int j = 0; j < D / 8; ++j) {
+                bf16x8 vh, vl;
+                Src<T>::load(vp + 8 * j, kok, vh, vl);
+#pragma unroll
+                for (int tp = 0; tp < TB; ++tp) {
+                    const bf16x8 v = tp == 0 ? vh : vl;
+                    const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+                    uint32_t pw[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) pw[q] = (uint32_t)__shfl_xor((int)w[q], 1, 64);
+                    if (key < Cp) {
+                        bf16* plane = s_vt + (size_t)tp * D * ldv;
+                        const bool even = (key & 1) == 0;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            // even lane: element 2q of itself (low) and of key+1 (high), row 8j+2q
+                            // odd lane : element 2q+1 of key-1 (low) and of itself (high), row 8j+2q+1
+                            const uint32_t mine = even ? (w[q] & 0xffffu) : (w[q] >> 16);
+                            const uint32_t other = even ? (pw[q] & 0xffffu) : (pw[q] >> 16);
+                            const uint32_t dw = even ? (mine | (other << 16)) : (other | (mine << 16));
+                            const int row = 8 * j + 2 * q + (even ? 0 : 1);
+                            const int c0 = even ? key : key - 1;
+                            *reinterpret_cast<uint32_t*>(plane + row * ldv + c0) = dw;
+                        }
+                    }
+                }
+            }
+        }
+
+        // S^T tiles
+        float y[4][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            if (rt < nrt) {
+                const int rr = lane & 15;
+                const int key = 32 * (rt >> 1) + 8 * (rr >> 2) + 4 * (rt & 1) + (rr & 3);
+                const bool kok = k0 + key < kend && key < C;
+                const T* kp = kbase + (kok ? (k0 + key) : 0) * kstride + 8 * (lane >> 4);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    bf16x8 kh, kl;
+                    Src<T>::load(kp + 32 * s, kok, kh, kl);
+                    acc = mfma(kh, qb[s], acc);
+                    if constexpr (TB == 2) acc = mfma(kl, qb[s], acc);
+                }
+                // output rows 4*(lane/16)+i are keys of this tile
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int orow = 4 * (lane >> 4) + i;
+                    const int okey = 32 * (rt >> 1) + 8 * (orow >> 2) + 4 * (rt & 1) + (orow & 3);
+                    float v = acc[i];
+                    if constexpr (TA == 2) v += __shfl_xor(v, G, 64);
+                    y[rt][i] = (okey < C && k0 + okey < kend) ? v * scale : -INFINITY;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[rt][i] = -INFINITY;
+            }
+        }
+        // online softmax per head column
+        float mb = -INFINITY;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mb = fmaxf(mb, y[rt][i]);
+        mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const float m_new = fmaxf(m_run, mb);
+        const float fac = __builtin_amdgcn_exp2f(m_run - m_new);
+        float ps = 0.f;
+        float pr[4][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = (rt < nrt && y[rt][i] != -INFINITY) ? __builtin_amdgcn_exp2f(y[rt][i] - m_new) : 0.f;
+                pr[rt][i] = head_col ? pv : 0.f;
+                ps += pv;
+            }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_run = l_run * fac + ps;
+        m_run = m_new;
+        // rescale O rows (heads 4*(lane/16)+i) by their heads' factors
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float f = __shfl(fac, 4 * (lane >> 4) + i, 64);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) o[ct][i] *= f;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // O += P V
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (2 * s < nrt) {
+                f32x8 pv8;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { pv8[i] = pr[2 * s][i]; pv8[4 + i] = pr[2 * s + 1][i]; }
+                // probabilities in bf16 (fp32 inputs: two bf16 terms)
+                bf16x8 ph, pl;
+                split8(pv8, ph, pl);
+                (void)pl;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int vrow = 16 * ct + (lane & 15);
+                    const bf16* vp = s_vt + vrow * ldv + 32 * s + 8 * (lane >> 4);
+                    const bf16x8 vh = *reinterpret_cast<const bf16x8*>(vp);
+                    o[ct] = mfma(ph, vh, o[ct]);
+                    if constexpr (TB == 2) {
+                        const bf16x8 vl = *reinterpret_cast<const bf16x8*>(vp + (size_t)D * ldv);
+                        o[ct] = mfma(ph, vl, o[ct]);
+                        o[ct] = mfma(pl, vh, o[ct]);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // normalise and store rows (heads) 4*(lane/16)+i < G
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int head = 4 * (lane >> 4) + i;
+        const float lh = __shfl(l_run, head & 15, 64);
+        const float inv = lh > 0.f ? 1.f / lh : 0.f;
+        if (head < G) {
+            T* op = (T*)a.O + (((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head) * D + (lane & 15);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) op[16 * ct] = static_cast<T>(o[ct][i] * inv);
+        }
+    }
+    if (a.lse && lane < G) {
+        a.lse[((int64_t)b * a.H_q + (int64_t)h * G + lane) * a.N_q + r] =
+            l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
+    }
+}
+
+template <int D, typename T>
+static hipError_t attn_d(const AttnArgs& a, hipStream_t s)
+{
+    const int Cp = a.C < 32 ? 32 : a.C;
+    const size_t lds = (size_t)4 * Src<T>::TERMS * D * (Cp + 8) * 2;
+    const int64_t total = (int64_t)a.B * a.H_kv * a.N_q;
+    const dim3 grid((unsigned)((total + 3) / 4));
+#define PISA_ATTN_G(GG)                                                                                        \
+    case GG: {                                                                                                 \
+        auto k = attn_kernel<D, T, GG>;                                                                        \
+        hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+        if (e != hipSuccess) return e;                                                                         \
+        hipLaunchKernelGGL(k, grid, dim3(256), lds, s, a, Cp);                                                 \
+        return hipGetLastError();                                                                              \
+    }
+    switch (a.G) {
+        PISA_ATTN_G(1)
+        PISA_ATTN_G(2)
+        PISA_ATTN_G(4)
+        PISA_ATTN_G(8)
+    case 16:
+        if constexpr (Src<T>::TERMS == 1) {
+            auto k = attn_kernel<D, T, 16>;
+            hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(k, grid, dim3(256), lds, s, a, Cp);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef PISA_ATTN_G
+}
+
+hipError_t launch_attn(const AttnArgs& a, int dtype, int d, hipStream_t s)
+{
+    if (dtype == 0) return d == 64 ? attn_d<64, float>(a, s) : attn_d<128, float>(a, s);
+    return d == 64 ? attn_d<64, bf16>(a, s) : attn_d<128, bf16>(a, s);
+}
+
+}  // namespace pisa

@@ -1,0 +1,217 @@
+// pisa_device.hpp -- device helpers for the gfx950 kernels of libpisa:
+// bf16 conversion and hi/lo splitting, the 16x16x32 bf16 MFMA, wavefront
+// primitives (shuffles, ballots, bitonic sort) and pyramid geometry.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pisa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+// ---------------------------------------------------------------------------
+// bf16: round-to-nearest-even conversion and an exact-to-2^-17 two-term split
+// x ~= hi + lo of a float, so that bf16 matrix products of fp32 operands keep
+// close to fp32 accuracy (the products are exact, the sums are fp32).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
+__device__ __forceinline__ float from_bf16(bf16 x) { return static_cast<float>(x); }
+
+__device__ __forceinline__ void split8(const f32x8& v, bf16x8& hi, bf16x8& lo)
+{
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        bf16 h = to_bf16(v[k]);
+        hi[k] = h;
+        lo[k] = to_bf16(v[k] - from_bf16(h));
+    }
+}
+
+__device__ __forceinline__ f32x8 load8f(const float* p)
+{
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    f32x4 a = q[0], b = q[1];
+    f32x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 load8h(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ bf16x8 zero8h()
+{
+    bf16x8 z;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) z[k] = to_bf16(0.0f);
+    return z;
+}
+
+// Load 8 consecutive elements of a bf16 or fp32 row as bf16 operand terms.
+// TERMS = 1 for bf16 sources (exact), 2 for fp32 sources (hi + lo).
+template <typename T> struct Src;
+template <> struct Src<bf16> {
+    static constexpr int TERMS = 1;
+    __device__ __forceinline__ static void load(const bf16* p, bool ok, bf16x8& hi, bf16x8& lo)
+    {
+        hi = ok ? load8h(p) : zero8h();
+        lo = zero8h();
+    }
+};
+template <> struct Src<float> {
+    static constexpr int TERMS = 2;
+    __device__ __forceinline__ static void load(const float* p, bool ok, bf16x8& hi, bf16x8& lo)
+    {
+        if (ok) {
+            split8(load8f(p), hi, lo);
+        } else {
+            hi = zero8h();
+            lo = zero8h();
+        }
+    }
+};
+
+// D += A * B for one 16x16x32 bf16 tile. Lane l holds A[l%16][k-chunk l/16]
+// and B[k-chunk l/16][l%16] (8 consecutive k each); D lane l holds rows
+// 4*(l/16) + i, i = 0..3, of column l % 16.
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront primitives.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ int shfl_xor(int v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, kWave); }
+__device__ __forceinline__ int shfl(int v, int src) { return __shfl(v, src, kWave); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ int rank_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Move each lane's value to lane dst (a permutation of 0..63).
+__device__ __forceinline__ int permute_to(int dst, int v) { return __builtin_amdgcn_ds_permute(dst << 2, v); }
+__device__ __forceinline__ float permute_to(int dst, float v)
+{
+    return __int_as_float(__builtin_amdgcn_ds_permute(dst << 2, __float_as_int(v)));
+}
+
+// Stable compaction: lanes with keep=true move, in lane order, to lanes
+// 0..count-1; the others fill the remaining lanes. Returns the count.
+__device__ __forceinline__ int compact(bool keep, int& a, float& b)
+{
+    int lane = lane_id();
+    uint64_t m = ballot(keep);
+    int cnt = __popcll(m);
+    int r = rank_below(m);
+    int dst = keep ? r : cnt + (lane - r);
+    a = permute_to(dst, a);
+    b = permute_to(dst, b);
+    return cnt;
+}
+
+// Maximum / sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_max(float x, int width)
+{
+    for (int o = 1; o < width; o <<= 1) x = fmaxf(x, shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float group_sum(float x, int width)
+{
+    for (int o = 1; o < width; o <<= 1) x += shfl_xor(x, o);
+    return x;
+}
+
+// Selection order: higher key first; equal keys -> lower id first.
+__device__ __forceinline__ bool before(float ka, int ia, float kb, int ib)
+{
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// Bitonic sort of (key, id) over the 64 lanes into selection order: after the
+// call lane 0 holds the first element. Ids must be distinct among lanes that
+// carry equal keys (padding lanes use key -inf and distinct large ids).
+__device__ __forceinline__ void bitonic_sort(float& key, int& id)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            float ok = shfl_xor(key, j);
+            int oi = shfl_xor(id, j);
+            bool forward = (lane & k) == 0 || k == 64;
+            bool lower = (lane & j) == 0;
+            bool want_first = (lower == forward);
+            bool other_first = before(ok, oi, key, id);
+            bool take = want_first ? other_first : !other_first;
+            if (take) {
+                key = ok;
+                id = oi;
+            }
+        }
+    }
+}
+
+// Sort ids ascending across the wave, carrying a float payload (ids distinct;
+// padding lanes use INT_MAX - lane).
+__device__ __forceinline__ void sort_ids_ascending(int& id, float& val)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            int oi = shfl_xor(id, j);
+            float ov = shfl_xor(val, j);
+            bool forward = (lane & k) == 0 || k == 64;
+            bool lower = (lane & j) == 0;
+            bool want_small = (lower == forward);
+            bool take = want_small ? (oi < id) : (oi > id);
+            if (take) {
+                id = oi;
+                val = ov;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pyramid geometry (C and g are powers of two): a level-l node covers
+// C * g^(l-1) tokens; M_l(n) = ceil(n / span_l); the top level L(n) is the
+// first level with one node.
+// ---------------------------------------------------------------------------
+struct Geo {
+    int c_log2, g_log2;
+    __device__ __forceinline__ int span_log2(int l) const { return c_log2 + (l - 1) * g_log2; }
+    __device__ __forceinline__ int64_t nodes(int64_t n, int l) const
+    {
+        int s = span_log2(l);
+        return (n + ((int64_t)1 << s) - 1) >> s;
+    }
+    __device__ __forceinline__ int top(int64_t n) const
+    {
+        int l = 1;
+        while (nodes(n, l) > 1) ++l;
+        return l;
+    }
+};
+
+}  // namespace pisa

@@ -1,0 +1,107 @@
+// pisa_internal.hpp -- kernel argument blocks and launchers shared between the
+// C ABI layer (capi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pisa.h"
+
+namespace pisa {
+
+// Pyramid geometry and storage, copied from pisa_pyramid (kernel argument).
+struct PyrArgs {
+    int B, H, d, C, g, g_log2, c_log2, L_cap;
+    int64_t N_cap;
+    int64_t M_cap[PISA_MAX_LEVELS + 1];
+    int64_t off[PISA_MAX_LEVELS + 1];
+    float* buf;
+};
+
+// Routing of one (query, KV head) item per workgroup (prefill fused,
+// prefill stage 1, decode).
+struct RouteArgs {
+    PyrArgs p;
+    const void* Q;        // prefill [B][N][H_q][d]; decode [B][H_q][d]
+    const void* K;        // [B][N_cap][H_kv][d]
+    int64_t N;            // prefill sequence length (unused for decode)
+    const int64_t* seqlen;  // decode: per-sequence length; null for prefill
+    int H_q, G, K_top, causal;
+    int32_t* idx;         // fused / decode output
+    float* score;         // nullable
+    // stage 1 outputs
+    int32_t* kept2;       // [B][H][N][K_top]
+    int64_t* meta;        // [B][H][N]
+    int32_t* counts;      // [B][H][M2] cluster sizes
+    int64_t M2;           // level-2 nodes for this N (1 if N <= C * ... see capi)
+};
+
+// Leaf scoring of clustered (query, retained level-2 node) pairs.
+struct Stage2Args {
+    PyrArgs p;
+    const void* Q;
+    const void* K;
+    int64_t N;
+    int H_q, G, K_top;
+    int64_t n_clusters;          // B * H * M2
+    int64_t M2;
+    const int32_t* offsets;      // [n_clusters + 1] entry offsets
+    const int32_t* chunk_off;    // [n_clusters + 1] chunk offsets
+    const int32_t* entries;      // (t << 6) | slot
+    float* u;                    // [B][H][N][g * K_top]
+};
+
+struct FinalArgs {
+    int B, H, C, g, c_log2, g_log2, K_top, causal;
+    int64_t N;
+    const int32_t* kept2;
+    const int64_t* meta;
+    const float* u;
+    int32_t* idx;
+    float* score;
+};
+
+struct ScatterArgs {
+    int B, H, K_top;
+    int64_t N, M2;
+    const int32_t* kept2;
+    const int64_t* meta;
+    const int32_t* offsets;
+    int32_t* cursor;
+    int32_t* entries;
+};
+
+struct AttnArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    int B, H_q, H_kv, G, C, K_top, causal;
+    int64_t N_q, N_kv, N_alloc;
+    const int32_t* idx;
+    const int64_t* kv_len;
+    void* O;
+    float* lse;
+};
+
+struct BsaArgs {
+    PyrArgs p;
+    const void* Q;
+    int64_t N;
+    int H_q, G, K_top, causal;
+    float* row_lse;  // [B][H_q][N] (workspace)
+    int32_t* idx;
+    float* score;
+};
+
+hipError_t launch_build(const PyrArgs& a, const void* K, int dtype, int64_t n, hipStream_t s);
+hipError_t launch_append(const PyrArgs& a, const void* K, int dtype, const int64_t* seqlen, hipStream_t s);
+hipError_t launch_route_query(const RouteArgs& a, int dtype, int d, int mode, hipStream_t s);
+hipError_t launch_two_stage(const RouteArgs& a, const Stage2Args& s2, const FinalArgs& f,
+                            const ScatterArgs& sc, int32_t* zero_base, int64_t zero_count, int dtype,
+                            int d, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_bsa(const BsaArgs& a, int dtype, int d, hipStream_t s);
+
+enum { MODE_FUSED = 0, MODE_STAGE1 = 1, MODE_DECODE = 2 };
+
+}  // namespace pisa

@@ -1,0 +1,220 @@
+"""Python binding of libpisa (include/pisa.h): argument marshalling only.
+
+Every step of the selection path runs in the library's HIP kernels; this module
+turns torch tensors into pointers, sizes and the current HIP stream, and turns
+negative status codes into exceptions. There is no fallback: if libpisa.so is
+missing or no GPU is present, the calls raise.
+
+Method: "Block Sparse Attention with Log-Linear Complexity" (PISA); the
+library header cites the sections each call implements.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libpisa.so"
+MAX_LEVELS = 32
+F32, BF16 = 0, 1
+TWO_STAGE, FUSED = 0, 1
+
+c_i32, c_i64, c_p, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+
+class PisaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("libpisa status %d: %s" % (status, msg))
+        self.status = status
+
+
+class _PyramidDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", c_i32), ("H_kv", c_i32), ("d", c_i32), ("C", c_i32), ("g", c_i32), ("L_cap", c_i32),
+        ("N_cap", c_i64),
+        ("M_cap", c_i64 * (MAX_LEVELS + 1)),
+        ("off", c_i64 * (MAX_LEVELS + 1)),
+        ("floats", c_i64),
+        ("buf", c_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpisa.so (built by hierarchical_top_amd.build or __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError("libpisa.so is not built (run: python -m hierarchical_top_amd.build)")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P = ctypes.POINTER(_PyramidDesc)
+        sig = {
+            "pisa_pyramid_plan": [P, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64],
+            "pisa_build_pyramid": [P, c_p, c_i32, c_i64, c_p],
+            "pisa_pyramid_append": [P, c_p, c_i32, c_p, c_p],
+            "pisa_route_prefill_workspace": [P, c_i64, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)],
+            "pisa_route_prefill": [P, c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p,
+                                   c_size, c_p],
+            "pisa_route_decode": [P, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p],
+            "pisa_sparse_attn": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p,
+                                 c_i32, c_i32, c_p, c_p, c_p, c_p],
+            "pisa_bsa_workspace": [P, c_i64, c_i32, ctypes.POINTER(c_size)],
+            "pisa_bsa_select": [P, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_size, c_p],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.pisa_status_str.argtypes = [ctypes.c_int]
+        L.pisa_status_str.restype = ctypes.c_char_p
+        L.pisa_last_error.argtypes = []
+        L.pisa_last_error.restype = ctypes.c_char_p
+        L.pisa_abi_version.argtypes = []
+        L.pisa_abi_version.restype = c_i32
+        _lib = L
+    return _lib
+
+
+EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
+           "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_bsa_workspace", "pisa_bsa_select",
+           "pisa_status_str", "pisa_last_error", "pisa_abi_version"]
+
+
+def _check(status: int):
+    if status != 0:
+        raise PisaError(status, lib().pisa_last_error().decode())
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("libpisa takes float32 or bfloat16 tensors, got %s" % x.dtype)
+
+
+def _ptr(x):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _dev(*xs):
+    for x in xs:
+        if x is not None and (not x.is_cuda or not x.is_contiguous()):
+            raise ValueError("libpisa takes contiguous GPU tensors")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Pyramid:
+    """Mean-pooled key pyramid for B sequences of up to N_cap tokens.
+
+    Owns its float32 summary buffer (a torch tensor on `device`).
+    """
+
+    def __init__(self, B: int, H_kv: int, d: int, C: int, g: int, N_cap: int, device="cuda"):
+        self.desc = _PyramidDesc()
+        _check(lib().pisa_pyramid_plan(ctypes.byref(self.desc), B, H_kv, d, C, g, N_cap))
+        self.buf = torch.empty(max(int(self.desc.floats), 1), dtype=torch.float32, device=device)
+        self.desc.buf = self.buf.data_ptr()
+        self.B, self.H_kv, self.d, self.C, self.g, self.N_cap = B, H_kv, d, C, g, N_cap
+
+    @property
+    def L_cap(self) -> int:
+        return int(self.desc.L_cap)
+
+    def level(self, l: int) -> torch.Tensor:
+        """Level-l storage [B][H_kv][M_cap[l]][d] (a view of the buffer)."""
+        o, M = int(self.desc.off[l]), int(self.desc.M_cap[l])
+        n = self.B * self.H_kv * M * self.d
+        return self.buf[o:o + n].view(self.B, self.H_kv, M, self.d)
+
+    def build(self, K: torch.Tensor, N: int):
+        """Build levels 1..L(N) from K [B][N_cap][H_kv][d]."""
+        _dev(K)
+        _check(lib().pisa_build_pyramid(ctypes.byref(self.desc), _ptr(K), _dt(K), N, _stream()))
+
+    def append(self, K: torch.Tensor, seqlen: torch.Tensor):
+        """Update the path of the newest token of each sequence (seqlen: int64 [B])."""
+        _dev(K, seqlen)
+        assert seqlen.dtype == torch.int64
+        _check(lib().pisa_pyramid_append(ctypes.byref(self.desc), _ptr(K), _dt(K), _ptr(seqlen), _stream()))
+
+
+def route_workspace_bytes(pyr: Pyramid, N: int, H_q: int, K_top: int, mode: int = TWO_STAGE) -> int:
+    n = c_size(0)
+    _check(lib().pisa_route_prefill_workspace(ctypes.byref(pyr.desc), N, H_q, K_top, mode, ctypes.byref(n)))
+    return int(n.value)
+
+
+def route_prefill(pyr: Pyramid, Q: torch.Tensor, K: torch.Tensor, N: int, K_top: int, causal: bool = True,
+                  mode: int = TWO_STAGE, with_score: bool = False, workspace: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None, score_out: torch.Tensor | None = None):
+    """Route every position of Q [B][N][H_q][d]; returns idx [B][H_kv][N][K_top] (and scores)."""
+    _dev(Q, K)
+    B, Nq, H_q, d = Q.shape
+    assert Nq == N and K.dtype == Q.dtype
+    idx = out if out is not None else torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.int32, device=Q.device)
+    score = None
+    if with_score:
+        score = score_out if score_out is not None else torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.float32,
+                                                                    device=Q.device)
+    need = route_workspace_bytes(pyr, N, H_q, K_top, mode)
+    ws = workspace
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    _check(lib().pisa_route_prefill(ctypes.byref(pyr.desc), _ptr(Q), _ptr(K), _dt(Q), N, H_q, K_top,
+                                    1 if causal else 0, H_q // pyr.H_kv, mode, _ptr(idx), _ptr(score),
+                                    _ptr(ws) if need else None, need, _stream()))
+    return (idx, score) if with_score else idx
+
+
+def route_decode(pyr: Pyramid, q: torch.Tensor, K: torch.Tensor, seqlen: torch.Tensor, K_top: int,
+                 with_score: bool = False, out: torch.Tensor | None = None, score_out: torch.Tensor | None = None):
+    """Route the newest token of each sequence: q [B][H_q][d]; returns idx [B][H_kv][K_top]."""
+    _dev(q, K, seqlen)
+    B, H_q, d = q.shape
+    idx = out if out is not None else torch.empty(B, pyr.H_kv, K_top, dtype=torch.int32, device=q.device)
+    score = None
+    if with_score:
+        score = score_out if score_out is not None else torch.empty(B, pyr.H_kv, K_top, dtype=torch.float32,
+                                                                    device=q.device)
+    _check(lib().pisa_route_decode(ctypes.byref(pyr.desc), _ptr(q), _ptr(K), _dt(q), _ptr(seqlen), H_q, K_top,
+                                   H_q // pyr.H_kv, _ptr(idx), _ptr(score), _stream()))
+    return (idx, score) if with_score else idx
+
+
+def sparse_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, block_idx: torch.Tensor, C: int, N_kv: int,
+                causal: bool = True, kv_len: torch.Tensor | None = None, with_lse: bool = False,
+                out: torch.Tensor | None = None):
+    """Block-sparse attention: Q [B][N_q][H_q][d], K/V [B][N_alloc][H_kv][d], block_idx [B][H_kv][N_q][K_top]."""
+    _dev(Q, K, V, block_idx, kv_len)
+    B, N_q, H_q, d = Q.shape
+    N_alloc, H_kv = K.shape[1], K.shape[2]
+    K_top = block_idx.shape[-1]
+    O = out if out is not None else torch.empty_like(Q)
+    lse = torch.empty(B, H_q, N_q, dtype=torch.float32, device=Q.device) if with_lse else None
+    _check(lib().pisa_sparse_attn(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, N_q, N_kv, N_alloc, H_q, H_kv, d, C,
+                                  _ptr(block_idx), K_top, 1 if causal else 0, _ptr(kv_len), _ptr(O), _ptr(lse),
+                                  _stream()))
+    return (O, lse) if with_lse else O
+
+
+def bsa_select(pyr: Pyramid, Q: torch.Tensor, N: int, K_top: int, causal: bool = True, with_score: bool = False,
+               workspace: torch.Tensor | None = None):
+    """Exhaustive single-level selection (comparison point); returns idx [B][H_kv][N][K_top]."""
+    _dev(Q)
+    B, Nq, H_q, d = Q.shape
+    idx = torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.int32, device=Q.device)
+    score = torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.float32, device=Q.device) if with_score else None
+    n = c_size(0)
+    _check(lib().pisa_bsa_workspace(ctypes.byref(pyr.desc), N, H_q, ctypes.byref(n)))
+    ws = workspace if workspace is not None and workspace.numel() >= n.value else \
+        torch.empty(int(n.value), dtype=torch.uint8, device=Q.device)
+    _check(lib().pisa_bsa_select(ctypes.byref(pyr.desc), _ptr(Q), _dt(Q), N, H_q, K_top, 1 if causal else 0,
+                                 H_q // pyr.H_kv, _ptr(idx), _ptr(score), _ptr(ws), int(n.value), _stream()))
+    return (idx, score) if with_score else idx

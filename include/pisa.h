@@ -1,0 +1,211 @@
+/*
+ * pisa.h -- C ABI of libpisa: PISA pyramid Top-K block selection and
+ * block-sparse attention for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Block Sparse Attention with Log-Linear Complexity" (PISA), arXiv
+ * HTML full text. Section and equation numbers below refer to that page. The
+ * page numbers blocks from 1; this interface numbers everything from 0.
+ *
+ * General conventions
+ * -------------------
+ * - Every pointer argument named as device memory must point to memory of the
+ *   current HIP device. The library never allocates, frees or synchronises:
+ *   the caller owns every buffer (inputs, outputs, the pyramid buffer and the
+ *   workspace) and keeps them alive until the work queued on `stream` is done.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   All work is queued asynchronously on it.
+ * - Arguments are validated on the host before anything is queued; a failed
+ *   check returns a negative status and queues nothing. pisa_last_error()
+ *   then returns a message naming the argument (per host thread).
+ * - Tensors are dense and row-major, innermost dimension last, base pointers
+ *   16-byte aligned. dtype PISA_BF16 is bfloat16, PISA_F32 is IEEE float.
+ * - Grouped-query heads are contiguous: query head h' reads KV head h' / G_Q,
+ *   where G_Q = H_q / H_kv (the `gqa_group` argument).
+ * - Block ids are 0-based leaf-block indices; leaf block i holds tokens
+ *   [i*C, min(i*C + C, n)).
+ * - Supported shapes: d in {64, 128}; C in {16, 32, 64}; g in {2, 4, 8, 16};
+ *   G_Q in {1, 2, 4, 8, 16}; G_Q * (2 if f32 else 1) <= 16;
+ *   1 <= K_top <= 64 and g * K_top <= 64, or K_top >= the number of leaf
+ *   blocks (then every eligible leaf is kept); causal routing needs K_top >= 3.
+ *   Other shapes return PISA_EUNSUPPORTED.
+ * - Calls do not share mutable state; two calls may run concurrently on
+ *   different streams if they do not write the same buffers.
+ */
+#ifndef PISA_H
+#define PISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PISA_ABI_VERSION 1
+#define PISA_MAX_LEVELS 32
+
+typedef enum pisa_status {
+    PISA_OK = 0,
+    PISA_EINVAL = -1,        /* an argument is out of range or inconsistent */
+    PISA_EUNSUPPORTED = -2,  /* valid, but no kernel is built for this shape */
+    PISA_ENOSPACE = -3,      /* a length exceeds the pyramid capacity, or the workspace is too small */
+    PISA_EHIP = -4           /* the HIP runtime reported an error while queueing */
+} pisa_status;
+
+typedef enum pisa_dtype { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
+
+typedef enum pisa_route_mode {
+    PISA_ROUTE_TWO_STAGE = 0,  /* section 3.3: intermediate levels per query, then leaf
+                                  scoring per retained level-2 node with key reuse */
+    PISA_ROUTE_FUSED = 1       /* all levels of one query in one program (per-query) */
+} pisa_route_mode;
+
+/*
+ * Key pyramid (section 3.2, "Fine-to-coarse block aggregation", eq 7-15).
+ * Level 0 is the caller's keys. Level 1 holds one summary per leaf block of C
+ * keys, level l+1 one per group of g level-l blocks; M_1 = ceil(n / C),
+ * M_{l+1} = ceil(M_l / g), and the top level L is the first with one block.
+ * Each summary is the mean of its existing children (the mean of the keys
+ * present for a leaf; an unweighted mean of the existing children above).
+ *
+ * Storage: float32, level l (1 <= l <= L_cap) at float offset off[l] of buf,
+ * laid out [B][H_kv][M_cap[l]][d]. Node j of level l for a sequence of n
+ * tokens is valid when j < ceil(n / (C * g^(l-1))).
+ *
+ * The descriptor is plain data owned by the caller: pisa_pyramid_plan() fills
+ * the geometry and `floats`; the caller then allocates `floats` float32 of
+ * device memory and stores the pointer in `buf`.
+ */
+typedef struct pisa_pyramid {
+    int32_t B, H_kv, d, C, g;
+    int32_t L_cap;                        /* levels at capacity */
+    int64_t N_cap;                        /* tokens per sequence the buffer holds */
+    int64_t M_cap[PISA_MAX_LEVELS + 1];   /* nodes per level at capacity; M_cap[0] = N_cap */
+    int64_t off[PISA_MAX_LEVELS + 1];     /* float offset of level l in buf */
+    int64_t floats;                       /* size of buf in float32 elements */
+    float* buf;                           /* device memory, set by the caller */
+} pisa_pyramid;
+
+/* Fill the geometry of a pyramid for B sequences of up to N_cap tokens with
+ * H_kv heads of dimension d, leaf size C and branching g. buf is set to NULL.
+ * Errors: PISA_EINVAL (non-positive sizes, N_cap too large for
+ * PISA_MAX_LEVELS levels), PISA_EUNSUPPORTED (d, C or g not supported). */
+pisa_status pisa_pyramid_plan(pisa_pyramid* p, int32_t B, int32_t H_kv, int32_t d, int32_t C,
+                              int32_t g, int64_t N_cap);
+
+/* Build every level of the pyramid over the first N tokens of K
+ * (section 3.2 eq 15). K: device, dtype dt, [B][N_cap][H_kv][d]. Writes levels
+ * 1..L(N) of p->buf. Summaries are fp32 sums in token (or child) order
+ * divided by the count. Errors: PISA_EINVAL (null pointers, N < 1),
+ * PISA_ENOSPACE (N > N_cap). */
+pisa_status pisa_build_pyramid(const pisa_pyramid* p, const void* K, pisa_dtype dt, int64_t N,
+                               void* stream);
+
+/* Decode cache update (section 3.3, "Decoding": only the current leaf mean and
+ * its ancestor path change when a token is appended). K: device
+ * [B][N_cap][H_kv][d] already holding the new token of sequence b at position
+ * seqlen[b] - 1. seqlen: device int64 [B], lengths after the append
+ * (1 <= seqlen[b] <= N_cap, not checked on the host: lengths live on the
+ * device). Recomputes, per (b, h), leaf floor((seqlen[b]-1)/C) and each of its
+ * ancestors up to level L(seqlen[b]) in the same order as
+ * pisa_build_pyramid, so the result is bit-identical to a rebuild.
+ * The previous lengths must have been built or appended one token at a time. */
+pisa_status pisa_pyramid_append(const pisa_pyramid* p, const void* K, pisa_dtype dt,
+                                const int64_t* seqlen, void* stream);
+
+/* Workspace bytes pisa_route_prefill needs for these arguments (0 for
+ * PISA_ROUTE_FUSED). */
+pisa_status pisa_route_prefill_workspace(const pisa_pyramid* p, int64_t N, int32_t H_q,
+                                         int32_t K_top, int32_t mode, size_t* bytes);
+
+/*
+ * Prefill routing (section 3.2 eq 16-22, appendix B). For every sequence b,
+ * position t < N and KV head h: starting from the single top block, at each
+ * level drop candidates that start after t (causal), keep all candidates if
+ * at most K_top remain, otherwise keep the forced nodes (ancestors of the
+ * first, previous and current leaf; causal only) plus the best
+ * K_top - |forced| others by the grouped LSE score
+ *     u_i = sum over the G_Q query heads h' of KV head h of
+ *           log sum_{r in children(i)} exp(q_{t,h'} . kbar_r / sqrt(d)),
+ * (leaves use their raw keys as children), ties to the lower index; then
+ * expand the kept nodes to their children. fp32 dot products and reductions.
+ *
+ * Q: device [B][N][H_q][d]; K: the keys the pyramid was built from
+ * ([B][N_cap][H_kv][d], dtype dt); the pyramid must hold a build over N.
+ * idx: device int32 [B][H_kv][N][K_top], ascending block ids, -1 padded.
+ * score: device float32 [B][H_kv][N][K_top] or NULL: the leaf-level u of a
+ * block kept by ranking, +inf for a block kept without a score, -inf padding.
+ * ws: device workspace of ws_bytes >= pisa_route_prefill_workspace().
+ * gqa_group must equal H_q / p->H_kv. causal: 1 = causal routing with the
+ * forced set, 0 = no eligibility filter and no forced set.
+ * Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE (N > N_cap or the
+ * workspace is too small), PISA_EHIP.
+ */
+pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void* K,
+                               pisa_dtype dt, int64_t N, int32_t H_q, int32_t K_top,
+                               int32_t causal, int32_t gqa_group, int32_t mode, int32_t* idx,
+                               float* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode routing (section 3.3, "Decoding"): the single-program selector that
+ * continues from the top level down to the leaves, for the newest token of
+ * each sequence (position seqlen[b] - 1, sequence length seqlen[b]), causal,
+ * with the same rules as pisa_route_prefill.
+ * q: device [B][H_q][d]; K: device [B][N_cap][H_kv][d]; seqlen: device int64 [B].
+ * idx: device int32 [B][H_kv][K_top]; score: device float32 [B][H_kv][K_top] or NULL.
+ */
+pisa_status pisa_route_decode(const pisa_pyramid* p, const void* q, const void* K,
+                              pisa_dtype dt, const int64_t* seqlen, int32_t H_q, int32_t K_top,
+                              int32_t gqa_group, int32_t* idx, float* score, void* stream);
+
+/*
+ * Block-sparse attention forward (section 3.1 eq 6). Query row r of sequence
+ * b sits at position kv_len[b] - N_q + r (kv_len NULL: every sequence has
+ * N_kv keys, so row r is position r when N_q = N_kv). It attends to the keys
+ * j < kv_len[b] of the blocks listed for its KV head, and under causal
+ * masking only to j <= its position (appendix B).
+ * Q: device [B][N_q][H_q][d]; K, V: device [B][N_alloc][H_kv][d];
+ * block_idx: device int32 [B][H_kv][N_q][K_top], -1 entries ignored, ids
+ * distinct per row; O: device [B][N_q][H_q][d], dtype dt;
+ * lse: device float32 [B][H_q][N_q] (natural-log normaliser) or NULL.
+ * A row with no visible key gets O = 0 and lse = -inf.
+ * fp32 softmax statistics and accumulation.
+ */
+pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_dtype dt,
+                             int32_t B, int64_t N_q, int64_t N_kv, int64_t N_alloc, int32_t H_q,
+                             int32_t H_kv, int32_t d, int32_t C, const int32_t* block_idx,
+                             int32_t K_top, int32_t causal, const int64_t* kv_len, void* O,
+                             float* lse, void* stream);
+
+/* Workspace bytes pisa_bsa_select needs. */
+pisa_status pisa_bsa_workspace(const pisa_pyramid* p, int64_t N, int32_t H_q, size_t* bytes);
+
+/*
+ * Exhaustive single-level selector in the style of BSA (section 3.1 eq 2-5),
+ * the comparison point: every eligible leaf (start <= t when causal) except
+ * the forced ones is scored by z = q_{t,h'} . kbar_i / sqrt(d) with the level-1
+ * summaries of the pyramid; z is normalised by a softmax over those leaves
+ * within each query head, and the G_Q probabilities are summed (the grouped
+ * rule the page gives for its BSA baseline). Keeps the forced leaves plus the
+ * best K_top - |forced|; keeps everything eligible when at most K_top leaves
+ * are eligible. Arguments and outputs as pisa_route_prefill; score holds the
+ * summed probability (+inf for blocks kept without a score).
+ */
+pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt, int64_t N,
+                            int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group,
+                            int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* pisa_status_str(pisa_status s);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* pisa_last_error(void);
+
+/* PISA_ABI_VERSION of the library. */
+int32_t pisa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H */

@@ -1,0 +1,135 @@
+"""GPU parity of the pyramid build and of prefill routing (fused and two-stage)
+against the CPU oracle, through the C ABI (hierarchical_top_amd.pisa)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hierarchical_top_amd import pisa, synth
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"two_stage": pisa.TWO_STAGE, "fused": pisa.FUSED}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def custom(name, **kw):
+    return synth.workload(name, **kw)
+
+
+CASES = {
+    "tiny": custom("tiny"),
+    # ragged tail (partial leaf and partial nodes), grouped heads, bf16
+    "ragged": synth.Workload("ragged", 1, 1000, 4, 2, 64, 16, 4, 8, "bf16", 0, 21, False),
+    # two sequences, eight-head groups, d=128
+    "batch2_g8": synth.Workload("b2g8", 2, 3000, 16, 2, 128, 32, 2, 8, "bf16", 4, 22, False),
+    # the page's grouping (16 query heads per KV head), g=2, d=64
+    "paper_shape": synth.Workload("paper", 1, 4096, 32, 2, 64, 64, 2, 8, "bf16", 0, 23, False),
+    # fp32 with two-head groups
+    "f32_g2": synth.Workload("f32g2", 1, 777, 4, 2, 64, 16, 2, 6, "f32", 0, 24, False),
+    "p16k": custom("p16k"),
+}
+
+
+def _inputs(w):
+    Q, K, V, _ = synth.make_prefill(w)
+    return Q, K
+
+
+def _oracle_route(w, Q, K, K_top, causal, t):
+    pyr = oracle.Pyramid(K.float().numpy(), w.N, w.C, w.g)
+    res = []
+    for b in range(w.B):
+        res.append(oracle.route(pyr, Q[b, t].float().numpy(), [b] * len(t), t, K_top, causal=causal))
+    return pyr, res
+
+
+def _gpu_route(w, Q, K, K_top, causal, mode):
+    Qd, Kd = Q.cuda(), K.cuda()
+    pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
+    pyr.build(Kd, w.N)
+    idx, score = pisa.route_prefill(pyr, Qd, Kd, w.N, K_top, causal=causal, mode=mode, with_score=True)
+    torch.cuda.synchronize()
+    return pyr, idx.cpu().numpy(), score.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "batch2_g8", "p16k"])
+def test_pyramid_build_matches_oracle(case):
+    """fp32 sums in token order vs fp64: |err| <= (n - 1) * 2^-24 * sum|x| / n + ulp, bounded
+    here by 4e-5 for |x| <= 20 (planted keys are N(0,1) * 3 rounded to bf16)."""
+    w = CASES[case]
+    Q, K = _inputs(w)
+    opyr = oracle.Pyramid(K.float().numpy(), w.N, w.C, w.g)
+    pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
+    pyr.build(K.cuda(), w.N)
+    torch.cuda.synchronize()
+    for l in range(1, opyr.L + 1):
+        got = pyr.level(l)[:, :, :opyr.M[l]].double().cpu().numpy()
+        np.testing.assert_allclose(got, opyr.level(l), rtol=0, atol=4e-5, err_msg="level %d" % l)
+
+
+def _positions(w, sample):
+    if sample is None or sample >= w.N:
+        return np.arange(w.N)
+    t = np.unique(np.concatenate([np.linspace(0, w.N - 1, sample).astype(np.int64), np.arange(3 * w.C),
+                                  np.arange(w.N - w.C, w.N)]))
+    return t
+
+
+@pytest.mark.parametrize("mode", ["two_stage", "fused"])
+@pytest.mark.parametrize("case,K_top,causal,sample", [
+    ("tiny", 4, True, None),
+    ("tiny", 32, True, None),
+    ("tiny", 64, True, None),
+    ("tiny", 4, False, None),
+    ("ragged", 8, True, None),
+    ("ragged", 8, False, None),
+    ("batch2_g8", 8, True, None),
+    ("paper_shape", 8, True, None),
+    ("f32_g2", 6, True, None),
+    ("p16k", 8, True, None),
+])
+def test_route_matches_oracle(mode, case, K_top, causal, sample):
+    w = CASES[case]
+    print("case", case, "mode", mode, "K_top", K_top, "causal", causal, flush=True)
+    Q, K = _inputs(w)
+    t = _positions(w, sample)
+    _, orc = _oracle_route(w, Q, K, K_top, causal, t)
+    _, idx, score = _gpu_route(w, Q, K, K_top, causal, MODES[mode])
+    M1 = -(-w.N // w.C)
+    for b in range(w.B):
+        gi = idx[b][:, t].transpose(1, 0, 2)
+        gs = score[b][:, t].transpose(1, 0, 2)
+        stats = compare(gi, gs, orc[b], t, w.C, K_top, causal=causal, M1=M1)
+        print(case, mode, b, stats)
+
+
+def test_fused_and_two_stage_agree_and_are_deterministic():
+    w = CASES["p16k"]
+    Q, K = _inputs(w)
+    _, i1, s1 = _gpu_route(w, Q, K, 8, True, pisa.TWO_STAGE)
+    _, i2, s2 = _gpu_route(w, Q, K, 8, True, pisa.TWO_STAGE)
+    _, i3, s3 = _gpu_route(w, Q, K, 8, True, pisa.FUSED)
+    assert (i1 == i2).all() and np.array_equal(s1, s2, equal_nan=True)  # bit-identical reruns
+    diff = (i1 != i3).any(-1).mean()
+    assert diff < 0.01, "fused and two-stage disagree on %.4f of the selections" % diff
+
+
+def test_outputs_are_fully_written():
+    w = CASES["ragged"]
+    Q, K = _inputs(w)
+    Qd, Kd = Q.cuda(), K.cuda()
+    pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
+    pyr.build(Kd, w.N)
+    for mode in (pisa.TWO_STAGE, pisa.FUSED):
+        out = torch.full((w.B, w.H_kv, w.N, 8), -7, dtype=torch.int32, device="cuda")
+        sc = torch.full((w.B, w.H_kv, w.N, 8), 12345.0, dtype=torch.float32, device="cuda")
+        pisa.route_prefill(pyr, Qd, Kd, w.N, 8, mode=mode, with_score=True, out=out, score_out=sc)
+        torch.cuda.synchronize()
+        assert not (out == -7).any() and not (sc == 12345.0).any()
