@@ -34,7 +34,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
     const int64_t r = item % a.N_q;
     const int h = (int)((item / a.N_q) % a.H_kv);
     const int b = (int)(item / ((int64_t)a.N_q * a.H_kv));
-    const int64_t nb = a.kv_len ? a.kv_len[b] : a.N_kv;
+    int64_t nb = a.kv_len ? a.kv_len[b] : a.N_kv;  // lengths may live on the device: keep them in range
+    nb = nb < 0 ? 0 : (nb > a.N_alloc ? a.N_alloc : nb);
     const int64_t pos = nb - a.N_q + r;
     const int C = a.C;
 

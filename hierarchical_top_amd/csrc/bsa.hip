@@ -1,5 +1,328 @@
-// bsa.hip -- exhaustive selector (placeholder until the MFMA kernel lands).
+// bsa.hip -- exhaustive single-level block selection in the style of BSA
+// ("Block Sparse Attention with Log-Linear Complexity", section 3.1 eq 2-5,
+// with the per-head normalisation its BSA baseline applies before summing the
+// heads of a group), the same-GPU comparison point for the pyramid router.
+//
+// Workgroup = 8 waves x QT queries of one KV head (QT = 16 / (G_Q * terms)).
+// Leaf means (pyramid level 1, fp32) are staged 64 at a time in LDS as two
+// bf16 terms and multiplied with the queries on MFMA (rows = query heads,
+// columns = leaves). Two sweeps over the eligible leaves:
+//   1. per head, a running base-2 log-sum-exp over the scored leaves;
+//   2. p = exp(z - lse) per head, u = sum over the group's heads, and a
+//      streaming top-(K_top - |forced|) list per lane; the 16 lanes of a
+//      query merge their lists with shuffles at the end.
+#include "pisa_device.hpp"
 #include "pisa_internal.hpp"
+
 namespace pisa {
-hipError_t launch_bsa(const BsaArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
+
+constexpr int kBsaWaves = 8;
+constexpr int kBsaKMax = 8;  // largest K_top the exhaustive selector supports
+
+template <int D, typename T, int G>
+__global__ __launch_bounds__(512) void bsa_kernel(BsaArgs a)
+{
+    constexpr int TA = Src<T>::TERMS;
+    constexpr int R = G * TA;           // rows per query
+    constexpr int QT = 16 / R;          // queries per wave
+    constexpr int NQ = R <= 4 ? 4 / R : 1;  // queries held by one lane group
+    constexpr int HG = R / TA;           // distinct head rows per query
+    constexpr int KS = D / 32;
+    constexpr int LDW = D + 8;
+    __shared__ __attribute__((aligned(16))) bf16 s_m[2][64 * LDW];
+
+    const PyrArgs& p = a.p;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4;
+    const int64_t N = a.N;
+    const int64_t per_wg = (int64_t)kBsaWaves * QT;
+    const int64_t ntile = (N + per_wg - 1) / per_wg;
+    const int64_t bh = blockIdx.x / ntile;
+    const int64_t t0 = (blockIdx.x % ntile) * per_wg;
+    const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+    const int64_t M1 = (N + p.C - 1) >> p.c_log2;
+    const float* lev1 = p.buf + p.off[1] + ((int64_t)b * p.H + h) * p.M_cap[1] * D;
+
+    // A operand rows
+    bf16x8 qa[KS];
+    {
+        const int r = lane & 15;
+        const int ql = r / R, term = (r % R) / G, head = r % G;
+        const int64_t tq = t0 + (int64_t)wave * QT + ql;
+        const bool has = tq < N;
+        const T* qp = (const T*)a.Q + (((int64_t)b * N + (has ? tq : 0)) * a.H_q + (int64_t)h * G + head) * D + 8 * (lane >> 4);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 vh, vl;
+            Src<T>::load(qp + 32 * s, has, vh, vl);
+            qa[s] = term == 0 ? vh : vl;
+        }
+    }
+    // per row i of this lane: its query and whether it scores at all
+    int64_t tq_i[4], c_i[4];
+    bool live_i[4], prim_i[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lg + i;
+        const int ql = r / R, rq = r % R;
+        tq_i[i] = t0 + (int64_t)wave * QT + ql;
+        c_i[i] = tq_i[i] >> p.c_log2;
+        const int64_t E = a.causal ? c_i[i] + 1 : M1;
+        live_i[i] = tq_i[i] < N && E > a.K_top;
+        prim_i[i] = (rq / G) == 0;
+    }
+    const int64_t tlast = min(N - 1, t0 + per_wg - 1);
+    const int64_t last_leaf = a.causal ? (tlast >> p.c_log2) : M1 - 1;
+    const int nchunks = (int)(last_leaf / 64) + 1;
+    const float scale = kLog2e * rsqrtf((float)D);
+
+    float m2[4], s2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m2[i] = -INFINITY; s2[i] = 0.f; }
+    // top lists: per lane, per held query q (NQ), KMAX entries in selection order
+    float tu[NQ][kBsaKMax];
+    int ti[NQ][kBsaKMax];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int j = 0; j < kBsaKMax; ++j) { tu[q][j] = -INFINITY; ti[q][j] = 0x7fffffff; }
+    // number of ranked picks of each held query
+    int rk[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int r = R <= 4 ? 4 * lg + q * R : 4 * lg;
+        const int64_t tq = t0 + (int64_t)wave * QT + r / R;
+        const int64_t c = tq >> p.c_log2;
+        const int nF = a.causal ? (c == 0 ? 1 : (c == 1 ? 2 : 3)) : 0;
+        rk[q] = a.K_top - nF;
+    }
+
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int ch = 0; ch < nchunks; ++ch) {
+            __syncthreads();
+            for (int i = threadIdx.x; i < 64 * (D / 8); i += 64 * kBsaWaves) {
+                const int rr = i / (D / 8), c8 = i % (D / 8);
+                const int64_t leaf = (int64_t)ch * 64 + rr;
+                bf16x8 vh, vl;
+                Src<float>::load(lev1 + (leaf < M1 ? leaf : 0) * D + 8 * c8, leaf < M1, vh, vl);
+                *reinterpret_cast<bf16x8*>(&s_m[0][rr * LDW + 8 * c8]) = vh;
+                *reinterpret_cast<bf16x8*>(&s_m[1][rr * LDW + 8 * c8]) = vl;
+            }
+            __syncthreads();
+            float y[4][4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const int rr = 16 * ct + (lane & 15);
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&s_m[0][rr * LDW + 32 * s + 8 * lg]);
+                    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&s_m[1][rr * LDW + 32 * s + 8 * lg]);
+                    acc = mfma(qa[s], bh, acc);
+                    acc = mfma(qa[s], bl, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[ct][i] = acc[i];
+            }
+            if constexpr (TA == 2) {
+                if constexpr (R <= 4) {
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int j = (i + G < 4) ? i + G : i;
+                            if (prim_i[i] && j != i) y[ct][i] += y[ct][j];
+                        }
+                } else {
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) y[ct][i] += shfl_xor(y[ct][i], 16 * (R / 8));
+                }
+            }
+            // mask: eligible, not forced, query live
+            bool ok[4][4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int64_t leaf = (int64_t)ch * 64 + 16 * ct + (lane & 15);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t c = c_i[i];
+                    bool v = live_i[i] && leaf < M1;
+                    if (a.causal) v = v && leaf <= c && leaf != 0 && leaf != c && leaf != c - 1;
+                    ok[ct][i] = v;
+                    y[ct][i] *= scale;
+                }
+            }
+            if (pass == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float cm = -INFINITY;
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) if (ok[ct][i]) cm = fmaxf(cm, y[ct][i]);
+                    if (cm > m2[i]) {
+                        s2[i] = (m2[i] == -INFINITY) ? 0.f : s2[i] * __builtin_amdgcn_exp2f(m2[i] - cm);
+                        m2[i] = cm;
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        if (ok[ct][i]) s2[i] += __builtin_amdgcn_exp2f(y[ct][i] - m2[i]);
+                }
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    float pv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        pv[i] = (ok[ct][i] && prim_i[i]) ? __builtin_amdgcn_exp2f(y[ct][i] - m2[i]) : 0.f;
+                    const int leaf = ch * 64 + 16 * ct + (lane & 15);
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        float u = 0.f;
+                        bool any = false;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const bool mine = R <= 4 ? (i / R == q) : true;
+                            if (mine) { u += pv[i]; any = any || ok[ct][i]; }
+                        }
+                        if constexpr (HG > 4) u += shfl_xor(u, 16);
+                        if constexpr (HG > 8) u += shfl_xor(u, 32);
+                        if (any) {
+                            float xu = u;
+                            int xi = leaf;
+#pragma unroll
+                            for (int j = 0; j < kBsaKMax; ++j) {
+                                if (j < rk[q] && before(xu, xi, tu[q][j], ti[q][j])) {
+                                    const float t_ = tu[q][j]; tu[q][j] = xu; xu = t_;
+                                    const int i_ = ti[q][j]; ti[q][j] = xi; xi = i_;
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if (pass == 0) {
+            // combine the 16 lanes of each row: (m, s) -> base-2 log-sum-exp
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float m = m2[i], s = s2[i];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    const float mo = shfl_xor(m, o), so = shfl_xor(s, o);
+                    const float mn = fmaxf(m, mo);
+                    if (mn != -INFINITY)
+                        s = (m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f(m - mn)) +
+                            (mo == -INFINITY ? 0.f : so * __builtin_amdgcn_exp2f(mo - mn));
+                    m = mn;
+                }
+                m2[i] = (m == -INFINITY) ? INFINITY : m + __builtin_amdgcn_logf(s);  // lse of the row
+            }
+        }
+    }
+
+    // merge the per-lane lists of each query over its 16 lanes
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            float ou[kBsaKMax];
+            int oi[kBsaKMax];
+#pragma unroll
+            for (int j = 0; j < kBsaKMax; ++j) { ou[j] = shfl_xor(tu[q][j], o); oi[j] = shfl_xor(ti[q][j], o); }
+#pragma unroll
+            for (int k = 0; k < kBsaKMax; ++k) {
+                float xu = ou[k];
+                int xi = oi[k];
+                if (xi == 0x7fffffff) continue;
+#pragma unroll
+                for (int j = 0; j < kBsaKMax; ++j) {
+                    if (j < rk[q] && before(xu, xi, tu[q][j], ti[q][j])) {
+                        const float t_ = tu[q][j]; tu[q][j] = xu; xu = t_;
+                        const int i_ = ti[q][j]; ti[q][j] = xi; xi = i_;
+                    }
+                }
+            }
+        }
+    }
+
+    // writers: lane (lane & 15) == 0 of the first lane group of each query
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        int qtile;
+        bool writer;
+        if constexpr (R <= 4) {
+            qtile = lg * NQ + q;
+            writer = (lane & 15) == 0;
+        } else {
+            qtile = lg / (R / 4);
+            writer = (lane & 15) == 0 && (lg % (R / 4)) == 0;
+        }
+        const int64_t tq = t0 + (int64_t)wave * QT + qtile;
+        if (!writer || tq >= N) continue;
+        const int64_t c = tq >> p.c_log2;
+        const int64_t E = a.causal ? c + 1 : M1;
+        int ids[kBsaKMax + 4];
+        float val[kBsaKMax + 4];
+#pragma unroll
+        for (int j = 0; j < kBsaKMax + 4; ++j) { ids[j] = 0x7fffffff; val[j] = -INFINITY; }
+        auto put = [&](int x, float v) {
+#pragma unroll
+            for (int j = 0; j < kBsaKMax + 4; ++j)
+                if (x < ids[j]) {
+                    const int i_ = ids[j]; ids[j] = x; x = i_;
+                    const float v_ = val[j]; val[j] = v; v = v_;
+                }
+        };
+        if (E <= a.K_top) {
+            for (int64_t l = 0; l < E; ++l) put((int)l, INFINITY);
+        } else {
+            if (a.causal) {
+                put(0, INFINITY);
+                if (c != 0) put((int)c, INFINITY);
+                if (c - 1 >= 1) put((int)(c - 1), INFINITY);
+            }
+#pragma unroll
+            for (int j = 0; j < kBsaKMax; ++j)
+                if (j < rk[q] && ti[q][j] != 0x7fffffff) put(ti[q][j], tu[q][j]);
+        }
+        const int64_t base = (((int64_t)b * p.H + h) * N + tq) * a.K_top;
+#pragma unroll
+        for (int j = 0; j < kBsaKMax + 4; ++j) {
+            if (j < a.K_top) {
+                const bool okj = ids[j] != 0x7fffffff;
+                a.idx[base + j] = okj ? ids[j] : -1;
+                if (a.score) a.score[base + j] = okj ? val[j] : -INFINITY;
+            }
+        }
+    }
+}
+
+template <int D, typename T>
+static hipError_t bsa_d(const BsaArgs& a, hipStream_t s)
+{
+    const int R = a.G * Src<T>::TERMS;
+    const int64_t per_wg = (int64_t)kBsaWaves * (16 / R);
+    const int64_t grid = (int64_t)a.p.B * a.p.H * ((a.N + per_wg - 1) / per_wg);
+    switch (a.G) {
+    case 1: hipLaunchKernelGGL((bsa_kernel<D, T, 1>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((bsa_kernel<D, T, 2>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((bsa_kernel<D, T, 4>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((bsa_kernel<D, T, 8>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
+    case 16:
+        if constexpr (Src<T>::TERMS == 1) {
+            hipLaunchKernelGGL((bsa_kernel<D, T, 16>), dim3((unsigned)grid), dim3(512), 0, s, a);
+            break;
+        }
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bsa(const BsaArgs& a, int dtype, int d, hipStream_t s)
+{
+    if (dtype == 0) return d == 64 ? bsa_d<64, float>(a, s) : bsa_d<128, float>(a, s);
+    return d == 64 ? bsa_d<64, bf16>(a, s) : bsa_d<128, bf16>(a, s);
+}
+
 }  // namespace pisa

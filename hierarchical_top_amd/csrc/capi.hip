@@ -337,17 +337,9 @@ pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_d
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn");
 }
 
-pisa_status pisa_bsa_workspace(const pisa_pyramid* p, int64_t N, int32_t H_q, size_t* bytes)
-{
-    if (!p || !bytes) return fail(PISA_EINVAL, "NULL argument");
-    if (N < 1 || H_q < 1) return fail(PISA_EINVAL, "N and H_q must be positive");
-    *bytes = al((size_t)p->B * H_q * N * 4);
-    return ok();
-}
-
 pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt, int64_t N, int32_t H_q,
-                            int32_t K_top, int32_t causal, int32_t gqa_group, int32_t* idx, float* score, void* ws,
-                            size_t ws_bytes, void* stream)
+                            int32_t K_top, int32_t causal, int32_t gqa_group, int32_t* idx, float* score,
+                            void* stream)
 {
     pisa_status s = check_pyramid(p);
     if (s != PISA_OK) return s;
@@ -359,15 +351,14 @@ pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt,
     const int G = gqa_group;
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return fail(PISA_EUNSUPPORTED, "gqa_group=%d", G);
     if (dt == PISA_F32 && G > 8) return fail(PISA_EUNSUPPORTED, "f32 selection supports gqa_group <= 8");
-    if (K_top < 1 || K_top > 32) return fail(PISA_EUNSUPPORTED, "exhaustive selector supports K_top <= 32");
+    if (K_top < 1) return fail(PISA_EINVAL, "K_top=%d < 1", K_top);
+    if (K_top > 8) return fail(PISA_EUNSUPPORTED, "exhaustive selector supports K_top <= 8");
     if (causal && K_top < 3) return fail(PISA_EINVAL, "causal selection needs K_top >= 3");
     if (!Q || !idx || !aligned16(Q)) return fail(PISA_EINVAL, "Q and idx must be non-NULL, Q 16-byte aligned");
-    size_t need = al((size_t)p->B * H_q * N * 4);
-    if (!ws || ws_bytes < need) return fail(PISA_ENOSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
     BsaArgs a;
     memset(&a, 0, sizeof(a));
     a.p = pyr_args(p); a.Q = Q; a.N = N; a.H_q = H_q; a.G = G; a.K_top = K_top; a.causal = causal ? 1 : 0;
-    a.row_lse = (float*)ws; a.idx = idx; a.score = score;
+    a.idx = idx; a.score = score;
     hipError_t e = launch_bsa(a, dt == PISA_F32 ? 0 : 1, p->d, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_bsa_select");
 }

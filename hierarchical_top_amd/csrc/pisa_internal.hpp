@@ -88,7 +88,6 @@ struct BsaArgs {
     const void* Q;
     int64_t N;
     int H_q, G, K_top, causal;
-    float* row_lse;  // [B][H_q][N] (workspace)
     int32_t* idx;
     float* score;
 };

@@ -61,8 +61,7 @@ def lib():
             "pisa_route_decode": [P, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_sparse_attn": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p,
                                  c_i32, c_i32, c_p, c_p, c_p, c_p],
-            "pisa_bsa_workspace": [P, c_i64, c_i32, ctypes.POINTER(c_size)],
-            "pisa_bsa_select": [P, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_size, c_p],
+            "pisa_bsa_select": [P, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -79,7 +78,7 @@ def lib():
 
 
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
-           "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_bsa_workspace", "pisa_bsa_select",
+           "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_bsa_select",
            "pisa_status_str", "pisa_last_error", "pisa_abi_version"]
 
 
@@ -205,16 +204,15 @@ def sparse_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, block_idx: to
 
 
 def bsa_select(pyr: Pyramid, Q: torch.Tensor, N: int, K_top: int, causal: bool = True, with_score: bool = False,
-               workspace: torch.Tensor | None = None):
+               out: torch.Tensor | None = None, score_out: torch.Tensor | None = None):
     """Exhaustive single-level selection (comparison point); returns idx [B][H_kv][N][K_top]."""
     _dev(Q)
     B, Nq, H_q, d = Q.shape
-    idx = torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.int32, device=Q.device)
-    score = torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.float32, device=Q.device) if with_score else None
-    n = c_size(0)
-    _check(lib().pisa_bsa_workspace(ctypes.byref(pyr.desc), N, H_q, ctypes.byref(n)))
-    ws = workspace if workspace is not None and workspace.numel() >= n.value else \
-        torch.empty(int(n.value), dtype=torch.uint8, device=Q.device)
+    idx = out if out is not None else torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.int32, device=Q.device)
+    score = None
+    if with_score:
+        score = score_out if score_out is not None else torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.float32,
+                                                                    device=Q.device)
     _check(lib().pisa_bsa_select(ctypes.byref(pyr.desc), _ptr(Q), _dt(Q), N, H_q, K_top, 1 if causal else 0,
-                                 H_q // pyr.H_kv, _ptr(idx), _ptr(score), _ptr(ws), int(n.value), _stream()))
+                                 H_q // pyr.H_kv, _ptr(idx), _ptr(score), _stream()))
     return (idx, score) if with_score else idx

@@ -177,9 +177,6 @@ pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_d
                              int32_t K_top, int32_t causal, const int64_t* kv_len, void* O,
                              float* lse, void* stream);
 
-/* Workspace bytes pisa_bsa_select needs. */
-pisa_status pisa_bsa_workspace(const pisa_pyramid* p, int64_t N, int32_t H_q, size_t* bytes);
-
 /*
  * Exhaustive single-level selector in the style of BSA (section 3.1 eq 2-5),
  * the comparison point: every eligible leaf (start <= t when causal) except
@@ -187,13 +184,15 @@ pisa_status pisa_bsa_workspace(const pisa_pyramid* p, int64_t N, int32_t H_q, si
  * summaries of the pyramid; z is normalised by a softmax over those leaves
  * within each query head, and the G_Q probabilities are summed (the grouped
  * rule the page gives for its BSA baseline). Keeps the forced leaves plus the
- * best K_top - |forced|; keeps everything eligible when at most K_top leaves
- * are eligible. Arguments and outputs as pisa_route_prefill; score holds the
- * summed probability (+inf for blocks kept without a score).
+ * best K_top - |forced| (ties to the lower index); keeps everything eligible
+ * when at most K_top leaves are eligible. Q, idx and score as in
+ * pisa_route_prefill; score holds the summed probability (+inf for blocks
+ * kept without a score). The pyramid must hold a build over N.
+ * Supported: K_top <= 8. Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE.
  */
 pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt, int64_t N,
                             int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group,
-                            int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
+                            int32_t* idx, float* score, void* stream);
 
 /* Static description of a status code. */
 const char* pisa_status_str(pisa_status s);

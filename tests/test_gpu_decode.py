@@ -1,0 +1,133 @@
+"""GPU decode path: incremental pyramid (bit-identical to a rebuild), the
+single-program decode router (against the oracle routing the newest token of
+the prefix), and decode-shaped attention, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hierarchical_top_amd import pisa, synth
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _rebuild_equal(pyr, K, b, n):
+    """Levels of sequence b in the incremental pyramid equal a fresh build over K[b, :n]."""
+    fresh = pisa.Pyramid(1, pyr.H_kv, pyr.d, pyr.C, pyr.g, pyr.N_cap)
+    fresh.build(K[b:b + 1].contiguous(), n)
+    M = oracle.levels(n, pyr.C, pyr.g)
+    for l in range(1, len(M)):
+        a = pyr.level(l)[b, :, :M[l]]
+        c = fresh.level(l)[0, :, :M[l]]
+        if not torch.equal(a, c):
+            return "level %d differs (max %g)" % (l, (a - c).abs().max().item())
+    return None
+
+
+def _check_route(K, q, b, n, C, g, K_top, idx, score):
+    opyr = oracle.Pyramid(K[b:b + 1, :n].float().cpu().numpy(), n, C, g)
+    orc = oracle.route(opyr, q[b:b + 1].float().cpu().numpy(), [0], [n - 1], K_top)
+    st = compare(idx[b:b + 1].cpu().numpy(), score[b:b + 1].cpu().numpy(), orc, np.array([n - 1]), C, K_top,
+                 max_near_tie_frac=1.0)
+    return st, orc["idx"]
+
+
+def test_decode_small_ragged_lengths():
+    B, H_q, H, d, C, g, K_top = 3, 4, 2, 64, 16, 4, 8
+    N0, steps = 1000, 100
+    cap = N0 + steps
+    gen = torch.Generator().manual_seed(41)
+    K_all = torch.randn(B, cap, H, d, generator=gen).to(torch.bfloat16)
+    q_all = torch.randn(steps, B, H_q, d, generator=gen).to(torch.bfloat16)
+    Kc = K_all.clone()
+    Kc[:, N0:] = 1e4  # not yet appended: must never be read
+    Kc = Kc.cuda()
+    pyr = pisa.Pyramid(B, H, d, C, g, cap)
+    pyr.build(Kc, N0)
+    lens = [N0] * B
+    checked = 0
+    for s in range(steps):
+        for b in range(B):
+            if s % (b + 1) == 0:  # sequences grow at different rates
+                Kc[b, lens[b]] = K_all[b, lens[b]].cuda()
+                lens[b] += 1
+        seqlen = torch.tensor(lens, dtype=torch.int64, device="cuda")
+        pyr.append(Kc, seqlen)
+        q = q_all[s].cuda()
+        idx, score = pisa.route_decode(pyr, q, Kc, seqlen, K_top, with_score=True)
+        torch.cuda.synchronize()
+        for b in range(B):
+            err = _rebuild_equal(pyr, Kc, b, lens[b])
+            assert err is None, "step %d seq %d: %s" % (s, b, err)
+            _check_route(Kc, q, b, lens[b], C, g, K_top, idx, score)
+            checked += 1
+    assert lens[0] == N0 + steps and checked == steps * B
+
+
+def test_decode_first_level_growth_and_short_sequences():
+    """Lengths 1, 2, C, C+1 and the level-count boundary of a tiny cache."""
+    B, H_q, H, d, C, g, K_top = 4, 2, 1, 64, 16, 2, 4
+    cap = 300
+    gen = torch.Generator().manual_seed(42)
+    K = torch.randn(B, cap, H, d, generator=gen).to(torch.bfloat16).cuda()
+    pyr = pisa.Pyramid(B, H, d, C, g, cap)
+    pyr.build(K, 1)
+    cur = 1
+    for n in [1, 2, 15, 16, 17, 32, 33, 128, 129, 256, 257, 300]:
+        seqlen = torch.full((B,), n, dtype=torch.int64, device="cuda")
+        while cur < n:  # append one token at a time
+            cur += 1
+            pyr.append(K, torch.full((B,), cur, dtype=torch.int64, device="cuda"))
+        q = torch.randn(B, H_q, d, generator=gen).to(torch.bfloat16).cuda()
+        idx, score = pisa.route_decode(pyr, q, K, seqlen, K_top, with_score=True)
+        torch.cuda.synchronize()
+        for b in range(B):
+            assert _rebuild_equal(pyr, K, b, n) is None
+            _check_route(K, q, b, n, C, g, K_top, idx, score)
+
+
+def test_decode_full_size_sampled():
+    """The decode workload (32 sequences, 262144-token caches, 32 / 8 heads, d=128,
+    C=64, g=4, K_top=8): three appended tokens; sequences 0, 17, 31 checked
+    against the oracle and against a rebuild after the level count grows 7 -> 8."""
+    w = synth.workload("decode", steps=3)
+    print("generating caches", flush=True)
+    Kc, Vc, q, k, v = synth.make_decode(w, "cuda")
+    pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N + w.steps)
+    pyr.build(Kc, w.N)
+    torch.cuda.synchronize()
+    lens = w.N
+    for s in range(w.steps):
+        Kc[:, lens] = k[s]
+        Vc[:, lens] = v[s]
+        lens += 1
+        seqlen = torch.full((w.B,), lens, dtype=torch.int64, device="cuda")
+        pyr.append(Kc, seqlen)
+        idx, score = pisa.route_decode(pyr, q[s], Kc, seqlen, w.K_top, with_score=True)
+        torch.cuda.synchronize()
+        sel_o = {}
+        for b in (0, 17, 31):
+            print("step", s, "seq", b, flush=True)
+            assert _rebuild_equal(pyr, Kc, b, lens) is None
+            st, sel_o[b] = _check_route(Kc, q[s], b, lens, w.C, w.g, w.K_top, idx, score)
+            print(st)
+        # attention of the new tokens over the oracle's selections (decode shape, N_q = 1)
+        sel = idx.clone()
+        for b, o in sel_o.items():
+            sel[b] = torch.from_numpy(o[0]).cuda()
+        O = pisa.sparse_attn(q[s].unsqueeze(1).contiguous(), Kc, Vc, sel.unsqueeze(2).contiguous(), w.C, lens,
+                             kv_len=seqlen)
+        torch.cuda.synchronize()
+        for b, o in sel_o.items():
+            want = oracle.sparse_attn(q[s][b:b + 1].float().cpu().numpy(), [0], [lens - 1],
+                                      Kc[b:b + 1, :lens].float().cpu().numpy(),
+                                      Vc[b:b + 1, :lens].float().cpu().numpy(), lens, w.C, o)
+            np.testing.assert_allclose(O[b, 0].float().cpu().numpy(), want["out"][0], atol=2e-2)
+    assert oracle.levels(lens, w.C, w.g)[-1] == 1 and len(oracle.levels(lens, w.C, w.g)) - 1 == 8
