@@ -1,0 +1,371 @@
+"""Benchmark of PISA pyramid Top-K block selection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+
+One step = one pass of the selection path over the 262,144-token workload
+(batch 1, 16 query heads sharing 4 KV heads, d=128, C=64, g=4, K_top=8,
+causal, bf16 N(0,1) Q/K with 32 planted key blocks per KV head): the pyramid
+build followed by prefill routing of every position ("Block Sparse Attention
+with Log-Linear Complexity", appendix B: selection timings include the
+summary construction and every selection stage, not the attention).
+`value` is routed queries per second (positions x batch / step time) with
+inputs resident in HBM.
+
+Also reported (field "extra"): route-only time of both routers, the
+exhaustive BSA-style selector on the same inputs, the 16K and 64K prefill
+workloads, block-sparse attention at 64K, and decode (32 sequences, 262,144
+cached tokens, 256 appended tokens: append + route microseconds per step).
+
+Prints ONE JSON line. Only one GPU is used; --gpus above 1 exits with an error.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+import torch
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+from hierarchical_top_amd import pisa, synth, workcount  # noqa: E402
+
+METRIC = "routed queries/sec at 64K and 256K tokens (GQA prefill); decode route µs/step"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+STAGES_TWO = ["build", "upper", "cluster", "leaf", "final"]
+STAGES_FUSED = ["build", "route_fused"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def events():
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    return a, b
+
+
+class Prefill:
+    """Inputs, pyramid, workspace and outputs of one prefill workload on the GPU."""
+
+    def __init__(self, w: synth.Workload, with_v=False):
+        self.w = w
+        Q, K, V, _ = synth.make_prefill(w)
+        self.Q_cpu, self.K_cpu = Q, K
+        self.Q, self.K = Q.cuda(), K.cuda()
+        self.V = V.cuda() if (with_v and V is not None) else None
+        self.pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
+        need = pisa.route_workspace_bytes(self.pyr, w.N, w.H_q, w.K_top, pisa.TWO_STAGE)
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        self.idx = torch.empty(w.B, w.H_kv, w.N, w.K_top, dtype=torch.int32, device="cuda")
+        self.bidx = torch.empty_like(self.idx)
+
+    def step(self, mode, stage_events=None):
+        """Pyramid build + routing of every position."""
+        w = self.w
+        if stage_events:
+            for name, (a, b) in stage_events.items():
+                pisa.time_stage(name, a, b)
+        self.pyr.build(self.K, w.N)
+        pisa.route_prefill(self.pyr, self.Q, self.K, w.N, w.K_top, mode=mode, workspace=self.ws, out=self.idx)
+
+    def route_only(self, mode):
+        w = self.w
+        pisa.route_prefill(self.pyr, self.Q, self.K, w.N, w.K_top, mode=mode, workspace=self.ws, out=self.idx)
+
+    def bsa(self):
+        w = self.w
+        pisa.bsa_select(self.pyr, self.Q, w.N, w.K_top, out=self.bidx)
+
+
+def time_fn(fn, reps, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = events()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "hierarchical_top_amd" / "csrc").glob("*")):
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    f = ROOT / "profiles" / "traffic.json"
+    if not f.exists():
+        return None
+    try:
+        rec = json.loads(f.read_text()).get("%s/%s" % (workload, kernel))
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def roofline(stage, ms, w, traffic):
+    """Roofline entry of one stage from its average duration (ms per launch)."""
+    G = w.H_q // w.H_kv
+    rw = workcount.route_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.g, w.K_top)
+    if stage in ("build",):
+        byts = workcount.build_bytes(w.B, w.N, w.H_kv, w.d, w.C, w.g)
+        ach = byts / (ms * 1e-3) / 1e9
+        return dict(kernel=stage, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS,
+                    traffic=traffic, algorithmic=byts, ms_per_launch=ms)
+    flops = {"leaf": 2 * rw["leaf_mac"], "upper": 2 * rw["upper_mac"],
+             "route_fused": 2 * (rw["leaf_mac"] + rw["upper_mac"])}.get(stage)
+    if flops is None:  # clustering / final select: integer passes over the per-query lists
+        items = w.B * w.H_kv * w.N
+        byts = items * (w.K_top * 4 * 3 + 8) if stage == "cluster" else items * (w.K_top * 4 * 2 + 8 + w.g * w.K_top * 4)
+        ach = byts / (ms * 1e-3) / 1e9
+        return dict(kernel=stage, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS,
+                    traffic=traffic, algorithmic=byts, ms_per_launch=ms)
+    ach = flops / (ms * 1e-3) / 1e12
+    return dict(kernel=stage, bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=ach / PEAK_BF16_TFLOPS, traffic=traffic, algorithmic=flops, ms_per_launch=ms)
+
+
+def sample_positions(N, C, n):
+    t = np.linspace(0, N - 1, n).astype(np.int64)
+    return np.unique(np.concatenate([t, np.arange(3 * C), np.arange(N - C, N)]))
+
+
+def cpu_baseline(P: Prefill, budget_s: float):
+    """The oracle on the host cores: full pyramid build, then routing of a growing
+    evenly spaced sample of positions until about budget_s seconds of routing."""
+    import oracle  # test infrastructure: only this leg of the benchmark calls it
+    w = P.w
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    Kf = P.K_cpu.float().numpy()
+    t0 = time.perf_counter()
+    opyr = oracle.Pyramid(Kf, w.N, w.C, w.g)
+    t_build = time.perf_counter() - t0
+    n = 256
+    gpu_idx = P.idx.cpu().numpy()
+    while True:
+        t = sample_positions(w.N, w.C, n)
+        Qs = P.Q_cpu[0, t].float().numpy()
+        t0 = time.perf_counter()
+        orc = oracle.route(opyr, Qs, [0] * len(t), t, w.K_top, causal=True, threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n >= w.N:
+            break
+        n = min(w.N, int(n * max(2.0, 0.5 * budget_s / max(dt, 1e-3))))
+    # routing cost per query position, weighted to the full sequence by the scored work
+    full = workcount.route_work(w.B, w.N, w.H_kv, w.H_q // w.H_kv, w.d, w.C, w.g, w.K_top)
+    samp = workcount.route_work(w.B, w.N, w.H_kv, w.H_q // w.H_kv, w.d, w.C, w.g, w.K_top, positions=t)
+    scale = (full["upper_mac"] + full["leaf_mac"]) / max(1, samp["upper_mac"] + samp["leaf_mac"])
+    t_route_full = dt * scale
+    qps = w.B * w.N / (t_build + t_route_full)
+    # parity of the GPU selection on the sampled positions
+    gi = gpu_idx[0][:, t].transpose(1, 0, 2)
+    same = (gi == orc["idx"]).all(-1)
+    outside = orc["gap"] >= 1e-3
+    parity = dict(sampled_positions=int(len(t)), items=int(same.size), identical=int(same.sum()),
+                  near_tie_items=int((~outside).sum()),
+                  mismatches_outside_band=int((~same & outside).sum()), band=1e-3)
+    res = dict(value=qps, unit="queries/s", cores=threads, kind="oracle",
+               sample="full fp64 pyramid build (%.2f s) + routing of %d evenly spaced positions x %d KV heads "
+                      "(%.2f s), extrapolated to all %d positions by the scored work (x%.1f)"
+                      % (t_build, len(t), w.H_kv, dt, w.N, scale),
+               build_s=t_build, route_sample_s=dt)
+    return res, parity
+
+
+def decode_bench(reps_steps: int):
+    w = synth.workload("decode", steps=reps_steps)
+    Kc, Vc, q, k, v = synth.make_decode(w, "cuda")
+    pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N + w.steps)
+    pyr.build(Kc, w.N)
+    idx = torch.empty(w.B, w.H_kv, w.K_top, dtype=torch.int32, device="cuda")
+    O = torch.empty(w.B, 1, w.H_q, w.d, dtype=torch.bfloat16, device="cuda")
+    seqlens = [torch.full((w.B,), w.N + s + 1, dtype=torch.int64, device="cuda") for s in range(w.steps)]
+    torch.cuda.synchronize()
+    ev = [(events(), events(), events()) for _ in range(w.steps)]
+    for s in range(w.steps):
+        n = w.N + s + 1
+        Kc[:, n - 1] = k[s]
+        Vc[:, n - 1] = v[s]
+        (a0, a1), (r0, r1), (t0, t1) = ev[s]
+        pisa.time_stage("append", a0, a1)
+        pisa.time_stage("route_decode", r0, r1)
+        pisa.time_stage("attn", t0, t1)
+        pyr.append(Kc, seqlens[s])
+        pisa.route_decode(pyr, q[s], Kc, seqlens[s], w.K_top, out=idx)
+        pisa.sparse_attn(q[s].unsqueeze(1), Kc, Vc, idx.unsqueeze(2), w.C, n, kv_len=seqlens[s], out=O)
+    torch.cuda.synchronize()
+    app = np.array([a.elapsed_time(b) for (a, b), _, _ in ev]) * 1e3
+    rt = np.array([a.elapsed_time(b) for _, (a, b), _ in ev]) * 1e3
+    at = np.array([a.elapsed_time(b) for _, _, (a, b) in ev]) * 1e3
+    both = app + rt
+    dw = workcount.decode_work([w.N + w.steps // 2] * w.B, w.H_kv, w.H_q // w.H_kv, w.d, w.C, w.g, w.K_top)
+    gbs = dw["bytes"] / (np.median(rt) * 1e-6) / 1e9
+    res = dict(steps=w.steps, B=w.B, cache_tokens=w.N, route_us_median=float(np.median(rt)),
+               route_us_p99=float(np.percentile(rt, 99)), append_us_median=float(np.median(app)),
+               append_plus_route_us_median=float(np.median(both)),
+               append_plus_route_us_p99=float(np.percentile(both, 99)),
+               attn_us_median=float(np.median(at)),
+               route_gathered_bytes=dw["bytes"], route_hbm_gbs=gbs, route_hbm_frac=gbs / PEAK_HBM_GBS)
+    del Kc, Vc
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_extra(name, reps, with_attn=False):
+    w = synth.workload(name)
+    P = Prefill(w, with_v=with_attn)
+    G = w.H_q // w.H_kv
+    out = {}
+    for mname, mode in (("two_stage", pisa.TWO_STAGE), ("fused", pisa.FUSED)):
+        out["build_route_ms_" + mname] = time_fn(lambda: P.step(mode), reps)
+        out["route_ms_" + mname] = time_fn(lambda: P.route_only(mode), reps)
+    best = min(out["build_route_ms_two_stage"], out["build_route_ms_fused"])
+    out["routed_queries_per_s"] = w.B * w.N / (best * 1e-3)
+    out["bsa_ms"] = time_fn(P.bsa, max(2, reps // 2))
+    bw = workcount.bsa_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.K_top)
+    out["bsa_alg_tflops_one_pass"] = 2 * bw["mac"] / (out["bsa_ms"] * 1e-3) / 1e12
+    # the pages' comparison: selection with summary construction vs the exhaustive selector
+    # (whose level-1 means come from the same build)
+    bms = time_fn(lambda: P.pyr.build(P.K, w.N), reps)
+    out["build_ms"] = bms
+    out["speedup_vs_bsa"] = (out["bsa_ms"] + bms) / best
+    if with_attn:
+        P.step(pisa.TWO_STAGE)
+        O = torch.empty_like(P.Q)
+        ms = time_fn(lambda: pisa.sparse_attn(P.Q, P.K, P.V, P.idx, w.C, w.N, out=O), reps)
+        aw = workcount.attn_work(w.B, w.N, w.H_q, w.d, w.C, w.K_top)
+        out["attn_ms"] = ms
+        out["attn_tflops"] = 2 * aw["mac"] / (ms * 1e-3) / 1e12
+        out["attn_mfma_frac"] = out["attn_tflops"] / PEAK_BF16_TFLOPS
+    del P
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", choices=["auto", "fused", "two_stage"], default="auto")
+    ap.add_argument("--quick", action="store_true", help="headline workload only (no extra workloads)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle routing to time")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the selection path is built and timed on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pisa.lib()  # fail loudly when the library is missing
+
+    w = synth.workload("p256k")
+    log("generating", w)
+    P = Prefill(w)
+    torch.cuda.synchronize()
+
+    # pick the router: both are timed once after warm-up
+    modes = {"two_stage": pisa.TWO_STAGE, "fused": pisa.FUSED}
+    pre = {m: time_fn(lambda: P.step(v), 3, warm=1) for m, v in modes.items()}
+    mname = min(pre, key=pre.get) if args.mode == "auto" else args.mode
+    mode = modes[mname]
+    stage_names = STAGES_TWO if mode == pisa.TWO_STAGE else STAGES_FUSED
+    log("pre-measure ms/step", pre, "->", mname)
+
+    for _ in range(args.warmup):
+        P.step(mode)
+    stage_ev = [{s: events() for s in stage_names} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0, t1 = events()
+    t0.record()
+    for k in range(args.steps):
+        P.step(mode, stage_ev[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    stages_ms = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in stage_ev])) for s in stage_names}
+    dom = max((s for s in stage_names), key=lambda s: stages_ms[s])
+    log("ms/step", ms, "stages", stages_ms)
+    traffic = load_traffic(dom, w.name)
+    roof = roofline(dom, stages_ms[dom], w, traffic)
+    roof_all = {s: {k: roofline(s, stages_ms[s], w, load_traffic(s, w.name))[k]
+                    for k in ("bound", "achieved", "unit", "frac")} for s in stage_names}
+
+    extra = dict(headline_mode=mname, premeasure_ms=pre, stage_ms=stages_ms, stage_roofline=roof_all)
+    extra["route_ms_two_stage"] = time_fn(lambda: P.route_only(pisa.TWO_STAGE), 5)
+    extra["route_ms_fused"] = time_fn(lambda: P.route_only(pisa.FUSED), 5)
+    extra["bsa_ms"] = time_fn(P.bsa, 3)
+    extra["build_ms"] = stages_ms["build"]
+    extra["speedup_vs_bsa"] = (extra["bsa_ms"] + stages_ms["build"]) / ms
+    G = w.H_q // w.H_kv
+    bw = workcount.bsa_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.K_top)
+    extra["bsa_alg_tflops_one_pass"] = 2 * bw["mac"] / (extra["bsa_ms"] * 1e-3) / 1e12
+
+    # the headline selection is left in P.idx for the parity check below
+    P.step(mode)
+    torch.cuda.synchronize()
+    cpu, parity = (None, None)
+    if not args.no_cpu:
+        log("cpu oracle baseline")
+        cpu, parity = cpu_baseline(P, args.cpu_budget)
+        log("cpu", cpu, parity)
+    del P
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        for name, reps, attn in (("p16k", 10, False), ("p64k", 5, True)):
+            log("extra", name)
+            extra[name] = prefill_extra(name, reps, with_attn=attn)
+        log("extra decode")
+        extra["decode"] = decode_bench(256)
+
+    line = {
+        "metric": METRIC,
+        "value": w.B * w.N / (ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill routing 256K: pyramid build + routing of every position",
+                   "B": w.B, "N": w.N, "H_q": w.H_q, "H_kv": w.H_kv, "d": w.d, "C": w.C, "g": w.g,
+                   "K_top": w.K_top, "causal": True, "planted_blocks_per_head": w.planted, "seed": w.seed,
+                   "router": mname},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,6 +13,9 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Armed stage events of this host thread (pisa_time_stage).
+thread_local hipEvent_t g_stage_ev[PISA_STAGE_COUNT][2] = {};
+
 pisa_status fail(pisa_status s, const char* fmt, ...)
 {
     va_list ap;
@@ -161,7 +164,30 @@ TwoStageLayout two_stage_layout(const pisa_pyramid* p, int64_t N, int K_top)
 
 }  // namespace
 
+namespace pisa {
+
+void stage_mark(int stage, bool stop, hipStream_t s)
+{
+    if (stage < 0 || stage >= PISA_STAGE_COUNT) return;
+    hipEvent_t& ev = g_stage_ev[stage][stop ? 1 : 0];
+    if (!ev) return;
+    hipEventRecord(ev, s);
+    ev = nullptr;  // one-shot: the stop event disarms the stage after the start one has fired
+}
+
+}  // namespace pisa
+
 extern "C" {
+
+pisa_status pisa_time_stage(int32_t stage, void* start_event, void* stop_event)
+{
+    if (stage < 0 || stage >= PISA_STAGE_COUNT) return fail(PISA_EINVAL, "stage id %d out of range", stage);
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(PISA_EINVAL, "pisa_time_stage needs both events or neither");
+    g_stage_ev[stage][0] = (hipEvent_t)start_event;
+    g_stage_ev[stage][1] = (hipEvent_t)stop_event;
+    return ok();
+}
 
 int32_t pisa_abi_version(void) { return PISA_ABI_VERSION; }
 
@@ -195,7 +221,9 @@ pisa_status pisa_build_pyramid(const pisa_pyramid* p, const void* K, pisa_dtype 
     if (!K || !aligned16(K)) return fail(PISA_EINVAL, "K is NULL or not 16-byte aligned");
     if (N < 1) return fail(PISA_EINVAL, "N=%lld < 1", (long long)N);
     if (N > p->N_cap) return fail(PISA_ENOSPACE, "N=%lld exceeds N_cap=%lld", (long long)N, (long long)p->N_cap);
+    stage_mark(PISA_STAGE_BUILD, false, (hipStream_t)stream);
     hipError_t e = launch_build(pyr_args(p), K, dt == PISA_F32 ? 0 : 1, N, (hipStream_t)stream);
+    stage_mark(PISA_STAGE_BUILD, true, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_build_pyramid");
 }
 
@@ -207,7 +235,9 @@ pisa_status pisa_pyramid_append(const pisa_pyramid* p, const void* K, pisa_dtype
     if (!dtype_ok(dt)) return fail(PISA_EINVAL, "dtype %d is not PISA_F32 or PISA_BF16", (int)dt);
     if (!K || !aligned16(K)) return fail(PISA_EINVAL, "K is NULL or not 16-byte aligned");
     if (!seqlen) return fail(PISA_EINVAL, "seqlen is NULL");
+    stage_mark(PISA_STAGE_APPEND, false, (hipStream_t)stream);
     hipError_t e = launch_append(pyr_args(p), K, dt == PISA_F32 ? 0 : 1, seqlen, (hipStream_t)stream);
+    stage_mark(PISA_STAGE_APPEND, true, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_pyramid_append");
 }
 
@@ -246,7 +276,9 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
     const int dti = dt == PISA_F32 ? 0 : 1;
     hipStream_t st = (hipStream_t)stream;
     if (mode == PISA_ROUTE_FUSED) {
+        stage_mark(PISA_STAGE_ROUTE_FUSED, false, st);
         hipError_t e = launch_route_query(r, dti, p->d, MODE_FUSED, st);
+        stage_mark(PISA_STAGE_ROUTE_FUSED, true, st);
         return e == hipSuccess ? ok() : hip_fail(e, "pisa_route_prefill (fused)");
     }
 
@@ -306,7 +338,9 @@ pisa_status pisa_route_decode(const pisa_pyramid* p, const void* q, const void* 
     r.Q = q; r.K = K; r.N = 0; r.seqlen = seqlen;
     r.H_q = H_q; r.G = gqa_group; r.K_top = K_top; r.causal = 1;
     r.idx = idx; r.score = score;
+    stage_mark(PISA_STAGE_ROUTE_DECODE, false, (hipStream_t)stream);
     hipError_t e = launch_route_query(r, dt == PISA_F32 ? 0 : 1, p->d, MODE_DECODE, (hipStream_t)stream);
+    stage_mark(PISA_STAGE_ROUTE_DECODE, true, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_route_decode");
 }
 
@@ -333,7 +367,9 @@ pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_d
     a.Q = Q; a.K = K; a.V = V; a.B = B; a.H_q = H_q; a.H_kv = H_kv; a.G = G; a.C = C; a.K_top = K_top;
     a.causal = causal ? 1 : 0; a.N_q = N_q; a.N_kv = N_kv; a.N_alloc = N_alloc; a.idx = block_idx;
     a.kv_len = kv_len; a.O = O; a.lse = lse;
+    stage_mark(PISA_STAGE_ATTN, false, (hipStream_t)stream);
     hipError_t e = launch_attn(a, dt == PISA_F32 ? 0 : 1, d, (hipStream_t)stream);
+    stage_mark(PISA_STAGE_ATTN, true, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn");
 }
 
@@ -359,7 +395,9 @@ pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt,
     memset(&a, 0, sizeof(a));
     a.p = pyr_args(p); a.Q = Q; a.N = N; a.H_q = H_q; a.G = G; a.K_top = K_top; a.causal = causal ? 1 : 0;
     a.idx = idx; a.score = score;
+    stage_mark(PISA_STAGE_BSA, false, (hipStream_t)stream);
     hipError_t e = launch_bsa(a, dt == PISA_F32 ? 0 : 1, p->d, (hipStream_t)stream);
+    stage_mark(PISA_STAGE_BSA, true, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_bsa_select");
 }
 

@@ -103,4 +103,8 @@ hipError_t launch_bsa(const BsaArgs& a, int dtype, int d, hipStream_t s);
 
 enum { MODE_FUSED = 0, MODE_STAGE1 = 1, MODE_DECODE = 2 };
 
+// Stage timing (pisa_time_stage): records the caller's armed start / stop
+// events on the launch stream around a stage; no-op when nothing is armed.
+void stage_mark(int stage, bool stop, hipStream_t s);
+
 }  // namespace pisa

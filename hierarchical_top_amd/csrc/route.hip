@@ -168,9 +168,13 @@ hipError_t launch_two_stage(const RouteArgs& r, const Stage2Args& s2, const Fina
                             int32_t* zero_base, int64_t zero_count, int dtype, int d, hipStream_t s)
 {
     hipError_t err;
+    // cluster sizes are counted with atomics by the stage-1 kernel: clear them first
+    stage_mark(PISA_STAGE_UPPER, false, s);
     hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, s, zero_base, zero_count);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_route_query(r, dtype, d, MODE_STAGE1, s)) != hipSuccess) return err;
+    stage_mark(PISA_STAGE_UPPER, true, s);
+    stage_mark(PISA_STAGE_CLUSTER, false, s);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, r.counts, s2.n_clusters,
                        const_cast<int32_t*>(s2.offsets), const_cast<int32_t*>(s2.chunk_off));
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -178,9 +182,13 @@ hipError_t launch_two_stage(const RouteArgs& r, const Stage2Args& s2, const Fina
     const unsigned gi = (unsigned)((items + 255) / 256);
     hipLaunchKernelGGL(scatter_kernel, dim3(gi), dim3(256), 0, s, sc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    stage_mark(PISA_STAGE_CLUSTER, true, s);
     const int64_t max_chunks = (items * f.K_top + kChunkQ - 1) / kChunkQ + s2.n_clusters;
+    stage_mark(PISA_STAGE_LEAF, false, s);
     err = dtype == 0 ? stage2_f32(s2, d, max_chunks, s) : stage2_bf16(s2, d, max_chunks, s);
     if (err != hipSuccess) return err;
+    stage_mark(PISA_STAGE_LEAF, true, s);
+    stage_mark(PISA_STAGE_FINAL, false, s);
     if (f.K_top <= 8)
         hipLaunchKernelGGL(final_kernel<8>, dim3(gi), dim3(256), 0, s, f);
     else if (f.K_top <= 16)
@@ -189,6 +197,7 @@ hipError_t launch_two_stage(const RouteArgs& r, const Stage2Args& s2, const Fina
         hipLaunchKernelGGL(final_kernel<32>, dim3(gi), dim3(256), 0, s, f);
     else
         hipLaunchKernelGGL(final_kernel<64>, dim3(gi), dim3(256), 0, s, f);
+    stage_mark(PISA_STAGE_FINAL, true, s);
     return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ def lib():
             "pisa_sparse_attn": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p,
                                  c_i32, c_i32, c_p, c_p, c_p, c_p],
             "pisa_bsa_select": [P, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
+            "pisa_time_stage": [c_i32, c_p, c_p],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -78,8 +79,12 @@ def lib():
 
 
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
-           "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_bsa_select",
+           "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_bsa_select", "pisa_time_stage",
            "pisa_status_str", "pisa_last_error", "pisa_abi_version"]
+
+# Stage ids of pisa_time_stage (include/pisa.h, enum pisa_stage).
+STAGES = {"build": 0, "append": 1, "route_fused": 2, "route_decode": 3, "upper": 4, "cluster": 5, "leaf": 6,
+          "final": 7, "attn": 8, "bsa": 9}
 
 
 def _check(status: int):
@@ -216,3 +221,15 @@ def bsa_select(pyr: Pyramid, Q: torch.Tensor, N: int, K_top: int, causal: bool =
     _check(lib().pisa_bsa_select(ctypes.byref(pyr.desc), _ptr(Q), _dt(Q), N, H_q, K_top, 1 if causal else 0,
                                  H_q // pyr.H_kv, _ptr(idx), _ptr(score), _stream()))
     return (idx, score) if with_score else idx
+
+
+def time_stage(stage: str, start: "torch.cuda.Event", stop: "torch.cuda.Event"):
+    """Arm a pair of timing events for the next call (on this thread) that runs `stage`.
+
+    The events must already exist as HIP events (record them once beforehand);
+    afterwards ``start.elapsed_time(stop)`` is the stage's duration on its stream.
+    """
+    for ev in (start, stop):
+        if not ev.cuda_event:
+            raise ValueError("record the event once before arming it")
+    _check(lib().pisa_time_stage(STAGES[stage], ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)))

@@ -194,6 +194,32 @@ pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt,
                             int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group,
                             int32_t* idx, float* score, void* stream);
 
+/*
+ * Stage timing, for measurement. The library queues each call as one or more
+ * kernel stages; pisa_time_stage arms, for the calling host thread, a pair of
+ * caller-created hipEvent_t (passed as void*) for one stage id. The next call
+ * on this thread that runs that stage records start_event on its stream just
+ * before the stage's first kernel and stop_event just after its last kernel,
+ * then disarms the stage. Nothing else changes: the events are the caller's,
+ * the library neither creates nor waits on them. Passing NULL events disarms.
+ * Errors: PISA_EINVAL (stage id out of range, or only one event given).
+ */
+typedef enum pisa_stage {
+    PISA_STAGE_BUILD = 0,         /* pisa_build_pyramid: all levels */
+    PISA_STAGE_APPEND = 1,        /* pisa_pyramid_append */
+    PISA_STAGE_ROUTE_FUSED = 2,   /* pisa_route_prefill, PISA_ROUTE_FUSED */
+    PISA_STAGE_ROUTE_DECODE = 3,  /* pisa_route_decode */
+    PISA_STAGE_UPPER = 4,         /* two-stage: levels L..2 per (query, KV head) */
+    PISA_STAGE_CLUSTER = 5,       /* two-stage: clear, scan and scatter of the query clusters */
+    PISA_STAGE_LEAF = 6,          /* two-stage: leaf scoring per retained level-2 node */
+    PISA_STAGE_FINAL = 7,         /* two-stage: final Select_K */
+    PISA_STAGE_ATTN = 8,          /* pisa_sparse_attn */
+    PISA_STAGE_BSA = 9,           /* pisa_bsa_select */
+    PISA_STAGE_COUNT = 10
+} pisa_stage;
+
+pisa_status pisa_time_stage(int32_t stage, void* start_event, void* stop_event);
+
 /* Static description of a status code. */
 const char* pisa_status_str(pisa_status s);
 

@@ -1,0 +1,164 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports every
+function include/pisa.h declares, and rejects bad arguments on the host with
+the documented status codes before anything is queued."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from hierarchical_top_amd import pisa
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "pisa.h"
+
+OK, EINVAL, EUNSUPPORTED, ENOSPACE = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not pisa.LIB_PATH.exists():
+        pytest.skip("libpisa.so is not built")
+    return pisa.lib()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pisa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("pisa_build_pyramid", "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn",
+              "pisa_pyramid_append", "pisa_bsa_select"):
+        assert f in names
+
+
+def test_library_exports_every_declared_function(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared_functions()) <= set(pisa.EXPORTS)
+    assert lib.pisa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in (OK, EINVAL, EUNSUPPORTED, ENOSPACE, -4):
+        assert lib.pisa_status_str(s)
+    assert lib.pisa_status_str(7) == b"unknown status"
+
+
+def plan(lib, *args):
+    d = pisa._PyramidDesc()
+    st = lib.pisa_pyramid_plan(ctypes.byref(d), *args)
+    return st, d
+
+
+def test_plan_geometry(lib):
+    st, d = plan(lib, 1, 4, 128, 64, 4, 262144)
+    assert st == OK
+    assert d.L_cap == 7
+    assert [d.M_cap[l] for l in range(8)] == [262144, 4096, 1024, 256, 64, 16, 4, 1]
+    # per-level offsets are 64-float aligned and non-overlapping
+    for l in range(1, 7):
+        assert d.off[l] % 64 == 0 and d.off[l + 1] >= d.off[l] + 4 * d.M_cap[l] * 128
+    assert d.floats >= d.off[7] + 4 * 128
+    st, d = plan(lib, 32, 8, 128, 64, 4, 262400)
+    assert st == OK and d.L_cap == 8
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 128, 64, 4, 1024), EINVAL),
+    ((1, 4, 128, 64, 4, 0), EINVAL),
+    ((1, 4, 96, 64, 4, 1024), EUNSUPPORTED),
+    ((1, 4, 128, 48, 4, 1024), EUNSUPPORTED),
+    ((1, 4, 128, 64, 3, 1024), EUNSUPPORTED),
+    ((1, 64, 128, 64, 4, 1024), EUNSUPPORTED),
+])
+def test_plan_rejects(lib, args, status):
+    st, _ = plan(lib, *args)
+    assert st == status
+    assert lib.pisa_last_error()
+
+
+def fake_pyramid(lib, B=1, H=4, d=128, C=64, g=4, N=4096):
+    st, desc = plan(lib, B, H, d, C, g, N)
+    assert st == OK
+    desc.buf = 1 << 20  # never dereferenced: every call below fails validation first
+    return desc
+
+
+FAKE = ctypes.c_void_p(1 << 24)
+
+
+def route(lib, desc, N=4096, H_q=16, K_top=8, causal=1, gqa=4, mode=pisa.TWO_STAGE, Q=FAKE, ws=None, ws_bytes=0,
+          dt=pisa.BF16):
+    return lib.pisa_route_prefill(ctypes.byref(desc), Q, FAKE, dt, N, H_q, K_top, causal, gqa, mode, FAKE, None,
+                                  ws, ws_bytes, None)
+
+
+def test_route_prefill_validation(lib):
+    desc = fake_pyramid(lib)
+    assert route(lib, desc, N=0) == EINVAL
+    assert route(lib, desc, N=4097) == ENOSPACE
+    assert route(lib, desc, H_q=15, gqa=3) == EINVAL
+    assert route(lib, desc, gqa=2) == EINVAL                       # gqa_group != H_q / H_kv
+    assert route(lib, desc, K_top=2) == EINVAL                     # causal needs room for the forced set
+    assert route(lib, desc, K_top=0, causal=0) == EINVAL
+    assert route(lib, desc, K_top=65) == EINVAL
+    assert route(lib, desc, K_top=32) == EUNSUPPORTED              # g * K_top = 128 candidates
+    assert route(lib, desc, dt=7) == EINVAL
+    assert route(lib, desc, Q=None) == EINVAL
+    assert route(lib, desc, Q=ctypes.c_void_p((1 << 24) + 4)) == EINVAL  # misaligned
+    assert route(lib, desc, mode=5) == EINVAL
+    # two-stage needs a workspace of the advertised size
+    n = ctypes.c_size_t(0)
+    assert lib.pisa_route_prefill_workspace(ctypes.byref(desc), 4096, 16, 8, pisa.TWO_STAGE, ctypes.byref(n)) == OK
+    assert n.value > 0
+    assert route(lib, desc, ws=FAKE, ws_bytes=n.value - 1) == ENOSPACE
+    m = ctypes.c_size_t(1)
+    assert lib.pisa_route_prefill_workspace(ctypes.byref(desc), 4096, 16, 8, pisa.FUSED, ctypes.byref(m)) == OK
+    assert m.value == 0
+
+
+def test_descriptor_must_come_from_plan(lib):
+    desc = fake_pyramid(lib)
+    desc.off[2] += 64
+    assert route(lib, desc) == EINVAL
+    desc = fake_pyramid(lib)
+    desc.buf = None
+    assert route(lib, desc) == EINVAL
+    assert lib.pisa_build_pyramid(None, FAKE, pisa.BF16, 16, None) == EINVAL
+
+
+def test_build_append_decode_validation(lib):
+    desc = fake_pyramid(lib)
+    assert lib.pisa_build_pyramid(ctypes.byref(desc), FAKE, pisa.BF16, 0, None) == EINVAL
+    assert lib.pisa_build_pyramid(ctypes.byref(desc), FAKE, pisa.BF16, 4097, None) == ENOSPACE
+    assert lib.pisa_build_pyramid(ctypes.byref(desc), None, pisa.BF16, 16, None) == EINVAL
+    assert lib.pisa_pyramid_append(ctypes.byref(desc), FAKE, pisa.BF16, None, None) == EINVAL
+    assert lib.pisa_route_decode(ctypes.byref(desc), FAKE, FAKE, pisa.BF16, None, 16, 8, 4, FAKE, None,
+                                 None) == EINVAL
+    assert lib.pisa_route_decode(ctypes.byref(desc), FAKE, FAKE, pisa.BF16, FAKE, 16, 2, 4, FAKE, None,
+                                 None) == EINVAL
+
+
+def test_attention_and_bsa_validation(lib):
+    a = lib.pisa_sparse_attn
+    assert a(FAKE, FAKE, FAKE, pisa.BF16, 1, 10, 5, 10, 8, 2, 128, 64, FAKE, 8, 1, None, FAKE, None, None) == EINVAL
+    assert a(FAKE, FAKE, FAKE, pisa.BF16, 1, 10, 10, 10, 8, 3, 128, 64, FAKE, 8, 1, None, FAKE, None, None) == EINVAL
+    assert a(FAKE, FAKE, FAKE, pisa.BF16, 1, 10, 10, 10, 8, 2, 80, 64, FAKE, 8, 1, None, FAKE, None,
+             None) == EUNSUPPORTED
+    assert a(FAKE, FAKE, None, pisa.BF16, 1, 10, 10, 10, 8, 2, 128, 64, FAKE, 8, 1, None, FAKE, None, None) == EINVAL
+    desc = fake_pyramid(lib)
+    b = lib.pisa_bsa_select
+    assert b(ctypes.byref(desc), FAKE, pisa.BF16, 4096, 16, 9, 1, 4, FAKE, None, None) == EUNSUPPORTED
+    assert b(ctypes.byref(desc), FAKE, pisa.BF16, 4096, 16, 2, 1, 4, FAKE, None, None) == EINVAL
+    assert b(ctypes.byref(desc), FAKE, pisa.BF16, 5000, 16, 8, 1, 4, FAKE, None, None) == ENOSPACE
+
+
+def test_time_stage_validation(lib):
+    assert lib.pisa_time_stage(10, None, None) == EINVAL
+    assert lib.pisa_time_stage(-1, None, None) == EINVAL
+    assert lib.pisa_time_stage(0, FAKE, None) == EINVAL
+    assert lib.pisa_time_stage(0, None, None) == OK  # disarm
