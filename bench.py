@@ -39,8 +39,10 @@ from hierarchical_top_amd import pisa, synth, workcount  # noqa: E402
 METRIC = "routed queries/sec at 64K and 256K tokens (GQA prefill); decode route µs/step"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+MODES = {"levels": pisa.LEVELS, "two_stage": pisa.TWO_STAGE, "fused": pisa.FUSED}
 STAGES_TWO = ["build", "upper", "cluster", "leaf", "final"]
 STAGES_FUSED = ["build", "route_fused"]
+ARMED = {"build": 1, "route_fused": 1, "leaf": 1, "upper": 8, "cluster": 8, "final": 8}
 
 
 def log(*a):
@@ -64,19 +66,27 @@ class Prefill:
         self.Q, self.K = Q.cuda(), K.cuda()
         self.V = V.cuda() if (with_v and V is not None) else None
         self.pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
-        need = pisa.route_workspace_bytes(self.pyr, w.N, w.H_q, w.K_top, pisa.TWO_STAGE)
+        need = max(pisa.route_workspace_bytes(self.pyr, w.N, w.H_q, w.K_top, m) for m in (pisa.TWO_STAGE, pisa.LEVELS))
         self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         self.idx = torch.empty(w.B, w.H_kv, w.N, w.K_top, dtype=torch.int32, device="cuda")
         self.bidx = torch.empty_like(self.idx)
 
     def step(self, mode, stage_events=None):
-        """Pyramid build + routing of every position."""
+        """Pyramid build + routing of every position. stage_events: {stage: [(start, stop), ...]}
+        armed for this step; returns {stage: number of pairs the step consumed}."""
         w = self.w
         if stage_events:
-            for name, (a, b) in stage_events.items():
-                pisa.time_stage(name, a, b)
+            for name, pairs in stage_events.items():
+                for a, b in pairs:
+                    pisa.time_stage(name, a, b)
         self.pyr.build(self.K, w.N)
         pisa.route_prefill(self.pyr, self.Q, self.K, w.N, w.K_top, mode=mode, workspace=self.ws, out=self.idx)
+        fired = {}
+        if stage_events:
+            for name, pairs in stage_events.items():
+                fired[name] = len(pairs) - pisa.time_stage_pending(name)
+                pisa.time_stage_clear(name)
+        return fired
 
     def route_only(self, mode):
         w = self.w
@@ -236,10 +246,10 @@ def prefill_extra(name, reps, with_attn=False):
     P = Prefill(w, with_v=with_attn)
     G = w.H_q // w.H_kv
     out = {}
-    for mname, mode in (("two_stage", pisa.TWO_STAGE), ("fused", pisa.FUSED)):
+    for mname, mode in MODES.items():
         out["build_route_ms_" + mname] = time_fn(lambda: P.step(mode), reps)
         out["route_ms_" + mname] = time_fn(lambda: P.route_only(mode), reps)
-    best = min(out["build_route_ms_two_stage"], out["build_route_ms_fused"])
+    best = min(out["build_route_ms_" + m] for m in MODES)
     out["routed_queries_per_s"] = w.B * w.N / (best * 1e-3)
     out["bsa_ms"] = time_fn(P.bsa, max(2, reps // 2))
     bw = workcount.bsa_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.K_top)
@@ -267,7 +277,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--mode", choices=["auto", "fused", "two_stage"], default="auto")
+    ap.add_argument("--mode", choices=["auto", "levels", "fused", "two_stage"], default="auto")
     ap.add_argument("--quick", action="store_true", help="headline workload only (no extra workloads)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle routing to time")
@@ -288,25 +298,28 @@ def main():
     torch.cuda.synchronize()
 
     # pick the router: both are timed once after warm-up
-    modes = {"two_stage": pisa.TWO_STAGE, "fused": pisa.FUSED}
-    pre = {m: time_fn(lambda: P.step(v), 3, warm=1) for m, v in modes.items()}
+    pre = {m: time_fn(lambda: P.step(v), 3, warm=1) for m, v in MODES.items()}
     mname = min(pre, key=pre.get) if args.mode == "auto" else args.mode
-    mode = modes[mname]
-    stage_names = STAGES_TWO if mode == pisa.TWO_STAGE else STAGES_FUSED
+    mode = MODES[mname]
+    stage_names = STAGES_FUSED if mode == pisa.FUSED else STAGES_TWO
     log("pre-measure ms/step", pre, "->", mname)
 
     for _ in range(args.warmup):
         P.step(mode)
-    stage_ev = [{s: events() for s in stage_names} for _ in range(args.steps)]
+    stage_ev = [{s: [events() for _ in range(ARMED[s])] for s in stage_names} for _ in range(args.steps)]
+    fired = []
     torch.cuda.synchronize()
     t0, t1 = events()
     t0.record()
     for k in range(args.steps):
-        P.step(mode, stage_ev[k])
+        fired.append(P.step(mode, stage_ev[k]))
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    stages_ms = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in stage_ev])) for s in stage_names}
+    # per stage: summed over its launches in one step, averaged over the steps
+    stages_ms = {s: float(np.mean([sum(a.elapsed_time(b) for a, b in e[s][:f[s]]) for e, f in zip(stage_ev, fired)]))
+                 for s in stage_names}
+    launches = {s: fired[0][s] for s in stage_names}
     dom = max((s for s in stage_names), key=lambda s: stages_ms[s])
     log("ms/step", ms, "stages", stages_ms)
     traffic = load_traffic(dom, w.name)
@@ -314,9 +327,10 @@ def main():
     roof_all = {s: {k: roofline(s, stages_ms[s], w, load_traffic(s, w.name))[k]
                     for k in ("bound", "achieved", "unit", "frac")} for s in stage_names}
 
-    extra = dict(headline_mode=mname, premeasure_ms=pre, stage_ms=stages_ms, stage_roofline=roof_all)
-    extra["route_ms_two_stage"] = time_fn(lambda: P.route_only(pisa.TWO_STAGE), 5)
-    extra["route_ms_fused"] = time_fn(lambda: P.route_only(pisa.FUSED), 5)
+    extra = dict(headline_mode=mname, premeasure_ms=pre, stage_ms=stages_ms, stage_launches=launches,
+                 stage_roofline=roof_all)
+    for m, v in MODES.items():
+        extra["route_ms_" + m] = time_fn(lambda: P.route_only(v), 5)
     extra["bsa_ms"] = time_fn(P.bsa, 3)
     extra["build_ms"] = stages_ms["build"]
     extra["speedup_vs_bsa"] = (extra["bsa_ms"] + stages_ms["build"]) / ms

@@ -13,8 +13,14 @@ namespace {
 
 thread_local char g_err[512] = "";
 
-// Armed stage events of this host thread (pisa_time_stage).
-thread_local hipEvent_t g_stage_ev[PISA_STAGE_COUNT][2] = {};
+// Armed stage events of this host thread (pisa_time_stage): a queue of up to
+// kStageSlots (start, stop) pairs per stage, consumed one per stage occurrence.
+constexpr int kStageSlots = 16;
+struct StageQueue {
+    hipEvent_t ev[kStageSlots][2];
+    int head, tail;
+};
+thread_local StageQueue g_stage[PISA_STAGE_COUNT] = {};
 
 pisa_status fail(pisa_status s, const char* fmt, ...)
 {
@@ -143,6 +149,53 @@ struct TwoStageLayout {
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Highest level with more than K_top nodes (0: no level is ranked).
+int levels_top(int64_t N, int C, int g, int K_top)
+{
+    int lt = 0;
+    for (int l = 1;; ++l) {
+        const int64_t M = nodes_at(N, C, g, l);
+        if (M > K_top) lt = l;
+        if (M <= 1) break;
+    }
+    return lt;
+}
+
+struct LevelsLayout {
+    size_t kept0, kept1, flags, u, counts, offsets, chunk_off, entries, total;
+    int64_t cnt_total, max_clusters;
+    int64_t cnt_off[PISA_MAX_LEVELS + 2];
+    int l_top;
+};
+
+LevelsLayout levels_layout(const pisa_pyramid* p, int64_t N, int K_top)
+{
+    LevelsLayout w;
+    memset(&w, 0, sizeof(w));
+    const int64_t items = (int64_t)p->B * p->H_kv * N;
+    const int64_t BH = (int64_t)p->B * p->H_kv;
+    w.l_top = levels_top(N, p->C, p->g, K_top);
+    int64_t c = 0;
+    for (int l = 1; l <= w.l_top; ++l) {
+        w.cnt_off[l] = c;
+        const int64_t nb = BH * nodes_at(N, p->C, p->g, l + 1);  // clusters of level l: kept nodes of level l + 1
+        c += nb;
+        if (nb > w.max_clusters) w.max_clusters = nb;
+    }
+    w.cnt_total = c;
+    size_t o = 0;
+    w.kept0 = o; o = al(o + (size_t)items * K_top * 4);
+    w.kept1 = o; o = al(o + (size_t)items * K_top * 4);
+    w.flags = o; o = al(o + (size_t)items * 8);
+    w.u = o; o = al(o + (size_t)items * p->g * K_top * 4);
+    w.counts = o; o = al(o + (size_t)2 * c * 4);  // counts, then cursors (cleared together)
+    w.offsets = o; o = al(o + (size_t)(w.max_clusters + 1) * 4);
+    w.chunk_off = o; o = al(o + (size_t)(w.max_clusters + 1) * 4);
+    w.entries = o; o = al(o + (size_t)items * K_top * 4);
+    w.total = o;
+    return w;
+}
+
 TwoStageLayout two_stage_layout(const pisa_pyramid* p, int64_t N, int K_top)
 {
     TwoStageLayout w;
@@ -169,10 +222,10 @@ namespace pisa {
 void stage_mark(int stage, bool stop, hipStream_t s)
 {
     if (stage < 0 || stage >= PISA_STAGE_COUNT) return;
-    hipEvent_t& ev = g_stage_ev[stage][stop ? 1 : 0];
-    if (!ev) return;
-    hipEventRecord(ev, s);
-    ev = nullptr;  // one-shot: the stop event disarms the stage after the start one has fired
+    StageQueue& q = g_stage[stage];
+    if (q.head == q.tail) return;
+    hipEventRecord(q.ev[q.head % kStageSlots][stop ? 1 : 0], s);
+    if (stop) ++q.head;  // this pair is consumed
 }
 
 }  // namespace pisa
@@ -184,9 +237,22 @@ pisa_status pisa_time_stage(int32_t stage, void* start_event, void* stop_event)
     if (stage < 0 || stage >= PISA_STAGE_COUNT) return fail(PISA_EINVAL, "stage id %d out of range", stage);
     if ((start_event == nullptr) != (stop_event == nullptr))
         return fail(PISA_EINVAL, "pisa_time_stage needs both events or neither");
-    g_stage_ev[stage][0] = (hipEvent_t)start_event;
-    g_stage_ev[stage][1] = (hipEvent_t)stop_event;
+    StageQueue& q = g_stage[stage];
+    if (!start_event) {
+        q.head = q.tail = 0;
+        return ok();
+    }
+    if (q.tail - q.head >= kStageSlots) return fail(PISA_ENOSPACE, "more than %d event pairs armed", kStageSlots);
+    q.ev[q.tail % kStageSlots][0] = (hipEvent_t)start_event;
+    q.ev[q.tail % kStageSlots][1] = (hipEvent_t)stop_event;
+    ++q.tail;
     return ok();
+}
+
+int32_t pisa_time_stage_pending(int32_t stage)
+{
+    if (stage < 0 || stage >= PISA_STAGE_COUNT) return -1;
+    return g_stage[stage].tail - g_stage[stage].head;
 }
 
 int32_t pisa_abi_version(void) { return PISA_ABI_VERSION; }
@@ -247,7 +313,9 @@ pisa_status pisa_route_prefill_workspace(const pisa_pyramid* p, int64_t N, int32
     (void)H_q;
     if (!p || !bytes) return fail(PISA_EINVAL, "NULL argument");
     if (N < 1 || K_top < 1 || K_top > 64) return fail(PISA_EINVAL, "N or K_top out of range");
-    *bytes = mode == PISA_ROUTE_FUSED ? 0 : two_stage_layout(p, N, K_top).total;
+    if (mode == PISA_ROUTE_FUSED) *bytes = 0;
+    else if (mode == PISA_ROUTE_LEVELS) *bytes = levels_layout(p, N, K_top).total;
+    else *bytes = two_stage_layout(p, N, K_top).total;
     return ok();
 }
 
@@ -263,7 +331,8 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
     if (s != PISA_OK) return s;
     if (!Q || !K || !idx) return fail(PISA_EINVAL, "Q, K and idx must be non-NULL");
     if (!aligned16(Q) || !aligned16(K)) return fail(PISA_EINVAL, "Q and K must be 16-byte aligned");
-    if (mode != PISA_ROUTE_FUSED && mode != PISA_ROUTE_TWO_STAGE) return fail(PISA_EINVAL, "mode=%d", mode);
+    if (mode != PISA_ROUTE_FUSED && mode != PISA_ROUTE_TWO_STAGE && mode != PISA_ROUTE_LEVELS)
+        return fail(PISA_EINVAL, "mode=%d", mode);
     const int64_t items = (int64_t)p->B * p->H_kv * N;
     if (items > ((int64_t)1 << 31) - 1) return fail(PISA_EUNSUPPORTED, "B * H_kv * N exceeds 2^31 - 1");
 
@@ -282,7 +351,39 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
         return e == hipSuccess ? ok() : hip_fail(e, "pisa_route_prefill (fused)");
     }
 
-    if (N >= ((int64_t)1 << 25)) return fail(PISA_EUNSUPPORTED, "two-stage routing needs N < 2^25");
+    if (N >= ((int64_t)1 << 25)) return fail(PISA_EUNSUPPORTED, "clustered routing needs N < 2^25");
+    if (mode == PISA_ROUTE_LEVELS) {
+        if (K_top > 16 && levels_top(N, p->C, p->g, K_top) > 0)
+            return fail(PISA_EUNSUPPORTED, "level-synchronous routing ranks at most K_top = 16 blocks");
+        if (items * K_top > ((int64_t)1 << 31) - 1)
+            return fail(PISA_EUNSUPPORTED, "B * H_kv * N * K_top exceeds 2^31 - 1");
+        const size_t lds_leaf = (size_t)p->g * p->C * (p->d + 8) * 2 * (dt == PISA_F32 ? 2 : 1);
+        const size_t lds_up = (size_t)p->g * p->g * (p->d + 8) * 2 * 2;
+        if (lds_leaf > 160 * 1024 || lds_up > 160 * 1024)
+            return fail(PISA_EUNSUPPORTED, "a node's rows do not fit in LDS for level-synchronous routing");
+        const LevelsLayout w = levels_layout(p, N, K_top);
+        if (!ws || ws_bytes < w.total)
+            return fail(PISA_ENOSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, w.total);
+        if (((uintptr_t)ws & 255) != 0) return fail(PISA_EINVAL, "workspace must be 256-byte aligned");
+        char* base = (char*)ws;
+        LevelsArgs la;
+        memset(&la, 0, sizeof(la));
+        la.r = r;
+        la.kept[0] = (int32_t*)(base + w.kept0);
+        la.kept[1] = (int32_t*)(base + w.kept1);
+        la.flags = (int64_t*)(base + w.flags);
+        la.u = (float*)(base + w.u);
+        la.counts = (int32_t*)(base + w.counts);
+        la.cursor = la.counts + w.cnt_total;
+        la.cnt_total = w.cnt_total;
+        memcpy(la.cnt_off, w.cnt_off, sizeof(la.cnt_off));
+        la.offsets = (int32_t*)(base + w.offsets);
+        la.chunk_off = (int32_t*)(base + w.chunk_off);
+        la.entries = (int32_t*)(base + w.entries);
+        la.l_top = w.l_top;
+        hipError_t e = launch_levels(la, dti, p->d, st);
+        return e == hipSuccess ? ok() : hip_fail(e, "pisa_route_prefill (levels)");
+    }
     if (items * K_top > ((int64_t)1 << 31) - 1) return fail(PISA_EUNSUPPORTED, "B * H_kv * N * K_top exceeds 2^31 - 1");
     const size_t lds = (size_t)p->g * p->C * (p->d + 8) * 2 * (dt == PISA_F32 ? 2 : 1);
     if (lds > 160 * 1024) return fail(PISA_EUNSUPPORTED, "g * C keys do not fit in LDS for two-stage routing");

@@ -1,0 +1,456 @@
+// levels.hip -- level-synchronous prefill routing ("Block Sparse Attention with
+// Log-Linear Complexity", section 3.2 eq 16-22; appendix B, "Causal masking").
+//
+// All (query, KV head) items advance one level at a time:
+//   select (level l+1)  : kept nodes of level l+1 per item; count, per kept
+//                         node, the items whose next level is ranked;
+//   scan                : cluster offsets and chunk counts;
+//   scatter             : cluster entries (t << 6 | slot);
+//   score (level l)     : clustered MFMA scoring of the candidates of level l
+//                         (levels_impl.hpp);
+//   select (level l)    : Select_K of level l, and so on down to the leaves,
+//                         whose select writes the ascending output.
+// Counting and scatter aggregate per workgroup in LDS, so a node kept by every
+// query (block 0 and the current path are forced) costs one global atomic per
+// workgroup, not one per query.
+#include <string.h>
+
+#include "pisa_device.hpp"
+#include "pisa_internal.hpp"
+
+namespace pisa {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelItemsPerThread = 4;
+constexpr int kLdsBins = 8192;  // cluster bins aggregated in LDS (larger levels use global atomics)
+
+// Eligible existing children of node P of level lp at level lp - 1, for query t.
+__device__ __forceinline__ int64_t n_children(int64_t P, int g, int64_t M_child, int64_t elig_max_child)
+{
+    const int64_t lo = P * g;
+    int64_t hi = lo + g;
+    if (hi > M_child) hi = M_child;
+    if (hi > elig_max_child + 1) hi = elig_max_child + 1;
+    return hi > lo ? hi - lo : 0;
+}
+
+// Forced nodes of level l for a query in leaf c (first, current and previous
+// leaf's ancestors), deduplicated; returns the count (0 without causal masking).
+__device__ __forceinline__ int forced_nodes(int64_t c, int shl, bool causal, int64_t F[3])
+{
+    if (!causal) return 0;
+    int n = 0;
+    F[n++] = 0;
+    const int64_t fc = c >> shl;
+    if (fc != 0) F[n++] = fc;
+    if (c >= 1) {
+        const int64_t fp = (c - 1) >> shl;
+        if (fp != 0 && fp != fc) F[n++] = fp;
+    }
+    return n;
+}
+
+__device__ __forceinline__ bool in3(int64_t x, const int64_t F[3], int nF)
+{
+    return (nF > 0 && x == F[0]) || (nF > 1 && x == F[1]) || (nF > 2 && x == F[2]);
+}
+
+template <int KMAX>
+__device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int64_t t, int* s_hist, bool use_lds)
+{
+    const int64_t i = bh * a.N + t;
+    const int K = a.K_top, g = 1 << a.g_log2;
+    const int l = a.level;
+    const int64_t c = t >> a.c_log2;
+    const bool causal = a.causal != 0;
+    const int shl = (l - 1) * a.g_log2;
+    const int span_log2 = a.c_log2 + shl;
+    const int64_t M_l = (a.N + ((int64_t)1 << span_log2) - 1) >> span_log2;
+    const int64_t elig_max = causal ? (t >> span_log2) : M_l - 1;
+
+    // candidates of this level: children of the kept nodes of level l + 1 (or all eligible nodes)
+    int64_t nA = 0;
+    const int32_t* kin = a.kept_in ? a.kept_in + i * K : nullptr;
+    if (a.init) {
+        nA = elig_max + 1 < M_l ? elig_max + 1 : M_l;
+    } else {
+        for (int s = 0; s < K; ++s) {
+            const int P = kin[s];
+            if (P < 0) break;
+            nA += n_children(P, g, M_l, elig_max);
+        }
+    }
+
+    int ids[KMAX];
+    float val[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) { ids[j] = 0x7fffffff; val[j] = -INFINITY; }
+    auto put = [&](int x, float v) {  // insert into the ascending id list
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (x < ids[j]) {
+                const int ti = ids[j]; ids[j] = x; x = ti;
+                const float tv = val[j]; val[j] = v; v = tv;
+            }
+    };
+    int nkept;
+    if (nA <= K) {
+        // at most K_top candidates: all are kept without scoring (section 3.2)
+        nkept = (int)nA;
+        if (a.init) {
+            for (int64_t x = 0; x < nA; ++x) put((int)x, INFINITY);
+        } else {
+            for (int s = 0; s < K; ++s) {
+                const int P = kin[s];
+                if (P < 0) break;
+                const int64_t nc = n_children(P, g, M_l, elig_max);
+                for (int64_t j = 0; j < nc; ++j) put((int)((int64_t)P * g + j), INFINITY);
+            }
+        }
+    } else {
+        int64_t F[3];
+        const int nF = forced_nodes(c, shl, causal, F);
+        const int R = K - nF;
+        float bu[KMAX];
+        int bi[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) { bu[j] = -INFINITY; bi[j] = 0x7fffffff; }
+        const float* urow = a.u + i * (int64_t)(K * g);
+        for (int s = 0; s < K; ++s) {
+            const int P = kin[s];
+            if (P < 0) break;
+            const int64_t nc = n_children(P, g, M_l, elig_max);
+            for (int64_t j = 0; j < nc; ++j) {
+                const int64_t x = (int64_t)P * g + j;
+                if (in3(x, F, nF)) continue;
+                float xu = urow[s * g + j];
+                int xi = (int)x;
+#pragma unroll
+                for (int q = 0; q < KMAX; ++q) {
+                    if (q < R && before(xu, xi, bu[q], bi[q])) {
+                        const float tu = bu[q]; bu[q] = xu; xu = tu;
+                        const int ti = bi[q]; bi[q] = xi; xi = ti;
+                    }
+                }
+            }
+        }
+        for (int k = 0; k < nF; ++k) put((int)F[k], INFINITY);
+#pragma unroll
+        for (int q = 0; q < KMAX; ++q)
+            if (q < R) put(bi[q], bu[q]);
+        nkept = K;
+    }
+
+    if (l == 1) {
+        int32_t* out = a.idx + i * K;
+        float* sc = a.score ? a.score + i * K : nullptr;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j < K) {
+                const bool ok = j < nkept;
+                out[j] = ok ? ids[j] : -1;
+                if (sc) sc[j] = ok ? val[j] : -INFINITY;
+            }
+        }
+        return;
+    }
+
+    int32_t* kout = a.kept_out + i * K;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (j < K) kout[j] = j < nkept ? ids[j] : -1;
+
+    // next level: is it ranked for this item, and which kept nodes own ranked candidates?
+    const int shl2 = shl - a.g_log2;
+    const int span2 = a.c_log2 + shl2;
+    const int64_t M_c = (a.N + ((int64_t)1 << span2) - 1) >> span2;
+    const int64_t em_c = causal ? (t >> span2) : M_c - 1;
+    int64_t nA2 = 0;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (j < nkept) nA2 += n_children(ids[j], g, M_c, em_c);
+    uint64_t mask = 0;
+    if (nA2 > K) {
+        int64_t F2[3];
+        const int nF2 = forced_nodes(c, shl2, causal, F2);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j < nkept) {
+                const int64_t P = ids[j];
+                const int64_t nc = n_children(P, g, M_c, em_c);
+                int64_t nforced = 0;
+                for (int k = 0; k < nF2; ++k) nforced += (F2[k] >= P * g && F2[k] < P * g + nc) ? 1 : 0;
+                if (nc > nforced) {
+                    mask |= (uint64_t)1 << j;
+                    if (use_lds) atomicAdd(&s_hist[P], 1);
+                    else atomicAdd(&a.counts[bh * a.M_bins + P], 1);
+                }
+            }
+        }
+    }
+    a.flags_out[i] = (int64_t)mask;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
+{
+    extern __shared__ int s_hist[];
+    const int64_t bh = blockIdx.y;
+    const int64_t t0 = (int64_t)blockIdx.x * (kSelThreads * kSelItemsPerThread);
+    const bool count = a.level > 1;
+    const bool use_lds = count && a.M_bins <= kLdsBins;
+    if (use_lds) {
+        for (int64_t k = threadIdx.x; k < a.M_bins; k += kSelThreads) s_hist[k] = 0;
+        __syncthreads();
+    }
+    for (int k = 0; k < kSelItemsPerThread; ++k) {
+        const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
+        if (t < a.N) select_item<KMAX>(a, bh, t, s_hist, use_lds);
+    }
+    if (use_lds) {
+        __syncthreads();
+        for (int64_t k = threadIdx.x; k < a.M_bins; k += kSelThreads) {
+            const int v = s_hist[k];
+            if (v) atomicAdd(&a.counts[bh * a.M_bins + k], v);
+        }
+    }
+}
+
+// Cluster entries: (t << 6) | slot for every flagged slot of every item, grouped
+// by kept node. Positions inside a cluster are reserved per workgroup.
+struct ScatterLvArgs {
+    int H, K_top;
+    int64_t N, M_bins;
+    const int32_t* kept;
+    const int64_t* flags;
+    const int32_t* offsets;
+    int32_t* cursor;
+    int32_t* entries;
+};
+
+__global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a)
+{
+    extern __shared__ int s_mem[];
+    int* s_cnt = s_mem;
+    int* s_pos = s_mem + a.M_bins;
+    const int64_t bh = blockIdx.y;
+    const int64_t t0 = (int64_t)blockIdx.x * (kSelThreads * kSelItemsPerThread);
+    const bool use_lds = a.M_bins <= kLdsBins;
+    const int32_t* base_off = a.offsets + bh * a.M_bins;
+    int32_t* cur = a.cursor + bh * a.M_bins;
+    if (use_lds) {
+        for (int64_t k = threadIdx.x; k < a.M_bins; k += kSelThreads) s_cnt[k] = 0;
+        __syncthreads();
+        for (int k = 0; k < kSelItemsPerThread; ++k) {
+            const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
+            if (t >= a.N) continue;
+            const int64_t i = bh * a.N + t;
+            uint64_t m = (uint64_t)a.flags[i];
+            while (m) {
+                const int s = __builtin_ctzll(m);
+                m &= m - 1;
+                atomicAdd(&s_cnt[a.kept[i * a.K_top + s]], 1);
+            }
+        }
+        __syncthreads();
+        for (int64_t k = threadIdx.x; k < a.M_bins; k += kSelThreads) {
+            const int v = s_cnt[k];
+            s_pos[k] = v ? base_off[k] + atomicAdd(&cur[k], v) : 0;
+        }
+        __syncthreads();
+    }
+    for (int k = 0; k < kSelItemsPerThread; ++k) {
+        const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
+        if (t >= a.N) continue;
+        const int64_t i = bh * a.N + t;
+        uint64_t m = (uint64_t)a.flags[i];
+        while (m) {
+            const int s = __builtin_ctzll(m);
+            m &= m - 1;
+            const int P = a.kept[i * a.K_top + s];
+            const int pos = use_lds ? atomicAdd(&s_pos[P], 1) : base_off[P] + atomicAdd(&cur[P], 1);
+            a.entries[pos] = (int32_t)((t << 6) | s);
+        }
+    }
+}
+
+// Exclusive scans of cluster sizes and of their chunk counts (one workgroup).
+__global__ __launch_bounds__(1024) void cluster_scan_kernel(const int32_t* __restrict__ counts, int64_t n, int qc,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ chunk_off)
+{
+    __shared__ int s_w0[16], s_w1[16];
+    __shared__ int s_carry[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) { s_carry[0] = 0; s_carry[1] = 0; }
+    __syncthreads();
+    for (int64_t base = 0; base < n; base += 1024) {
+        const int64_t i = base + tid;
+        const int cnt = i < n ? counts[i] : 0;
+        const int nch = (cnt + qc - 1) / qc;
+        int x0 = cnt, x1 = nch;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y0 = __shfl_up(x0, o, 64), y1 = __shfl_up(x1, o, 64);
+            if (lane >= o) { x0 += y0; x1 += y1; }
+        }
+        if (lane == 63) { s_w0[wave] = x0; s_w1[wave] = x1; }
+        __syncthreads();
+        int p0 = s_carry[0], p1 = s_carry[1];
+        for (int w = 0; w < wave; ++w) { p0 += s_w0[w]; p1 += s_w1[w]; }
+        if (i < n) {
+            offsets[i] = p0 + x0 - cnt;
+            chunk_off[i] = p1 + x1 - nch;
+        }
+        __syncthreads();
+        if (tid == 1023) { s_carry[0] = p0 + x0; s_carry[1] = p1 + x1; }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        offsets[n] = s_carry[0];
+        chunk_off[n] = s_carry[1];
+    }
+}
+
+__global__ void fill_zero_lv_kernel(int32_t* p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+static int64_t nodes_n(int64_t n, int c_log2, int g_log2, int l)
+{
+    const int sh = c_log2 + (l - 1) * g_log2;
+    return (n + ((int64_t)1 << sh) - 1) >> sh;
+}
+
+static hipError_t launch_select(const SelectArgs& sa, int K_top, hipStream_t s)
+{
+    const int64_t per = (int64_t)kSelThreads * kSelItemsPerThread;
+    const dim3 grid((unsigned)((sa.N + per - 1) / per), (unsigned)(sa.B * sa.H));
+    const size_t lds = (sa.level > 1 && sa.M_bins <= kLdsBins) ? (size_t)sa.M_bins * 4 : 0;
+    if (K_top <= 8)
+        hipLaunchKernelGGL(select_kernel<8>, grid, dim3(kSelThreads), lds, s, sa);
+    else
+        hipLaunchKernelGGL(select_kernel<16>, grid, dim3(kSelThreads), lds, s, sa);
+    return hipGetLastError();
+}
+
+hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
+{
+    const RouteArgs& r = a.r;
+    const PyrArgs& p = r.p;
+    const int64_t N = r.N;
+    const int BH = p.B * p.H;
+    hipError_t err;
+
+    SelectArgs sa;
+    memset(&sa, 0, sizeof(sa));
+    sa.B = p.B; sa.H = p.H; sa.c_log2 = p.c_log2; sa.g_log2 = p.g_log2; sa.K_top = r.K_top;
+    sa.causal = r.causal; sa.N = N; sa.idx = r.idx; sa.score = r.score;
+
+    if (a.l_top == 0) {
+        // at most K_top leaf blocks: every eligible leaf is kept
+        sa.level = 1;
+        sa.init = 1;
+        return launch_select(sa, r.K_top, s);
+    }
+
+    stage_mark(PISA_STAGE_CLUSTER, false, s);
+    hipLaunchKernelGGL(fill_zero_lv_kernel, dim3(256), dim3(256), 0, s, a.counts, 2 * a.cnt_total);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    stage_mark(PISA_STAGE_CLUSTER, true, s);
+
+    // the level above the first ranked one: every eligible node is kept
+    int cur = 0;
+    stage_mark(PISA_STAGE_FINAL, false, s);
+    sa.level = a.l_top + 1;
+    sa.init = 1;
+    sa.kept_out = a.kept[cur];
+    sa.flags_out = a.flags;
+    sa.M_bins = nodes_n(N, p.c_log2, p.g_log2, a.l_top + 1);
+    sa.counts = a.counts + a.cnt_off[a.l_top];
+    if ((err = launch_select(sa, r.K_top, s)) != hipSuccess) return err;
+    stage_mark(PISA_STAGE_FINAL, true, s);
+
+    for (int l = a.l_top; l >= 1; --l) {
+        const int64_t M_bins = nodes_n(N, p.c_log2, p.g_log2, l + 1);
+        const int64_t n_clusters = (int64_t)BH * M_bins;
+        const bool leaf = l == 1;
+        const int qc = leaf ? 128 : 256;
+        int32_t* counts = a.counts + a.cnt_off[l];
+        int32_t* cursor = a.cursor + a.cnt_off[l];
+
+        stage_mark(PISA_STAGE_CLUSTER, false, s);
+        hipLaunchKernelGGL(cluster_scan_kernel, dim3(1), dim3(1024), 0, s, counts, n_clusters, qc, a.offsets,
+                           a.chunk_off);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        ScatterLvArgs sc;
+        sc.H = p.H; sc.K_top = r.K_top; sc.N = N; sc.M_bins = M_bins;
+        sc.kept = a.kept[cur]; sc.flags = a.flags; sc.offsets = a.offsets; sc.cursor = cursor;
+        sc.entries = a.entries;
+        {
+            const int64_t per = (int64_t)kSelThreads * kSelItemsPerThread;
+            const dim3 grid((unsigned)((N + per - 1) / per), (unsigned)BH);
+            const size_t lds = M_bins <= kLdsBins ? (size_t)2 * M_bins * 4 : 0;
+            hipLaunchKernelGGL(scatter_lv_kernel, grid, dim3(kSelThreads), lds, s, sc);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        stage_mark(PISA_STAGE_CLUSTER, true, s);
+
+        ScoreArgs sc2;
+        memset(&sc2, 0, sizeof(sc2));
+        sc2.Q = r.Q; sc2.N = N; sc2.H = p.H; sc2.H_q = r.H_q; sc2.G = r.G; sc2.K_top = r.K_top; sc2.g = p.g;
+        if (leaf) {
+            sc2.rows = r.K;
+            sc2.rows_b_stride = p.N_cap * p.H * d;
+            sc2.rows_h_stride = d;
+            sc2.row_stride = (int64_t)p.H * d;
+            sc2.rows_limit = N;
+            sc2.rc = p.C;
+        } else {
+            sc2.rows = p.buf + p.off[l - 1];
+            sc2.rows_b_stride = (int64_t)p.H * p.M_cap[l - 1] * d;
+            sc2.rows_h_stride = p.M_cap[l - 1] * d;
+            sc2.row_stride = d;
+            sc2.rows_limit = nodes_n(N, p.c_log2, p.g_log2, l - 1);
+            sc2.rc = p.g;
+        }
+        sc2.qc = qc;
+        sc2.n_clusters = n_clusters;
+        sc2.M_bins = M_bins;
+        sc2.offsets = a.offsets; sc2.chunk_off = a.chunk_off; sc2.entries = a.entries; sc2.u = a.u;
+        const int64_t grid = ((int64_t)BH * N * r.K_top + qc - 1) / qc + n_clusters;
+        stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, false, s);
+        if ((err = launch_score(sc2, dtype, d, leaf, grid, s)) != hipSuccess) return err;
+        stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, true, s);
+
+        stage_mark(PISA_STAGE_FINAL, false, s);
+        sa.level = l;
+        sa.init = 0;
+        sa.kept_in = a.kept[cur];
+        sa.u = a.u;
+        sa.kept_out = a.kept[cur ^ 1];
+        sa.flags_out = a.flags;
+        sa.M_bins = nodes_n(N, p.c_log2, p.g_log2, l);
+        sa.counts = l > 1 ? a.counts + a.cnt_off[l - 1] : nullptr;
+        if ((err = launch_select(sa, r.K_top, s)) != hipSuccess) return err;
+        stage_mark(PISA_STAGE_FINAL, true, s);
+        cur ^= 1;
+    }
+    return hipSuccess;
+}
+
+}  // namespace pisa
+
+namespace pisa {
+
+hipError_t score_bf16(const ScoreArgs& a, int d, bool key_rows, int64_t grid, hipStream_t s);
+hipError_t score_f32(const ScoreArgs& a, int d, bool key_rows, int64_t grid, hipStream_t s);
+
+hipError_t launch_score(const ScoreArgs& a, int dtype, int d, bool key_rows, int64_t grid, hipStream_t s)
+{
+    return dtype == 0 ? score_f32(a, d, key_rows, grid, s) : score_bf16(a, d, key_rows, grid, s);
+}
+
+}  // namespace pisa

@@ -92,12 +92,65 @@ struct BsaArgs {
     float* score;
 };
 
+// Level-synchronous routing: clustered scoring of one level.
+struct ScoreArgs {
+    const void* Q;            // [B][N][H_q][d]
+    int64_t N;
+    int H, H_q, G, K_top, g;
+    const void* rows;         // level l-1 data: summaries (float) or keys (dtype of Q)
+    int64_t rows_b_stride;    // elements between sequences
+    int64_t rows_h_stride;    // elements between KV heads
+    int64_t row_stride;       // elements between consecutive rows
+    int64_t rows_limit;       // rows that exist (nodes of level l-1, or tokens)
+    int rc;                   // rows per candidate (g, or C at the leaf level)
+    int qc;                   // entries per chunk
+    int64_t n_clusters;       // B * H * M_bins
+    int64_t M_bins;           // nodes of level l+1 (cluster keys)
+    const int32_t* offsets;   // [n_clusters + 1]
+    const int32_t* chunk_off; // [n_clusters + 1]
+    const int32_t* entries;   // (t << 6) | slot
+    float* u;                 // [B][H][N][K_top * g]
+};
+
+// Per-item selection of one level, and counting of the next level's clusters.
+struct SelectArgs {
+    int B, H, c_log2, g_log2, K_top, causal;
+    int64_t N;
+    int level;                // the level whose kept set is produced
+    int init;                 // 1: the candidates are all eligible nodes of `level`
+    const int32_t* kept_in;   // [items][K_top] kept nodes of level + 1
+    const float* u;           // [items][K_top * g] scores of the candidates of `level`
+    int32_t* kept_out;        // [items][K_top] (level > 1)
+    int64_t* flags_out;       // [items] slots of kept_out whose children are scored next
+    int32_t* counts;          // [B * H][M_bins] cluster sizes for the next level (level > 1)
+    int64_t M_bins;           // nodes of `level`
+    int32_t* idx;             // level 1: [items][K_top]
+    float* score;             // level 1: [items][K_top] or null
+};
+
+struct LevelsArgs {
+    RouteArgs r;              // pyramid, Q, K, N, heads, K_top, causal, outputs
+    int32_t* kept[2];
+    int64_t* flags;
+    float* u;
+    int32_t* counts;          // per scored level, at cnt_off[level]
+    int32_t* cursor;          // same layout as counts
+    int64_t cnt_total;
+    int64_t cnt_off[PISA_MAX_LEVELS + 2];
+    int32_t* offsets;
+    int32_t* chunk_off;
+    int32_t* entries;
+    int l_top;                // highest scored level (0: nothing is scored)
+};
+
 hipError_t launch_build(const PyrArgs& a, const void* K, int dtype, int64_t n, hipStream_t s);
 hipError_t launch_append(const PyrArgs& a, const void* K, int dtype, const int64_t* seqlen, hipStream_t s);
 hipError_t launch_route_query(const RouteArgs& a, int dtype, int d, int mode, hipStream_t s);
 hipError_t launch_two_stage(const RouteArgs& a, const Stage2Args& s2, const FinalArgs& f,
                             const ScatterArgs& sc, int32_t* zero_base, int64_t zero_count, int dtype,
                             int d, hipStream_t s);
+hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int dtype, int d, bool key_rows, int64_t grid, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_bsa(const BsaArgs& a, int dtype, int d, hipStream_t s);
 

@@ -18,7 +18,7 @@ import torch
 LIB_PATH = Path(__file__).resolve().parent / "libpisa.so"
 MAX_LEVELS = 32
 F32, BF16 = 0, 1
-TWO_STAGE, FUSED = 0, 1
+TWO_STAGE, FUSED, LEVELS = 0, 1, 2
 
 c_i32, c_i64, c_p, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -63,6 +63,7 @@ def lib():
                                  c_i32, c_i32, c_p, c_p, c_p, c_p],
             "pisa_bsa_select": [P, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_time_stage": [c_i32, c_p, c_p],
+            "pisa_time_stage_pending": [c_i32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -80,6 +81,7 @@ def lib():
 
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
            "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_bsa_select", "pisa_time_stage",
+           "pisa_time_stage_pending",
            "pisa_status_str", "pisa_last_error", "pisa_abi_version"]
 
 # Stage ids of pisa_time_stage (include/pisa.h, enum pisa_stage).
@@ -233,3 +235,12 @@ def time_stage(stage: str, start: "torch.cuda.Event", stop: "torch.cuda.Event"):
         if not ev.cuda_event:
             raise ValueError("record the event once before arming it")
     _check(lib().pisa_time_stage(STAGES[stage], ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)))
+
+
+def time_stage_pending(stage: str) -> int:
+    """Armed event pairs of `stage` not consumed yet on this thread."""
+    return int(lib().pisa_time_stage_pending(STAGES[stage]))
+
+
+def time_stage_clear(stage: str):
+    _check(lib().pisa_time_stage(STAGES[stage], None, None))

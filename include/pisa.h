@@ -57,7 +57,10 @@ typedef enum pisa_dtype { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
 typedef enum pisa_route_mode {
     PISA_ROUTE_TWO_STAGE = 0,  /* section 3.3: intermediate levels per query, then leaf
                                   scoring per retained level-2 node with key reuse */
-    PISA_ROUTE_FUSED = 1       /* all levels of one query in one program (per-query) */
+    PISA_ROUTE_FUSED = 1,      /* all levels of one query in one program (per-query) */
+    PISA_ROUTE_LEVELS = 2      /* all queries advance one level at a time; at every level
+                                  the (query, kept node) pairs are clustered by node and
+                                  scored with the node's data staged once (K_top <= 16) */
 } pisa_route_mode;
 
 /*
@@ -114,7 +117,7 @@ pisa_status pisa_pyramid_append(const pisa_pyramid* p, const void* K, pisa_dtype
                                 const int64_t* seqlen, void* stream);
 
 /* Workspace bytes pisa_route_prefill needs for these arguments (0 for
- * PISA_ROUTE_FUSED). */
+ * PISA_ROUTE_FUSED). The workspace must be 256-byte aligned. */
 pisa_status pisa_route_prefill_workspace(const pisa_pyramid* p, int64_t N, int32_t H_q,
                                          int32_t K_top, int32_t mode, size_t* bytes);
 
@@ -196,29 +199,34 @@ pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt,
 
 /*
  * Stage timing, for measurement. The library queues each call as one or more
- * kernel stages; pisa_time_stage arms, for the calling host thread, a pair of
- * caller-created hipEvent_t (passed as void*) for one stage id. The next call
- * on this thread that runs that stage records start_event on its stream just
- * before the stage's first kernel and stop_event just after its last kernel,
- * then disarms the stage. Nothing else changes: the events are the caller's,
- * the library neither creates nor waits on them. Passing NULL events disarms.
- * Errors: PISA_EINVAL (stage id out of range, or only one event given).
+ * kernel stages; a stage may run several times in one call (once per level).
+ * pisa_time_stage appends a pair of caller-created hipEvent_t (passed as
+ * void*) to a queue, per host thread and stage id (at most 16 pairs). Each
+ * later occurrence of that stage on this thread consumes the oldest pair: it
+ * records start_event on its stream just before the stage's first kernel and
+ * stop_event just after its last one. The events are the caller's; the
+ * library neither creates nor waits on them. NULL events clear the stage's
+ * queue. pisa_time_stage_pending returns the pairs not yet consumed (-1 for
+ * a bad stage id). Errors: PISA_EINVAL (stage id out of range, or only one
+ * event given), PISA_ENOSPACE (queue full).
  */
 typedef enum pisa_stage {
     PISA_STAGE_BUILD = 0,         /* pisa_build_pyramid: all levels */
     PISA_STAGE_APPEND = 1,        /* pisa_pyramid_append */
     PISA_STAGE_ROUTE_FUSED = 2,   /* pisa_route_prefill, PISA_ROUTE_FUSED */
     PISA_STAGE_ROUTE_DECODE = 3,  /* pisa_route_decode */
-    PISA_STAGE_UPPER = 4,         /* two-stage: levels L..2 per (query, KV head) */
-    PISA_STAGE_CLUSTER = 5,       /* two-stage: clear, scan and scatter of the query clusters */
-    PISA_STAGE_LEAF = 6,          /* two-stage: leaf scoring per retained level-2 node */
-    PISA_STAGE_FINAL = 7,         /* two-stage: final Select_K */
+    PISA_STAGE_UPPER = 4,         /* two-stage: levels L..2 per (query, KV head);
+                                     level-synchronous: clustered scoring of one level >= 2 */
+    PISA_STAGE_CLUSTER = 5,       /* clear, scan and scatter of the query clusters */
+    PISA_STAGE_LEAF = 6,          /* leaf scoring of the clustered (query, level-2 node) pairs */
+    PISA_STAGE_FINAL = 7,         /* two-stage: final Select_K; level-synchronous: Select_K of one level */
     PISA_STAGE_ATTN = 8,          /* pisa_sparse_attn */
     PISA_STAGE_BSA = 9,           /* pisa_bsa_select */
     PISA_STAGE_COUNT = 10
 } pisa_stage;
 
 pisa_status pisa_time_stage(int32_t stage, void* start_event, void* stop_event);
+int32_t pisa_time_stage_pending(int32_t stage);
 
 /* Static description of a status code. */
 const char* pisa_status_str(pisa_status s);

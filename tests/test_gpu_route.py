@@ -10,7 +10,7 @@ from tests.parity import compare
 
 pytestmark = pytest.mark.gpu
 
-MODES = {"two_stage": pisa.TWO_STAGE, "fused": pisa.FUSED}
+MODES = {"two_stage": pisa.TWO_STAGE, "fused": pisa.FUSED, "levels": pisa.LEVELS}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -82,7 +82,7 @@ def _positions(w, sample):
     return t
 
 
-@pytest.mark.parametrize("mode", ["two_stage", "fused"])
+@pytest.mark.parametrize("mode", ["two_stage", "fused", "levels"])
 @pytest.mark.parametrize("case,K_top,causal,sample", [
     ("tiny", 4, True, None),
     ("tiny", 32, True, None),
@@ -97,6 +97,8 @@ def _positions(w, sample):
 ])
 def test_route_matches_oracle(mode, case, K_top, causal, sample):
     w = CASES[case]
+    if mode == "levels" and 16 < K_top < -(-w.N // w.C):
+        pytest.skip("the level-synchronous router ranks at most 16 blocks")
     print("case", case, "mode", mode, "K_top", K_top, "causal", causal, flush=True)
     Q, K = _inputs(w)
     t = _positions(w, sample)
@@ -110,15 +112,19 @@ def test_route_matches_oracle(mode, case, K_top, causal, sample):
         print(case, mode, b, stats)
 
 
-def test_fused_and_two_stage_agree_and_are_deterministic():
+def test_routers_agree_and_are_deterministic():
     w = CASES["p16k"]
     Q, K = _inputs(w)
     _, i1, s1 = _gpu_route(w, Q, K, 8, True, pisa.TWO_STAGE)
     _, i2, s2 = _gpu_route(w, Q, K, 8, True, pisa.TWO_STAGE)
     _, i3, s3 = _gpu_route(w, Q, K, 8, True, pisa.FUSED)
+    _, i4, s4 = _gpu_route(w, Q, K, 8, True, pisa.LEVELS)
+    _, i5, s5 = _gpu_route(w, Q, K, 8, True, pisa.LEVELS)
     assert (i1 == i2).all() and np.array_equal(s1, s2, equal_nan=True)  # bit-identical reruns
-    diff = (i1 != i3).any(-1).mean()
-    assert diff < 0.01, "fused and two-stage disagree on %.4f of the selections" % diff
+    assert (i4 == i5).all() and np.array_equal(s4, s5, equal_nan=True)
+    for other, name in ((i3, "fused"), (i4, "levels")):
+        diff = (i1 != other).any(-1).mean()
+        assert diff < 0.01, "%s and two-stage disagree on %.4f of the selections" % (name, diff)
 
 
 def test_outputs_are_fully_written():
@@ -127,9 +133,12 @@ def test_outputs_are_fully_written():
     Qd, Kd = Q.cuda(), K.cuda()
     pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
     pyr.build(Kd, w.N)
-    for mode in (pisa.TWO_STAGE, pisa.FUSED):
+    for mode in (pisa.TWO_STAGE, pisa.FUSED, pisa.LEVELS):
+        ws = torch.full((pisa.route_workspace_bytes(pyr, w.N, w.H_q, 8, mode) + 1,), 0x5A, dtype=torch.uint8,
+                        device="cuda")  # stale workspace contents must not matter
         out = torch.full((w.B, w.H_kv, w.N, 8), -7, dtype=torch.int32, device="cuda")
         sc = torch.full((w.B, w.H_kv, w.N, 8), 12345.0, dtype=torch.float32, device="cuda")
-        pisa.route_prefill(pyr, Qd, Kd, w.N, 8, mode=mode, with_score=True, out=out, score_out=sc)
+        pisa.route_prefill(pyr, Qd, Kd, w.N, 8, mode=mode, with_score=True, out=out, score_out=sc,
+                           workspace=ws if ws.numel() > 1 else None)
         torch.cuda.synchronize()
         assert not (out == -7).any() and not (sc == 12345.0).any()
