@@ -162,7 +162,7 @@ int levels_top(int64_t N, int C, int g, int K_top)
 }
 
 struct LevelsLayout {
-    size_t kept0, kept1, flags, u, counts, offsets, chunk_off, entries, total;
+    size_t kept0, kept1, flags, u, counts, offsets, chunk_off, chunk_cl, block_sums, entries, total;
     int64_t cnt_total, max_clusters;
     int64_t cnt_off[PISA_MAX_LEVELS + 2];
     int l_top;
@@ -178,7 +178,10 @@ LevelsLayout levels_layout(const pisa_pyramid* p, int64_t N, int K_top)
     int64_t c = 0;
     for (int l = 1; l <= w.l_top; ++l) {
         w.cnt_off[l] = c;
-        const int64_t nb = BH * nodes_at(N, p->C, p->g, l + 1);  // clusters of level l: kept nodes of level l + 1
+        // clusters of level l: (query window, sequence and KV head, kept node of level l + 1)
+        const int wl = pisa::cluster_win_log2(l);
+        const int64_t n_win = (N + ((int64_t)1 << wl) - 1) >> wl;
+        const int64_t nb = n_win * BH * nodes_at(N, p->C, p->g, l + 1);
         c += nb;
         if (nb > w.max_clusters) w.max_clusters = nb;
     }
@@ -191,6 +194,9 @@ LevelsLayout levels_layout(const pisa_pyramid* p, int64_t N, int K_top)
     w.counts = o; o = al(o + (size_t)2 * c * 4);  // counts, then cursors (cleared together)
     w.offsets = o; o = al(o + (size_t)(w.max_clusters + 1) * 4);
     w.chunk_off = o; o = al(o + (size_t)(w.max_clusters + 1) * 4);
+    // chunks of a level: at most entries / chunk + clusters (smallest chunk: kRegChunk entries)
+    w.chunk_cl = o; o = al(o + (size_t)(items * K_top / pisa::kRegChunk + w.max_clusters + 1) * 4);
+    w.block_sums = o; o = al(o + (size_t)2 * (w.max_clusters / 1024 + 2) * 4);
     w.entries = o; o = al(o + (size_t)items * K_top * 4);
     w.total = o;
     return w;
@@ -379,6 +385,8 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
         memcpy(la.cnt_off, w.cnt_off, sizeof(la.cnt_off));
         la.offsets = (int32_t*)(base + w.offsets);
         la.chunk_off = (int32_t*)(base + w.chunk_off);
+        la.chunk_cl = (int32_t*)(base + w.chunk_cl);
+        la.block_sums = (int32_t*)(base + w.block_sums);
         la.entries = (int32_t*)(base + w.entries);
         la.l_top = w.l_top;
         hipError_t e = launch_levels(la, dti, p->d, st);

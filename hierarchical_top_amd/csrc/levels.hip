@@ -55,11 +55,16 @@ __device__ __forceinline__ bool in3(int64_t x, const int64_t F[3], int nF)
     return (nF > 0 && x == F[0]) || (nF > 1 && x == F[1]) || (nF > 2 && x == F[2]);
 }
 
-template <int KMAX>
+// Select_K of one level, one item per thread. KMAX >= K_top; GB = g when the
+// item's candidate scores are loaded into registers up front (g in {2, 4}),
+// 0 to read them from memory as they are needed (larger g).
+constexpr int kSelItemsPerBlock = kSelThreads * kSelItemsPerThread;
+
+template <int KMAX, int GB>
 __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int64_t t, int* s_hist, bool use_lds)
 {
     const int64_t i = bh * a.N + t;
-    const int K = a.K_top, g = 1 << a.g_log2;
+    const int K = a.K_top, g = GB ? GB : 1 << a.g_log2;
     const int l = a.level;
     const int64_t c = t >> a.c_log2;
     const bool causal = a.causal != 0;
@@ -68,17 +73,21 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
     const int64_t M_l = (a.N + ((int64_t)1 << span_log2) - 1) >> span_log2;
     const int64_t elig_max = causal ? (t >> span_log2) : M_l - 1;
 
-    // candidates of this level: children of the kept nodes of level l + 1 (or all eligible nodes)
+    // kept nodes of level l + 1 (the parents of this level's candidates)
+    int kin[KMAX];
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) kin[s] = -1;
     int64_t nA = 0;
-    const int32_t* kin = a.kept_in ? a.kept_in + i * K : nullptr;
     if (a.init) {
         nA = elig_max + 1 < M_l ? elig_max + 1 : M_l;
     } else {
-        for (int s = 0; s < K; ++s) {
-            const int P = kin[s];
-            if (P < 0) break;
-            nA += n_children(P, g, M_l, elig_max);
-        }
+        const int32_t* kp = a.kept_in + i * K;
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s)
+            if (s < K) kin[s] = kp[s];
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s)
+            if (kin[s] >= 0) nA += n_children(kin[s], g, M_l, elig_max);
     }
 
     int ids[KMAX];
@@ -100,11 +109,11 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
         if (a.init) {
             for (int64_t x = 0; x < nA; ++x) put((int)x, INFINITY);
         } else {
-            for (int s = 0; s < K; ++s) {
-                const int P = kin[s];
-                if (P < 0) break;
-                const int64_t nc = n_children(P, g, M_l, elig_max);
-                for (int64_t j = 0; j < nc; ++j) put((int)((int64_t)P * g + j), INFINITY);
+#pragma unroll
+            for (int s = 0; s < KMAX; ++s) {
+                if (kin[s] < 0) continue;
+                const int64_t nc = n_children(kin[s], g, M_l, elig_max);
+                for (int64_t j = 0; j < nc; ++j) put((int)((int64_t)kin[s] * g + j), INFINITY);
             }
         }
     } else {
@@ -116,21 +125,49 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) { bu[j] = -INFINITY; bi[j] = 0x7fffffff; }
         const float* urow = a.u + i * (int64_t)(K * g);
-        for (int s = 0; s < K; ++s) {
-            const int P = kin[s];
-            if (P < 0) break;
-            const int64_t nc = n_children(P, g, M_l, elig_max);
-            for (int64_t j = 0; j < nc; ++j) {
-                const int64_t x = (int64_t)P * g + j;
-                if (in3(x, F, nF)) continue;
-                float xu = urow[s * g + j];
-                int xi = (int)x;
+        auto offer = [&](float xu, int xi) {
 #pragma unroll
-                for (int q = 0; q < KMAX; ++q) {
-                    if (q < R && before(xu, xi, bu[q], bi[q])) {
-                        const float tu = bu[q]; bu[q] = xu; xu = tu;
-                        const int ti = bi[q]; bi[q] = xi; xi = ti;
+            for (int q = 0; q < KMAX; ++q) {
+                if (q < R && before(xu, xi, bu[q], bi[q])) {
+                    const float tu = bu[q]; bu[q] = xu; xu = tu;
+                    const int ti = bi[q]; bi[q] = xi; xi = ti;
+                }
+            }
+        };
+        if constexpr (GB > 0) {
+            // the whole score row in registers: K * g floats, 16-byte loads when aligned
+            float ur[KMAX * GB];
+            if (((K * GB) & 3) == 0) {
+#pragma unroll
+                for (int v = 0; v < KMAX * GB / 4; ++v) {
+                    if (4 * v < K * GB) {
+                        const f32x4 x4 = reinterpret_cast<const f32x4*>(urow)[v];
+                        ur[4 * v] = x4[0]; ur[4 * v + 1] = x4[1]; ur[4 * v + 2] = x4[2]; ur[4 * v + 3] = x4[3];
                     }
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < KMAX * GB; ++v)
+                    if (v < K * GB) ur[v] = urow[v];
+            }
+#pragma unroll
+            for (int s = 0; s < KMAX; ++s) {
+                if (kin[s] < 0) continue;
+                const int64_t nc = n_children(kin[s], g, M_l, elig_max);
+#pragma unroll
+                for (int j = 0; j < GB; ++j) {
+                    const int64_t x = (int64_t)kin[s] * GB + j;
+                    if (j < nc && !in3(x, F, nF)) offer(ur[s * GB + j], (int)x);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KMAX; ++s) {
+                if (kin[s] < 0) continue;
+                const int64_t nc = n_children(kin[s], g, M_l, elig_max);
+                for (int64_t j = 0; j < nc; ++j) {
+                    const int64_t x = (int64_t)kin[s] * g + j;
+                    if (!in3(x, F, nF)) offer(urow[s * g + j], (int)x);
                 }
             }
         }
@@ -159,6 +196,7 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
         if (j < K) kout[j] = j < nkept ? ids[j] : -1;
+    if (!a.counts) return;  // the next level is scored densely: no clusters to count
 
     // next level: is it ranked for this item, and which kept nodes own ranked candidates?
     const int shl2 = shl - a.g_log2;
@@ -182,8 +220,20 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
                 for (int k = 0; k < nF2; ++k) nforced += (F2[k] >= P * g && F2[k] < P * g + nc) ? 1 : 0;
                 if (nc > nforced) {
                     mask |= (uint64_t)1 << j;
-                    if (use_lds) atomicAdd(&s_hist[P], 1);
-                    else atomicAdd(&a.counts[bh * a.M_bins + P], 1);
+                    if (use_lds) {
+                        // forced and current-path nodes are shared by neighbouring queries:
+                        // one LDS atomic per wave when every active lane adds to the same bin
+                        const uint64_t act = ballot(true);
+                        const int64_t P0 = __builtin_amdgcn_readfirstlane((int)P);
+                        if (ballot(P == P0) == act) {
+                            if (lane_id() == __builtin_ctzll(act)) atomicAdd(&s_hist[P0], __popcll(act));
+                        } else {
+                            atomicAdd(&s_hist[P], 1);
+                        }
+                    } else {
+                        const int64_t BH = (int64_t)a.B * a.H;
+                        atomicAdd(&a.counts[((t >> a.win_log2) * BH + bh) * a.M_bins + P], 1);
+                    }
                 }
             }
         }
@@ -191,13 +241,13 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
     a.flags_out[i] = (int64_t)mask;
 }
 
-template <int KMAX>
+template <int KMAX, int GB>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
 {
     extern __shared__ int s_hist[];
     const int64_t bh = blockIdx.y;
-    const int64_t t0 = (int64_t)blockIdx.x * (kSelThreads * kSelItemsPerThread);
-    const bool count = a.level > 1;
+    const int64_t t0 = (int64_t)blockIdx.x * kSelItemsPerBlock;
+    const bool count = a.level > 1 && a.counts;
     const bool use_lds = count && a.M_bins <= kLdsBins;
     if (use_lds) {
         for (int64_t k = threadIdx.x; k < a.M_bins; k += kSelThreads) s_hist[k] = 0;
@@ -205,13 +255,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     }
     for (int k = 0; k < kSelItemsPerThread; ++k) {
         const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
-        if (t < a.N) select_item<KMAX>(a, bh, t, s_hist, use_lds);
+        if (t < a.N) select_item<KMAX, GB>(a, bh, t, s_hist, use_lds);
     }
     if (use_lds) {
         __syncthreads();
+        const int64_t BH = (int64_t)a.B * a.H;
+        int32_t* cnt = a.counts + ((t0 >> a.win_log2) * BH + bh) * a.M_bins;  // the block lies in one window
         for (int64_t k = threadIdx.x; k < a.M_bins; k += kSelThreads) {
             const int v = s_hist[k];
-            if (v) atomicAdd(&a.counts[bh * a.M_bins + k], v);
+            if (v) atomicAdd(&cnt[k], v);
         }
     }
 }
@@ -219,14 +271,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
 // Cluster entries: (t << 6) | slot for every flagged slot of every item, grouped
 // by kept node. Positions inside a cluster are reserved per workgroup.
 struct ScatterLvArgs {
-    int H, K_top;
-    int64_t N, M_bins;
+    int H, K_top, win_log2;
+    int64_t N, M_bins, BH;
     const int32_t* kept;
     const int64_t* flags;
     const int32_t* offsets;
     int32_t* cursor;
     int32_t* entries;
 };
+
+// Adds v to an LDS counter and returns the old value, with one atomic per wave
+// when every active lane targets the same counter.
+__device__ __forceinline__ int lds_add(int* p_mine, int P, int* base_arr)
+{
+    const uint64_t act = ballot(true);
+    const int P0 = __builtin_amdgcn_readfirstlane(P);
+    if (ballot(P == P0) == act) {
+        const int leader = __builtin_ctzll(act);
+        int old = 0;
+        if (lane_id() == leader) old = atomicAdd(&base_arr[P0], __popcll(act));
+        old = __shfl(old, leader, 64);
+        return old + rank_below(act);
+    }
+    return atomicAdd(p_mine, 1);
+}
 
 __global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a)
 {
@@ -236,20 +304,21 @@ __global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a
     const int64_t bh = blockIdx.y;
     const int64_t t0 = (int64_t)blockIdx.x * (kSelThreads * kSelItemsPerThread);
     const bool use_lds = a.M_bins <= kLdsBins;
-    const int32_t* base_off = a.offsets + bh * a.M_bins;
-    int32_t* cur = a.cursor + bh * a.M_bins;
     if (use_lds) {
+        const int64_t cbase = ((t0 >> a.win_log2) * a.BH + bh) * a.M_bins;  // the block lies in one window
+        const int32_t* base_off = a.offsets + cbase;
+        int32_t* cur = a.cursor + cbase;
         for (int64_t k = threadIdx.x; k < a.M_bins; k += kSelThreads) s_cnt[k] = 0;
         __syncthreads();
         for (int k = 0; k < kSelItemsPerThread; ++k) {
             const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
             if (t >= a.N) continue;
             const int64_t i = bh * a.N + t;
-            uint64_t m = (uint64_t)a.flags[i];
-            while (m) {
-                const int s = __builtin_ctzll(m);
-                m &= m - 1;
-                atomicAdd(&s_cnt[a.kept[i * a.K_top + s]], 1);
+            const uint64_t m = (uint64_t)a.flags[i];
+            for (int s = 0; s < a.K_top; ++s) {
+                if (!((m >> s) & 1)) continue;
+                const int P = a.kept[i * a.K_top + s];
+                lds_add(&s_cnt[P], P, s_cnt);
             }
         }
         __syncthreads();
@@ -258,56 +327,118 @@ __global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a
             s_pos[k] = v ? base_off[k] + atomicAdd(&cur[k], v) : 0;
         }
         __syncthreads();
-    }
-    for (int k = 0; k < kSelItemsPerThread; ++k) {
-        const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
-        if (t >= a.N) continue;
-        const int64_t i = bh * a.N + t;
-        uint64_t m = (uint64_t)a.flags[i];
-        while (m) {
-            const int s = __builtin_ctzll(m);
-            m &= m - 1;
-            const int P = a.kept[i * a.K_top + s];
-            const int pos = use_lds ? atomicAdd(&s_pos[P], 1) : base_off[P] + atomicAdd(&cur[P], 1);
-            a.entries[pos] = (int32_t)((t << 6) | s);
+        for (int k = 0; k < kSelItemsPerThread; ++k) {
+            const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
+            if (t >= a.N) continue;
+            const int64_t i = bh * a.N + t;
+            const uint64_t m = (uint64_t)a.flags[i];
+            for (int s = 0; s < a.K_top; ++s) {
+                if (!((m >> s) & 1)) continue;
+                const int P = a.kept[i * a.K_top + s];
+                const int pos = lds_add(&s_pos[P], P, s_pos);
+                a.entries[pos] = (int32_t)((t << 6) | s);
+            }
+        }
+    } else {
+        for (int k = 0; k < kSelItemsPerThread; ++k) {
+            const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
+            if (t >= a.N) continue;
+            const int64_t i = bh * a.N + t;
+            const int64_t cbase = ((t >> a.win_log2) * a.BH + bh) * a.M_bins;
+            uint64_t m = (uint64_t)a.flags[i];
+            while (m) {
+                const int s = __builtin_ctzll(m);
+                m &= m - 1;
+                const int P = a.kept[i * a.K_top + s];
+                const int pos = a.offsets[cbase + P] + atomicAdd(&a.cursor[cbase + P], 1);
+                a.entries[pos] = (int32_t)((t << 6) | s);
+            }
         }
     }
 }
 
-// Exclusive scans of cluster sizes and of their chunk counts (one workgroup).
-__global__ __launch_bounds__(1024) void cluster_scan_kernel(const int32_t* __restrict__ counts, int64_t n, int qc,
-                                                            int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ chunk_off)
+// Exclusive scans of cluster sizes and of their chunk counts, in two passes:
+// per-block totals, then each block scans its 1024 clusters after adding the
+// totals of the blocks before it.
+__device__ __forceinline__ void block_scan2(int& x0, int& x1, int* s_w0, int* s_w1)
 {
-    __shared__ int s_w0[16], s_w1[16];
-    __shared__ int s_carry[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) { s_carry[0] = 0; s_carry[1] = 0; }
-    __syncthreads();
-    for (int64_t base = 0; base < n; base += 1024) {
-        const int64_t i = base + tid;
-        const int cnt = i < n ? counts[i] : 0;
-        const int nch = (cnt + qc - 1) / qc;
-        int x0 = cnt, x1 = nch;
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y0 = __shfl_up(x0, o, 64), y1 = __shfl_up(x1, o, 64);
-            if (lane >= o) { x0 += y0; x1 += y1; }
-        }
-        if (lane == 63) { s_w0[wave] = x0; s_w1[wave] = x1; }
-        __syncthreads();
-        int p0 = s_carry[0], p1 = s_carry[1];
-        for (int w = 0; w < wave; ++w) { p0 += s_w0[w]; p1 += s_w1[w]; }
-        if (i < n) {
-            offsets[i] = p0 + x0 - cnt;
-            chunk_off[i] = p1 + x1 - nch;
-        }
-        __syncthreads();
-        if (tid == 1023) { s_carry[0] = p0 + x0; s_carry[1] = p1 + x1; }
-        __syncthreads();
+    const int v0 = x0, v1 = x1;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y0 = __shfl_up(x0, o, 64), y1 = __shfl_up(x1, o, 64);
+        if (lane >= o) { x0 += y0; x1 += y1; }
     }
-    if (tid == 0) {
-        offsets[n] = s_carry[0];
-        chunk_off[n] = s_carry[1];
+    if (lane == 63) { s_w0[wave] = x0; s_w1[wave] = x1; }
+    __syncthreads();
+    int p0 = 0, p1 = 0;
+    for (int w = 0; w < wave; ++w) { p0 += s_w0[w]; p1 += s_w1[w]; }
+    x0 = p0 + x0 - v0;  // exclusive
+    x1 = p1 + x1 - v1;
+}
+
+__global__ __launch_bounds__(1024) void scan_totals_kernel(const int32_t* __restrict__ counts, int64_t n, int qc,
+                                                           int32_t* __restrict__ sums)
+{
+    __shared__ int s0[16], s1[16];
+    const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+    const int cnt = i < n ? counts[i] : 0;
+    int x0 = cnt, x1 = (cnt + qc - 1) / qc;
+    for (int o = 32; o > 0; o >>= 1) { x0 += __shfl_xor(x0, o, 64); x1 += __shfl_xor(x1, o, 64); }
+    if ((threadIdx.x & 63) == 0) { s0[threadIdx.x >> 6] = x0; s1[threadIdx.x >> 6] = x1; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int a0 = 0, a1 = 0;
+        for (int w = 0; w < 16; ++w) { a0 += s0[w]; a1 += s1[w]; }
+        sums[2 * blockIdx.x] = a0;
+        sums[2 * blockIdx.x + 1] = a1;
+    }
+}
+
+__global__ __launch_bounds__(1024) void scan_final_kernel(const int32_t* __restrict__ counts, int64_t n, int qc,
+                                                          const int32_t* __restrict__ sums,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ chunk_off,
+                                                          int32_t* __restrict__ chunk_cl)
+{
+    __shared__ int s_w0[16], s_w1[16], s_b[2];
+    // prefix of the earlier blocks' totals
+    if (threadIdx.x < 64) {
+        int a0 = 0, a1 = 0;
+        for (int k = threadIdx.x; k < (int)blockIdx.x; k += 64) { a0 += sums[2 * k]; a1 += sums[2 * k + 1]; }
+        for (int o = 32; o > 0; o >>= 1) { a0 += __shfl_xor(a0, o, 64); a1 += __shfl_xor(a1, o, 64); }
+        if (threadIdx.x == 0) { s_b[0] = a0; s_b[1] = a1; }
+    }
+    __syncthreads();
+    const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+    const int cnt = i < n ? counts[i] : 0;
+    const int nch = (cnt + qc - 1) / qc;
+    int x0 = cnt, x1 = nch;
+    block_scan2(x0, x1, s_w0, s_w1);
+    x0 += s_b[0];
+    x1 += s_b[1];
+    if (i < n) {
+        offsets[i] = x0;
+        chunk_off[i] = x1;
+        for (int k = 0; k < nch; ++k) chunk_cl[x1 + k] = (int32_t)i;  // chunk -> cluster
+    }
+    if (i == n - 1) {
+        offsets[n] = x0 + cnt;
+        chunk_off[n] = x1 + nch;
+    }
+}
+
+// Output when no level is ranked (at most K_top leaf blocks): all eligible leaves.
+__global__ __launch_bounds__(256) void keep_all_kernel(SelectArgs a)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)a.B * a.H * a.N) return;
+    const int64_t t = i % a.N;
+    const int64_t M1 = (a.N + ((int64_t)1 << a.c_log2) - 1) >> a.c_log2;
+    const int64_t last = a.causal ? (t >> a.c_log2) : M1 - 1;
+    const int64_t n = last + 1 < M1 ? last + 1 : M1;
+    for (int j = 0; j < a.K_top; ++j) {
+        a.idx[i * a.K_top + j] = j < n ? j : -1;
+        if (a.score) a.score[i * a.K_top + j] = j < n ? INFINITY : -INFINITY;
     }
 }
 
@@ -326,13 +457,20 @@ static int64_t nodes_n(int64_t n, int c_log2, int g_log2, int l)
 
 static hipError_t launch_select(const SelectArgs& sa, int K_top, hipStream_t s)
 {
-    const int64_t per = (int64_t)kSelThreads * kSelItemsPerThread;
-    const dim3 grid((unsigned)((sa.N + per - 1) / per), (unsigned)(sa.B * sa.H));
-    const size_t lds = (sa.level > 1 && sa.M_bins <= kLdsBins) ? (size_t)sa.M_bins * 4 : 0;
-    if (K_top <= 8)
-        hipLaunchKernelGGL(select_kernel<8>, grid, dim3(kSelThreads), lds, s, sa);
-    else
-        hipLaunchKernelGGL(select_kernel<16>, grid, dim3(kSelThreads), lds, s, sa);
+    const dim3 grid((unsigned)((sa.N + kSelItemsPerBlock - 1) / kSelItemsPerBlock), (unsigned)(sa.B * sa.H));
+    const size_t lds = (sa.level > 1 && sa.counts && sa.M_bins <= kLdsBins) ? (size_t)sa.M_bins * 4 : 0;
+    const int g = 1 << sa.g_log2;
+#define PISA_SEL(KM, GBV) hipLaunchKernelGGL((select_kernel<KM, GBV>), grid, dim3(kSelThreads), lds, s, sa)
+    if (K_top <= 8) {
+        if (g == 4) PISA_SEL(8, 4);
+        else if (g == 2) PISA_SEL(8, 2);
+        else PISA_SEL(8, 0);
+    } else {
+        if (g == 4) PISA_SEL(16, 4);
+        else if (g == 2) PISA_SEL(16, 2);
+        else PISA_SEL(16, 0);
+    }
+#undef PISA_SEL
     return hipGetLastError();
 }
 
@@ -350,10 +488,10 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
     sa.causal = r.causal; sa.N = N; sa.idx = r.idx; sa.score = r.score;
 
     if (a.l_top == 0) {
-        // at most K_top leaf blocks: every eligible leaf is kept
-        sa.level = 1;
-        sa.init = 1;
-        return launch_select(sa, r.K_top, s);
+        // at most K_top leaf blocks: every eligible leaf is kept, unscored (section 3.2)
+        const int64_t items = (int64_t)BH * N;
+        hipLaunchKernelGGL(keep_all_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, sa);
+        return hipGetLastError();
     }
 
     stage_mark(PISA_STAGE_CLUSTER, false, s);
@@ -370,28 +508,79 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
     sa.flags_out = a.flags;
     sa.M_bins = nodes_n(N, p.c_log2, p.g_log2, a.l_top + 1);
     sa.counts = a.counts + a.cnt_off[a.l_top];
+    sa.win_log2 = cluster_win_log2(a.l_top);
+    {
+        const bool dl = a.l_top >= 2 && (p.g == 2 || p.g == 4) &&
+                        nodes_n(N, p.c_log2, p.g_log2, a.l_top + 1) <= kDenseParents &&
+                        nodes_n(N, p.c_log2, p.g_log2, a.l_top - 1) <= kDenseRows;
+        if (dl) sa.counts = nullptr;
+    }
     if ((err = launch_select(sa, r.K_top, s)) != hipSuccess) return err;
     stage_mark(PISA_STAGE_FINAL, true, s);
 
+    const int64_t per_blk = (int64_t)kSelThreads * kSelItemsPerThread;
+    // levels scored densely (see kDenseParents / kDenseRows)
+    auto dense_level = [&](int l) {
+        return l >= 2 && (p.g == 2 || p.g == 4) && nodes_n(N, p.c_log2, p.g_log2, l + 1) <= kDenseParents &&
+               nodes_n(N, p.c_log2, p.g_log2, l - 1) <= kDenseRows;
+    };
     for (int l = a.l_top; l >= 1; --l) {
+        if (dense_level(l)) {
+            DenseArgs da;
+            memset(&da, 0, sizeof(da));
+            da.Q = r.Q; da.N = N; da.B = p.B; da.H = p.H; da.H_q = r.H_q; da.G = r.G; da.K_top = r.K_top; da.g = p.g;
+            da.causal = r.causal;
+            da.rows = p.buf + p.off[l - 1];
+            da.rows_b_stride = (int64_t)p.H * p.M_cap[l - 1] * d;
+            da.rows_h_stride = p.M_cap[l - 1] * d;
+            da.rows_limit = nodes_n(N, p.c_log2, p.g_log2, l - 1);
+            da.par_span_log2 = p.c_log2 + l * p.g_log2;
+            da.M_par = nodes_n(N, p.c_log2, p.g_log2, l + 1);
+            da.kept = a.kept[cur];
+            da.u = a.u;
+            stage_mark(PISA_STAGE_UPPER, false, s);
+            if ((err = launch_dense(da, dtype, d, s)) != hipSuccess) return err;
+            stage_mark(PISA_STAGE_UPPER, true, s);
+            stage_mark(PISA_STAGE_FINAL, false, s);
+            sa.level = l;
+            sa.init = 0;
+            sa.kept_in = a.kept[cur];
+            sa.u = a.u;
+            sa.kept_out = a.kept[cur ^ 1];
+            sa.flags_out = a.flags;
+            sa.M_bins = nodes_n(N, p.c_log2, p.g_log2, l);
+            sa.counts = (l > 1 && !dense_level(l - 1)) ? a.counts + a.cnt_off[l - 1] : nullptr;
+            sa.win_log2 = l > 1 ? cluster_win_log2(l - 1) : 0;
+            if ((err = launch_select(sa, r.K_top, s)) != hipSuccess) return err;
+            stage_mark(PISA_STAGE_FINAL, true, s);
+            cur ^= 1;
+            continue;
+        }
         const int64_t M_bins = nodes_n(N, p.c_log2, p.g_log2, l + 1);
-        const int64_t n_clusters = (int64_t)BH * M_bins;
+        const int wl = cluster_win_log2(l);
+        const int64_t n_win = (N + ((int64_t)1 << wl) - 1) >> wl;
+        const int64_t n_clusters = n_win * BH * M_bins;
         const bool leaf = l == 1;
-        const int qc = leaf ? 128 : 256;
+        // leaf: 256 entries per workgroup sharing one node's g * C staged keys; upper levels with
+        // g * g <= 16 rows per node: 32 entries per wave, rows held in registers
+        const bool reg_rows = !leaf && p.g * p.g <= 16;
+        const int qc = reg_rows ? kRegChunk : 256;
         int32_t* counts = a.counts + a.cnt_off[l];
         int32_t* cursor = a.cursor + a.cnt_off[l];
 
         stage_mark(PISA_STAGE_CLUSTER, false, s);
-        hipLaunchKernelGGL(cluster_scan_kernel, dim3(1), dim3(1024), 0, s, counts, n_clusters, qc, a.offsets,
-                           a.chunk_off);
+        const unsigned nsb = (unsigned)((n_clusters + 1023) / 1024);
+        hipLaunchKernelGGL(scan_totals_kernel, dim3(nsb), dim3(1024), 0, s, counts, n_clusters, qc, a.block_sums);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(scan_final_kernel, dim3(nsb), dim3(1024), 0, s, counts, n_clusters, qc, a.block_sums,
+                           a.offsets, a.chunk_off, a.chunk_cl);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         ScatterLvArgs sc;
-        sc.H = p.H; sc.K_top = r.K_top; sc.N = N; sc.M_bins = M_bins;
+        sc.H = p.H; sc.K_top = r.K_top; sc.win_log2 = wl; sc.N = N; sc.M_bins = M_bins; sc.BH = BH;
         sc.kept = a.kept[cur]; sc.flags = a.flags; sc.offsets = a.offsets; sc.cursor = cursor;
         sc.entries = a.entries;
         {
-            const int64_t per = (int64_t)kSelThreads * kSelItemsPerThread;
-            const dim3 grid((unsigned)((N + per - 1) / per), (unsigned)BH);
+            const dim3 grid((unsigned)((N + per_blk - 1) / per_blk), (unsigned)BH);
             const size_t lds = M_bins <= kLdsBins ? (size_t)2 * M_bins * 4 : 0;
             hipLaunchKernelGGL(scatter_lv_kernel, grid, dim3(kSelThreads), lds, s, sc);
             if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -419,10 +608,16 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         sc2.qc = qc;
         sc2.n_clusters = n_clusters;
         sc2.M_bins = M_bins;
-        sc2.offsets = a.offsets; sc2.chunk_off = a.chunk_off; sc2.entries = a.entries; sc2.u = a.u;
-        const int64_t grid = ((int64_t)BH * N * r.K_top + qc - 1) / qc + n_clusters;
+        sc2.BH = BH;
+        // leaf windows are large and shared by all XCDs (one window's queries and keys at a
+        // time in the last-level cache); small upper-level windows go to one XCD each (L2)
+        sc2.xcd = leaf ? 0 : 1;
+        sc2.offsets = a.offsets; sc2.chunk_off = a.chunk_off; sc2.chunk_cl = a.chunk_cl; sc2.entries = a.entries;
+        sc2.u = a.u;
+        int64_t grid = ((int64_t)BH * N * r.K_top + qc - 1) / qc + n_clusters;  // bound on the chunks
+        if (reg_rows) grid = (grid + kRegWaves - 1) / kRegWaves;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, false, s);
-        if ((err = launch_score(sc2, dtype, d, leaf, grid, s)) != hipSuccess) return err;
+        if ((err = launch_score(sc2, dtype, d, leaf ? 1 : (reg_rows ? 2 : 0), grid, s)) != hipSuccess) return err;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, true, s);
 
         stage_mark(PISA_STAGE_FINAL, false, s);
@@ -433,7 +628,8 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         sa.kept_out = a.kept[cur ^ 1];
         sa.flags_out = a.flags;
         sa.M_bins = nodes_n(N, p.c_log2, p.g_log2, l);
-        sa.counts = l > 1 ? a.counts + a.cnt_off[l - 1] : nullptr;
+        sa.counts = (l > 1 && !dense_level(l - 1)) ? a.counts + a.cnt_off[l - 1] : nullptr;
+        sa.win_log2 = l > 1 ? cluster_win_log2(l - 1) : 0;
         if ((err = launch_select(sa, r.K_top, s)) != hipSuccess) return err;
         stage_mark(PISA_STAGE_FINAL, true, s);
         cur ^= 1;
@@ -445,12 +641,20 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
 
 namespace pisa {
 
-hipError_t score_bf16(const ScoreArgs& a, int d, bool key_rows, int64_t grid, hipStream_t s);
-hipError_t score_f32(const ScoreArgs& a, int d, bool key_rows, int64_t grid, hipStream_t s);
+hipError_t dense_bf16(const DenseArgs& a, int d, hipStream_t s);
+hipError_t dense_f32(const DenseArgs& a, int d, hipStream_t s);
 
-hipError_t launch_score(const ScoreArgs& a, int dtype, int d, bool key_rows, int64_t grid, hipStream_t s)
+hipError_t launch_dense(const DenseArgs& a, int dtype, int d, hipStream_t s)
 {
-    return dtype == 0 ? score_f32(a, d, key_rows, grid, s) : score_bf16(a, d, key_rows, grid, s);
+    return dtype == 0 ? dense_f32(a, d, s) : dense_bf16(a, d, s);
+}
+
+hipError_t score_bf16(const ScoreArgs& a, int d, int kind, int64_t grid, hipStream_t s);
+hipError_t score_f32(const ScoreArgs& a, int d, int kind, int64_t grid, hipStream_t s);
+
+hipError_t launch_score(const ScoreArgs& a, int dtype, int d, int kind, int64_t grid, hipStream_t s)
+{
+    return dtype == 0 ? score_f32(a, d, kind, grid, s) : score_bf16(a, d, kind, grid, s);
 }
 
 }  // namespace pisa

@@ -15,9 +15,9 @@
 //   in-lane reduction;
 //   sum of 2^(z log2(e) / sqrt(d)) over the candidate's rows, log2, sum over
 //   the G_Q heads (eq 22), scaled by ln 2 -> u[item][slot * g + child].
-// Without max-subtraction when the sum is a normal float (the common case),
-// with it otherwise (per column, so a column's result never depends on which
-// other queries share its wave).
+// The sum is taken without max-subtraction when it is a normal float (the
+// common case) and with it otherwise, per column, so a column's result never
+// depends on which other queries share its wave.
 #pragma once
 
 #include "pisa_device.hpp"
@@ -25,265 +25,550 @@
 
 namespace pisa {
 
-// Rows staged per workgroup and row-class selectors.
-enum { RC2 = 2, RC4 = 4, RC8 = 8, RC16 = 16 };  // rows per candidate: 2, 4, 8, or a multiple of 16
-
-constexpr int kScoreThreads = 256;
 constexpr int kScoreNQT = 2;  // query tiles (of 16 columns) per wave pass
 
 __device__ __forceinline__ int64_t xcd_chunk(int64_t blk, int64_t total)
 {
     // blocks are dealt round-robin over the 8 XCDs: give each XCD one
-    // contiguous range of chunks so the chunks of a cluster share an L2
+    // contiguous range of chunks so the chunks of a window share an L2
     const int64_t per = total >> 3;
     if (blk < (per << 3)) return (blk & 7) * per + (blk >> 3);
     return blk;
 }
 
-// ---------------------------------------------------------------------------
-// Reductions of e = 2^(scaled logit) values held by a lane (4 rows of one
-// column per row tile) into per-candidate sums.
-// ---------------------------------------------------------------------------
-template <int D, typename T, typename TS, int RC>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
+// log2 of sum_i 2^z_i over the N values of z (all finite or -inf), plus the
+// cross-lane partners selected by XMASK (bit 0: lanes ^ 16, bit 1: lanes ^ 32).
+// Fast path without max-subtraction; exact-max path when the plain sum is not
+// a normal positive float. `exists` = the candidate has at least one row.
+template <int N, int XMASK, typename F>
+__device__ __forceinline__ float lse2f(F zf, bool exists)
+{
+    float e[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) e[i] = __builtin_amdgcn_exp2f(zf(i));
+#pragma unroll
+    for (int w = 1; w < N; w <<= 1)  // pairwise tree: independent adds
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w) e[i] += e[i + w];
+    float s = e[0];
+    if constexpr (XMASK & 1) s = add_xor16(s);
+    if constexpr (XMASK & 2) s = add_xor32(s);
+    float l2 = __builtin_amdgcn_logf(s);
+    const bool bad = exists && !(s > 0.f && s < INFINITY);
+    if (__builtin_expect(ballot(bad) != 0, 0)) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < N; ++i) m = fmaxf(m, zf(i));
+        if constexpr (XMASK & 1) m = max_xor16(m);
+        if constexpr (XMASK & 2) m = max_xor32(m);
+        float s2 = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) s2 += __builtin_amdgcn_exp2f(zf(i) - m);
+        }
+        if constexpr (XMASK & 1) s2 = add_xor16(s2);
+        if constexpr (XMASK & 2) s2 = add_xor32(s2);
+        const float l2m = m == -INFINITY ? -INFINITY : m + __builtin_amdgcn_logf(s2);
+        if (bad) l2 = l2m;
+    }
+    return l2;
+}
+
+template <int N, int XMASK>
+__device__ __forceinline__ float lse2(const float* z, bool exists)
+{
+    float e[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) e[i] = __builtin_amdgcn_exp2f(z[i]);
+#pragma unroll
+    for (int w = 1; w < N; w <<= 1)  // pairwise tree: independent adds
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w) e[i] += e[i + w];
+    float s = e[0];
+    if constexpr (XMASK & 1) s = add_xor16(s);
+    if constexpr (XMASK & 2) s = add_xor32(s);
+    float l2 = __builtin_amdgcn_logf(s);
+    const bool bad = exists && !(s > 0.f && s < INFINITY);
+    if (__builtin_expect(ballot(bad) != 0, 0)) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < N; ++i) m = fmaxf(m, z[i]);
+        if constexpr (XMASK & 1) m = max_xor16(m);
+        if constexpr (XMASK & 2) m = max_xor32(m);
+        float s2 = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) s2 += __builtin_amdgcn_exp2f(z[i] - m);
+        }
+        if constexpr (XMASK & 1) s2 = add_xor16(s2);
+        if constexpr (XMASK & 2) s2 = add_xor32(s2);
+        const float l2m = m == -INFINITY ? -INFINITY : m + __builtin_amdgcn_logf(s2);
+        if (bad) l2 = l2m;
+    }
+    return l2;
+}
+
+// RC: rows per candidate (g for summary rows, C for key rows), a compile-time
+// constant in {2, 4, 8, 16, 32, 64}. WAVES: waves per workgroup.
+template <int D, typename T, typename TS, int RC, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(ScoreArgs a)
 {
     constexpr int TA = Src<T>::TERMS;   // query terms
     constexpr int TB = Src<TS>::TERMS;  // row terms
     constexpr int KS = D / 32;
     constexpr int LDW = D + 8;          // LDS row stride (bf16 elements)
+    constexpr int TPC = RC >= 16 ? RC / 16 : 1;
     extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
     bf16* s_rows = reinterpret_cast<bf16*>(s_raw);
+    int* s_ent = reinterpret_cast<int*>(s_raw + (size_t)TB * ((a.g * RC + 15) & ~15) * LDW * 2);
 
     const int64_t total = a.chunk_off[a.n_clusters];
     if ((int64_t)blockIdx.x >= total) return;
-    const int64_t chunk = xcd_chunk(blockIdx.x, total);
-    // cluster: the last cl with chunk_off[cl] <= chunk
-    int64_t lo = 0, hi = a.n_clusters;
-    while (hi - lo > 1) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (a.chunk_off[mid] <= chunk) lo = mid; else hi = mid;
-    }
-    const int64_t cl = lo;
-    const int64_t e0 = a.offsets[cl] + (chunk - a.chunk_off[cl]) * a.qc;
-    const int64_t e1 = min((int64_t)a.offsets[cl + 1], e0 + a.qc);
+    const int64_t chunk = a.xcd ? xcd_chunk(blockIdx.x, total) : (int64_t)blockIdx.x;
+    const int64_t cl = a.chunk_cl[chunk];
+    const int e0 = a.offsets[cl] + (int)(chunk - a.chunk_off[cl]) * a.qc;
+    const int e1 = min(a.offsets[cl + 1], e0 + a.qc);
     const int64_t P = cl % a.M_bins;
-    const int64_t bh = cl / a.M_bins;
+    const int64_t bh = (cl / a.M_bins) % a.BH;
     const int h = (int)(bh % a.H);
     const int b = (int)(bh / a.H);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4;
     const int G = a.G, GT = a.G * TA, QT = 16 / GT;
-    const int g = a.g, RCr = a.rc;  // children per candidate (runtime)
-    const int nrows = g * RCr;      // rows of P's grandchildren
-    const int nrows_pad = (nrows + 15) & ~15;  // staged rows (whole MFMA row tiles; padding is zero)
+    const int g = a.g;
+    const int nrows = g * RC;                       // rows of P's grandchildren
+    const int nrows_pad = (nrows + 15) & ~15;       // staged rows (whole MFMA row tiles; padding is zero)
     const int64_t row0 = P * (int64_t)nrows;
-
-    // Stage P's grandchildren rows (bf16 hi plane, and a lo plane for fp32 rows).
-    const TS* rb = reinterpret_cast<const TS*>(a.rows) + (int64_t)b * a.rows_b_stride + (int64_t)h * a.rows_h_stride;
-    for (int i = threadIdx.x; i < nrows_pad * (D / 8); i += kScoreThreads) {
-        const int r = i / (D / 8), c8 = i % (D / 8);
-        const bool ok = r < nrows && row0 + r < a.rows_limit;
-        bf16x8 vh, vl;
-        Src<TS>::load(rb + (ok ? (row0 + r) : 0) * a.row_stride + 8 * c8, ok, vh, vl);
-        *reinterpret_cast<bf16x8*>(s_rows + r * LDW + 8 * c8) = vh;
-        if constexpr (TB == 2) *reinterpret_cast<bf16x8*>(s_rows + (nrows_pad + r) * LDW + 8 * c8) = vl;
-    }
-    __syncthreads();
+    const int64_t rem = a.rows_limit - row0;        // rows of P that exist
+    const int lim_rows = rem < nrows ? (int)rem : nrows;
 
     const float scale = kLog2e * rsqrtf((float)D);
     const int col = lane & 15;
     const int qi = col / GT, term = (col % GT) / G, head = col % G;
+    const bool writer_col = lg == 0 && head == 0 && term == 0;
     const int ucols = a.K_top * g;
-    const int64_t nent = e1 - e0;
-    const int ntiles = (int)((nent + QT - 1) / QT);
-    const int nrt = nrows_pad / 16;  // row tiles
+    const int ntiles = (e1 - e0 + QT - 1) / QT;
+    const T* Qb = reinterpret_cast<const T*>(a.Q) + (int64_t)b * a.N * a.H_q * D + (h * G + head) * D + 8 * lg;
+    const uint32_t qrow = (uint32_t)(a.H_q * D);
+    float* ub = a.u + bh * a.N * ucols;
 
-    for (int tp = wave * kScoreNQT; tp < ntiles; tp += 4 * kScoreNQT) {
-        // B operands: queries of kScoreNQT tiles
+    // one pass = kScoreNQT query tiles of this wave; loaded one pass ahead of its use
+    struct QPass {
         bf16x8 qb[kScoreNQT][KS];
-        int ent[kScoreNQT];
         bool has[kScoreNQT];
+        float* up[kScoreNQT];
+    };
+    auto load_pass = [&](int tp, QPass& Pq) {
+        auto& qb = Pq.qb;
+        auto& has = Pq.has;
+        auto& up = Pq.up;
+        // B operands: queries of kScoreNQT tiles. Lanes past the chunk's end
+        // load the last entry's query (valid memory) and never write.
 #pragma unroll
         for (int qt = 0; qt < kScoreNQT; ++qt) {
-            const int64_t e = e0 + (int64_t)(tp + qt) * QT + qi;
-            has[qt] = (tp + qt) < ntiles && qi < QT && e < e1;
-            ent[qt] = has[qt] ? a.entries[e] : 0;
-            const int64_t tq = ent[qt] >> 6;
-            const T* qp = reinterpret_cast<const T*>(a.Q) +
-                          (((int64_t)b * a.N + tq) * a.H_q + (int64_t)h * G + head) * D + 8 * lg;
+            const int e = e0 + (tp + qt) * QT + qi;
+            has[qt] = e < e1;
+            const int ent = s_ent[(has[qt] ? e : e1 - 1) - e0];
+            const uint32_t tq = (uint32_t)ent >> 6;
+            const T* qp = Qb + (uint64_t)tq * qrow;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 bf16x8 vh, vl;
-                Src<T>::load(qp + 32 * s, has[qt], vh, vl);
+                Src<T>::load(qp + 32 * s, true, vh, vl);
                 qb[qt][s] = term == 0 ? vh : vl;
             }
+            up[qt] = ub + (uint64_t)tq * (uint32_t)ucols + (ent & 63) * g;
         }
 
-        if constexpr (RC == RC16) {
-            // one candidate (RCr / 16 row tiles) at a time
-            const int tpc = RCr / 16;
+    };
+    auto compute = [&](QPass& Pq) {
+        auto& qb = Pq.qb;
+        auto& has = Pq.has;
+        auto& up = Pq.up;
+        if constexpr (RC >= 16) {
+            // one candidate (TPC row tiles) at a time; lane holds 4 rows per tile of its column
             for (int j = 0; j < g; ++j) {
-                if (row0 + (int64_t)j * RCr >= a.rows_limit) break;  // P's remaining children do not exist
-                f32x4 acc[4][kScoreNQT];
+                const int lim = lim_rows - j * RC;  // rows of candidate j that exist
+                if (lim <= 0) break;
+                f32x4 acc[TPC][kScoreNQT];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
+                for (int rt = 0; rt < TPC; ++rt)
 #pragma unroll
                     for (int qt = 0; qt < kScoreNQT; ++qt) acc[rt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    if (rt < tpc) {
-                        const int r = (j * tpc + rt) * 16 + (lane & 15);
+                for (int rt = 0; rt < TPC; ++rt) {
+                    const int r = (j * TPC + rt) * 16 + (lane & 15);
 #pragma unroll
-                        for (int s = 0; s < KS; ++s) {
-                            const bf16x8 ah = *reinterpret_cast<const bf16x8*>(s_rows + r * LDW + 32 * s + 8 * lg);
+                    for (int s = 0; s < KS; ++s) {
+                        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(s_rows + r * LDW + 32 * s + 8 * lg);
 #pragma unroll
-                            for (int qt = 0; qt < kScoreNQT; ++qt) acc[rt][qt] = mfma(ah, qb[qt][s], acc[rt][qt]);
-                            if constexpr (TB == 2) {
-                                const bf16x8 al =
-                                    *reinterpret_cast<const bf16x8*>(s_rows + (nrows_pad + r) * LDW + 32 * s + 8 * lg);
+                        for (int qt = 0; qt < kScoreNQT; ++qt) acc[rt][qt] = mfma(ah, qb[qt][s], acc[rt][qt]);
+                        if constexpr (TB == 2) {
+                            const bf16x8 al =
+                                *reinterpret_cast<const bf16x8*>(s_rows + (nrows_pad + r) * LDW + 32 * s + 8 * lg);
 #pragma unroll
-                                for (int qt = 0; qt < kScoreNQT; ++qt) acc[rt][qt] = mfma(al, qb[qt][s], acc[rt][qt]);
-                            }
+                            for (int qt = 0; qt < kScoreNQT; ++qt) acc[rt][qt] = mfma(al, qb[qt][s], acc[rt][qt]);
                         }
                     }
                 }
 #pragma unroll
                 for (int qt = 0; qt < kScoreNQT; ++qt) {
-                    // logits of this lane's rows; fp32 queries: add the low-term column
-                    float z[4][4];
+                    if constexpr (TA == 2) {  // add the low query term of the same head
 #pragma unroll
-                    for (int rt = 0; rt < 4; ++rt)
+                        for (int rt = 0; rt < TPC; ++rt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float v = acc[rt][qt][i];
-                            if constexpr (TA == 2) v += shfl_xor(v, G);
-                            const int64_t row = row0 + (int64_t)(j * tpc + rt) * 16 + 4 * lg + i;
-                            z[rt][i] = (rt < tpc && row < a.rows_limit) ? v * scale : -INFINITY;
-                        }
-                    float s = 0.f;
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) s += __builtin_amdgcn_exp2f(z[rt][i]);
-                    s += shfl_xor(s, 16);
-                    s += shfl_xor(s, 32);
-                    float l2 = __builtin_amdgcn_logf(s);
-                    const bool bad = !(s > 0.f && s < INFINITY);
-                    if (__builtin_expect(ballot(bad) != 0, 0)) {
-                        float m = -INFINITY;
-#pragma unroll
-                        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) m = fmaxf(m, z[rt][i]);
-                        m = fmaxf(m, shfl_xor(m, 16));
-                        m = fmaxf(m, shfl_xor(m, 32));
-                        float s2 = 0.f;
-                        if (m != -INFINITY) {
-#pragma unroll
-                            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) s2 += __builtin_amdgcn_exp2f(z[rt][i] - m);
-                        }
-                        s2 += shfl_xor(s2, 16);
-                        s2 += shfl_xor(s2, 32);
-                        const float l2m = m == -INFINITY ? -INFINITY : m + __builtin_amdgcn_logf(s2);
-                        if (bad) l2 = l2m;
+                            for (int i = 0; i < 4; ++i) acc[rt][qt][i] += shfl_xor(acc[rt][qt][i], G);
                     }
-                    // sum over the heads of the entry (adjacent columns)
-                    for (int o = 1; o < G; o <<= 1) l2 += shfl_xor(l2, o);
-                    // writer: first lane group, head 0, term 0 of each entry
-                    if (has[qt] && lg == 0 && head == 0 && term == 0) {
-                        const int64_t tq = ent[qt] >> 6;
-                        const int slot = ent[qt] & 63;
-                        a.u[((int64_t)bh * a.N + tq) * ucols + slot * g + j] = l2 * kLn2;
-                    }
+                    const bool tail = lim < RC;  // the tail block of the sequence: rows past its end drop out
+                    auto zf = [&](int x) {
+                        const int rt = x >> 2, i = x & 3;
+                        const float zz = acc[rt][qt][i] * scale;
+                        return (tail && rt * 16 + 4 * lg + i >= lim) ? -INFINITY : zz;
+                    };
+                    float l2 = lse2f<TPC * 4, 3>(zf, true);
+                    l2 = sum_adjacent(l2, G);  // heads are adjacent columns
+                    if (has[qt] && writer_col) up[qt][j] = l2 * kLn2;
                 }
             }
         } else {
-            // all nrows (<= 64) rows; candidate of row r is r / RC
+            // all rows of P (g * RC <= 64: at most 4 row tiles); candidate of row r is r / RC
+            constexpr int CPL = RC < 4 ? 4 / RC : 1;  // candidates per lane and row tile
+            constexpr int RPL = 4 / CPL;               // rows per candidate held by one lane
+            const int nrt = nrows_pad / 16;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                if (rt < nrt) {
-                    f32x4 acc[kScoreNQT];
+                if (rt >= nrt) break;
+                f32x4 acc[kScoreNQT];
 #pragma unroll
-                    for (int qt = 0; qt < kScoreNQT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const int r = rt * 16 + (lane & 15);
+                for (int qt = 0; qt < kScoreNQT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int r = rt * 16 + (lane & 15);
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) {
-                        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(s_rows + r * LDW + 32 * s + 8 * lg);
+                for (int s = 0; s < KS; ++s) {
+                    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(s_rows + r * LDW + 32 * s + 8 * lg);
 #pragma unroll
-                        for (int qt = 0; qt < kScoreNQT; ++qt) acc[qt] = mfma(ah, qb[qt][s], acc[qt]);
-                        if constexpr (TB == 2) {
-                            const bf16x8 al =
-                                *reinterpret_cast<const bf16x8*>(s_rows + (nrows_pad + r) * LDW + 32 * s + 8 * lg);
+                    for (int qt = 0; qt < kScoreNQT; ++qt) acc[qt] = mfma(ah, qb[qt][s], acc[qt]);
+                    if constexpr (TB == 2) {
+                        const bf16x8 al =
+                            *reinterpret_cast<const bf16x8*>(s_rows + (nrows_pad + r) * LDW + 32 * s + 8 * lg);
 #pragma unroll
-                            for (int qt = 0; qt < kScoreNQT; ++qt) acc[qt] = mfma(al, qb[qt][s], acc[qt]);
-                        }
+                        for (int qt = 0; qt < kScoreNQT; ++qt) acc[qt] = mfma(al, qb[qt][s], acc[qt]);
+                    }
+                }
+#pragma unroll
+                for (int qt = 0; qt < kScoreNQT; ++qt) {
+                    float z[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = acc[qt][i];
+                        if constexpr (TA == 2) v += shfl_xor(v, G);
+                        z[i] = v * scale;
+                    }
+                    if (lim_rows < nrows_pad) {  // padding rows, or a tail node with missing children
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (rt * 16 + 4 * lg + i >= lim_rows) z[i] = -INFINITY;
                     }
 #pragma unroll
-                    for (int qt = 0; qt < kScoreNQT; ++qt) {
-                        float z[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float v = acc[qt][i];
-                            if constexpr (TA == 2) v += shfl_xor(v, G);
-                            const int rr = rt * 16 + 4 * lg + i;
-                            z[i] = (rr < nrows && row0 + rr < a.rows_limit) ? v * scale : -INFINITY;
-                        }
-                        // candidate sums: RC rows each
-                        constexpr int CPL = 4 / (RC < 4 ? RC : 4);  // candidates per lane (RC = 2 -> 2)
-                        float s[CPL], m[CPL];
-#pragma unroll
-                        for (int k = 0; k < CPL; ++k) {
-                            s[k] = 0.f;
-                            m[k] = -INFINITY;
-#pragma unroll
-                            for (int i = 0; i < 4 / CPL; ++i) {
-                                s[k] += __builtin_amdgcn_exp2f(z[k * (4 / CPL) + i]);
-                                m[k] = fmaxf(m[k], z[k * (4 / CPL) + i]);
-                            }
-                            if constexpr (RC == RC8) {
-                                s[k] += shfl_xor(s[k], 16);
-                                m[k] = fmaxf(m[k], shfl_xor(m[k], 16));
-                            }
-                        }
-                        float l2[CPL];
-                        bool badk[CPL];
-                        bool badl = false;
-#pragma unroll
-                        for (int k = 0; k < CPL; ++k) {
-                            // a candidate part with no existing row is never written; it is not a bad sum
-                            const int rfirst = rt * 16 + 4 * lg + k * (4 / CPL);
-                            const bool exists = rfirst < nrows && row0 + rfirst < a.rows_limit;
-                            l2[k] = __builtin_amdgcn_logf(s[k]);
-                            badk[k] = exists && !(s[k] > 0.f && s[k] < INFINITY);
-                            badl = badl || badk[k];
-                        }
-                        if (__builtin_expect(ballot(badl) != 0, 0)) {
-#pragma unroll
-                            for (int k = 0; k < CPL; ++k) {
-                                float s2 = 0.f;
-                                if (m[k] != -INFINITY)
-#pragma unroll
-                                    for (int i = 0; i < 4 / CPL; ++i)
-                                        s2 += __builtin_amdgcn_exp2f(z[k * (4 / CPL) + i] - m[k]);
-                                if constexpr (RC == RC8) s2 += shfl_xor(s2, 16);
-                                const float l2m = m[k] == -INFINITY ? -INFINITY : m[k] + __builtin_amdgcn_logf(s2);
-                                if (badk[k]) l2[k] = l2m;
-                            }
-                        }
-#pragma unroll
-                        for (int k = 0; k < CPL; ++k) {
-                            for (int o = 1; o < G; o <<= 1) l2[k] += shfl_xor(l2[k], o);
-                            const int rfirst = rt * 16 + 4 * lg + k * (4 / CPL);  // first row of this candidate part
-                            const int j = rfirst / RC;                            // candidate (child of P)
-                            const bool owner = RC == RC8 ? (lg & 1) == 0 : true;
-                            if (has[qt] && owner && head == 0 && term == 0 && j < g && rfirst < nrows) {
-                                const int64_t tq = ent[qt] >> 6;
-                                const int slot = ent[qt] & 63;
-                                a.u[((int64_t)bh * a.N + tq) * ucols + slot * g + j] = l2[k] * kLn2;
-                            }
-                        }
+                    for (int k = 0; k < CPL; ++k) {
+                        const int rfirst = rt * 16 + 4 * lg + k * RPL;  // first row of this candidate part
+                        const bool exists = rfirst < lim_rows;
+                        float l2 = lse2<RPL, RC == 8 ? 1 : 0>(z + k * RPL, exists);
+                        l2 = sum_adjacent(l2, G);
+                        const int j = rfirst / RC;  // candidate (child of P)
+                        const bool owner = RC == 8 ? (lg & 1) == 0 : true;
+                        if (has[qt] && owner && head == 0 && term == 0 && exists) up[qt][j] = l2 * kLn2;
                     }
+                }
+            }
+        }
+    };
+    QPass A, B;
+    const int stride = WAVES * kScoreNQT;
+    int tp = wave * kScoreNQT;
+
+    // Stage P's grandchildren rows (bf16 hi plane, and a lo plane for fp32 rows).
+    const TS* rb = reinterpret_cast<const TS*>(a.rows) + (int64_t)b * a.rows_b_stride + (int64_t)h * a.rows_h_stride +
+                   row0 * a.row_stride;
+    for (int i = threadIdx.x; i < nrows_pad * (D / 8); i += 64 * WAVES) {
+        const int r = i / (D / 8), c8 = i % (D / 8);
+        const bool ok = r < lim_rows;
+        bf16x8 vh, vl;
+        Src<TS>::load(rb + (ok ? r : 0) * a.row_stride + 8 * c8, ok, vh, vl);
+        *reinterpret_cast<bf16x8*>(s_rows + r * LDW + 8 * c8) = vh;
+        if constexpr (TB == 2) *reinterpret_cast<bf16x8*>(s_rows + (nrows_pad + r) * LDW + 8 * c8) = vl;
+    }
+    // the chunk's entries (<= qc) next to the rows
+    for (int i = threadIdx.x; i < e1 - e0; i += 64 * WAVES) s_ent[i] = a.entries[e0 + i];
+    __syncthreads();
+
+    if (tp < ntiles) {
+        load_pass(tp, A);
+        while (true) {
+            if (tp + stride < ntiles) load_pass(tp + stride, B);
+            compute(A);
+            tp += stride;
+            if (tp >= ntiles) break;
+            if (tp + stride < ntiles) load_pass(tp + stride, A);
+            compute(B);
+            tp += stride;
+            if (tp >= ntiles) break;
+        }
+    }
+}
+
+// Upper levels with g * g <= 16 grandchildren per node (one MFMA row tile):
+// one wave per chunk of kRegChunk entries, no LDS and no workgroup barrier.
+// The wave loads P's rows (fp32 summaries, as two bf16 terms) straight into
+// its A operand registers; RC = g rows per candidate.
+template <int D, typename T, int RC>
+__global__ __launch_bounds__(64 * kRegWaves) void score_reg_kernel(ScoreArgs a)
+{
+    constexpr int TA = Src<T>::TERMS;
+    constexpr int KS = D / 32;
+    constexpr int CPL = RC < 4 ? 4 / RC : 1;  // candidates per lane
+    constexpr int RPL = 4 / CPL;               // rows per candidate held by one lane
+    const int64_t total = a.chunk_off[a.n_clusters];
+    const int64_t nblk = (total + kRegWaves - 1) / kRegWaves;
+    if ((int64_t)blockIdx.x >= nblk) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4;
+    const int64_t lblk = a.xcd ? xcd_chunk(blockIdx.x, nblk) : (int64_t)blockIdx.x;
+    const int64_t chunk = lblk * kRegWaves + wave;
+    if (chunk >= total) return;  // the whole wave leaves; no barrier follows
+    const int64_t cl = a.chunk_cl[chunk];
+    const int e0 = a.offsets[cl] + (int)(chunk - a.chunk_off[cl]) * a.qc;
+    const int e1 = min(a.offsets[cl + 1], e0 + a.qc);
+    const int64_t P = cl % a.M_bins;
+    const int64_t bh = (cl / a.M_bins) % a.BH;
+    const int h = (int)(bh % a.H);
+    const int b = (int)(bh / a.H);
+    const int G = a.G, GT = a.G * TA, QT = 16 / GT;
+    const int g = a.g;
+    const int nrows = g * RC;  // <= 16
+    const int64_t row0 = P * (int64_t)nrows;
+    const int64_t rem = a.rows_limit - row0;
+    const int lim_rows = rem < nrows ? (int)rem : nrows;
+
+    // A operand: row (lane & 15) of P's rows, k-chunk 8 * lg + 32 * s
+    bf16x8 ah[KS], al[KS];
+    {
+        const int r = lane & 15;
+        const bool ok = r < lim_rows;
+        const float* rp = reinterpret_cast<const float*>(a.rows) + (int64_t)b * a.rows_b_stride +
+                          (int64_t)h * a.rows_h_stride + (row0 + (ok ? r : 0)) * a.row_stride + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) Src<float>::load(rp + 32 * s, ok, ah[s], al[s]);
+    }
+
+    const float scale = kLog2e * rsqrtf((float)D);
+    const int col = lane & 15;
+    const int qi = col / GT, term = (col % GT) / G, head = col % G;
+    const int ucols = a.K_top * g;
+    const int ntiles = (e1 - e0 + QT - 1) / QT;
+    const T* Qb = reinterpret_cast<const T*>(a.Q) + (int64_t)b * a.N * a.H_q * D + (h * G + head) * D + 8 * lg;
+    const uint32_t qrow = (uint32_t)(a.H_q * D);
+    float* ub = a.u + bh * a.N * ucols;
+    // the chunk's entries (<= 64), one per lane, fetched once; passes take theirs by shuffle
+    const int ent_lane = a.entries[e0 + (lane < e1 - e0 ? lane : e1 - e0 - 1)];
+
+    struct QPass {
+        bf16x8 qb[kScoreNQT][KS];
+        bool has[kScoreNQT];
+        float* up[kScoreNQT];
+    };
+    auto load_pass = [&](int tp, QPass& Pq) {
+        auto& qb = Pq.qb;
+        auto& has = Pq.has;
+        auto& up = Pq.up;
+#pragma unroll
+        for (int qt = 0; qt < kScoreNQT; ++qt) {
+            const int e = e0 + (tp + qt) * QT + qi;
+            has[qt] = e < e1;
+            const int ent = shfl(ent_lane, has[qt] ? e - e0 : e1 - 1 - e0);
+            const uint32_t tq = (uint32_t)ent >> 6;
+            const T* qp = Qb + (uint64_t)tq * qrow;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                bf16x8 vh, vl;
+                Src<T>::load(qp + 32 * s, true, vh, vl);
+                qb[qt][s] = term == 0 ? vh : vl;
+            }
+            up[qt] = ub + (uint64_t)tq * (uint32_t)ucols + (ent & 63) * g;
+        }
+    };
+    auto compute = [&](QPass& Pq) {
+        auto& qb = Pq.qb;
+        auto& has = Pq.has;
+        auto& up = Pq.up;
+        f32x4 acc[kScoreNQT];
+#pragma unroll
+        for (int qt = 0; qt < kScoreNQT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int qt = 0; qt < kScoreNQT; ++qt) {
+                acc[qt] = mfma(ah[s], qb[qt][s], acc[qt]);
+                acc[qt] = mfma(al[s], qb[qt][s], acc[qt]);
+            }
+#pragma unroll
+        for (int qt = 0; qt < kScoreNQT; ++qt) {
+            float z[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = acc[qt][i];
+                if constexpr (TA == 2) v += shfl_xor(v, G);
+                z[i] = v * scale;
+            }
+            if (lim_rows < 16) {  // padding rows, or a tail node with missing children
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * lg + i >= lim_rows) z[i] = -INFINITY;
+            }
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                const int rfirst = 4 * lg + k * RPL;
+                const bool exists = rfirst < lim_rows;
+                float l2 = lse2<RPL, 0>(z + k * RPL, exists);
+                l2 = sum_adjacent(l2, G);
+                if (has[qt] && head == 0 && term == 0 && exists) up[qt][rfirst / RC] = l2 * kLn2;
+            }
+        }
+    };
+    // passes of kScoreNQT tiles, each loaded one pass ahead of its use
+    QPass A, B;
+    int tp = 0;
+    load_pass(tp, A);
+    while (true) {
+        if (tp + kScoreNQT < ntiles) load_pass(tp + kScoreNQT, B);
+        compute(A);
+        tp += kScoreNQT;
+        if (tp >= ntiles) break;
+        if (tp + kScoreNQT < ntiles) load_pass(tp + kScoreNQT, A);
+        compute(B);
+        tp += kScoreNQT;
+        if (tp >= ntiles) break;
+    }
+}
+
+// Dense scoring of one upper level (g = GB in {2, 4}). Workgroup = 4 waves x
+// up to 4 column tiles of (query, head) columns = QW consecutive queries of one
+// (sequence, KV head). Rows (level l-1 summaries of the eligible level-(l+1)
+// nodes) stream through LDS in batches of 4 row tiles as two bf16 terms; a row
+// tile holds 16 / g^2 parents whose g children are the candidates. A per-query
+// table maps each parent to its slot in the query's kept list (0xFF = not
+// kept); only kept parents' candidates are written to u.
+constexpr int kDenseBatch = 4;
+constexpr int kDenseQW = 64;  // queries per workgroup (at most)
+
+template <int D, typename T, int GB>
+__global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
+{
+    constexpr int TA = Src<T>::TERMS;
+    constexpr int KS = D / 32;
+    constexpr int LDW = D + 8;
+    constexpr int RP = GB * GB;  // rows per parent: 4 or 16
+    constexpr int CPL = 4 / GB;  // candidates per lane: 2 (g = 2) or 1 (g = 4)
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
+    bf16* s_rows = reinterpret_cast<bf16*>(s_raw);  // [2][kDenseBatch * 16][LDW]
+    uint8_t* s_slot = s_raw + 2 * kDenseBatch * 16 * LDW * 2;
+
+    const int G = a.G, GT = G * TA, QT = 16 / GT;
+    const int nct = GT < 4 ? GT : 4;  // column tiles per wave
+    const int QW = 4 * nct * QT;
+    const int K = a.K_top;
+    const int64_t bh = blockIdx.y;
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const int64_t t0 = (int64_t)blockIdx.x * QW;
+    if (t0 >= a.N) return;
+    const int64_t tl = (t0 + QW < a.N ? t0 + QW : a.N) - 1;
+    const int64_t pm = a.causal ? tl >> a.par_span_log2 : a.M_par - 1;  // last eligible parent
+    const int npar = (int)((pm < a.M_par - 1 ? pm : a.M_par - 1) + 1);  // eligible parents of the tile
+
+    for (int k = threadIdx.x; k < QW * npar; k += 256) s_slot[k] = 0xFF;
+    __syncthreads();
+    for (int k = threadIdx.x; k < QW * K; k += 256) {
+        const int q = k / K, sl = k % K;
+        const int64_t t = t0 + q;
+        if (t < a.N) {
+            const int P = a.kept[(bh * a.N + t) * K + sl];
+            if (P >= 0 && P < npar) s_slot[q * npar + P] = (uint8_t)sl;
+        }
+    }
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4;
+    const int col = lane & 15;
+    const int qi = col / GT, term = (col % GT) / G, head = col % G;
+    const float scale = kLog2e * rsqrtf((float)D);
+    const int ucols = K * GB;
+
+    bf16x8 qb[4][KS];
+    int qloc[4];
+    bool qok[4];
+    const T* Qb = reinterpret_cast<const T*>(a.Q) + (int64_t)b * a.N * a.H_q * D + (h * G + head) * D + 8 * lg;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        qloc[ct] = (wave * nct + ct) * QT + qi;
+        const int64_t t = t0 + qloc[ct];
+        qok[ct] = ct < nct && t < a.N;
+        const T* qp = Qb + (uint64_t)(qok[ct] ? t : t0) * (uint32_t)(a.H_q * D);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 vh, vl;
+            Src<T>::load(qp + 32 * s, true, vh, vl);
+            qb[ct][s] = term == 0 ? vh : vl;
+        }
+    }
+
+    const int nrows = npar * RP;
+    const int nrt = (nrows + 15) / 16;
+    const float* rb = a.rows + (int64_t)b * a.rows_b_stride + (int64_t)h * a.rows_h_stride;
+    for (int kb = 0; kb < nrt; kb += kDenseBatch) {
+        __syncthreads();  // the previous batch is consumed (first pass: the slot table is written)
+        for (int i = threadIdx.x; i < kDenseBatch * 16 * (D / 8); i += 256) {
+            const int r = i / (D / 8), c8 = i % (D / 8);
+            const int64_t row = (int64_t)kb * 16 + r;
+            const bool ok = row < nrows && row < a.rows_limit;
+            bf16x8 vh, vl;
+            Src<float>::load(rb + (ok ? row : 0) * D + 8 * c8, ok, vh, vl);
+            *reinterpret_cast<bf16x8*>(s_rows + r * LDW + 8 * c8) = vh;
+            *reinterpret_cast<bf16x8*>(s_rows + (kDenseBatch * 16 + r) * LDW + 8 * c8) = vl;
+        }
+        __syncthreads();
+        const int kend = kb + kDenseBatch < nrt ? kb + kDenseBatch : nrt;
+        for (int k = kb; k < kend; ++k) {
+            const int rl = (k - kb) * 16 + (lane & 15);
+            bf16x8 ah[KS], al[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                ah[s] = *reinterpret_cast<const bf16x8*>(s_rows + rl * LDW + 32 * s + 8 * lg);
+                al[s] = *reinterpret_cast<const bf16x8*>(s_rows + (kDenseBatch * 16 + rl) * LDW + 32 * s + 8 * lg);
+            }
+            const int rfirst = k * 16 + 4 * lg;  // this lane's first row
+            const int P = rfirst / RP;           // its parent (all four rows share it)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                if (ct >= nct) break;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    acc = mfma(ah[s], qb[ct][s], acc);
+                    acc = mfma(al[s], qb[ct][s], acc);
+                }
+                float z[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = acc[i];
+                    if constexpr (TA == 2) v += shfl_xor(v, G);
+                    z[i] = (rfirst + i < nrows && rfirst + i < a.rows_limit) ? v * scale : -INFINITY;
+                }
+                const int slot = P < npar ? s_slot[qloc[ct] * npar + P] : 0xFF;
+#pragma unroll
+                for (int kk = 0; kk < CPL; ++kk) {
+                    const int r0 = rfirst + kk * GB;  // first row of the candidate
+                    const bool exists = r0 < nrows && r0 < a.rows_limit;
+                    float l2 = lse2<GB, 0>(z + kk * GB, exists);
+                    l2 = sum_adjacent(l2, G);
+                    const int j = (r0 % RP) / GB;  // candidate = child j of P
+                    if (qok[ct] && head == 0 && term == 0 && exists && slot != 0xFF)
+                        a.u[(bh * a.N + t0 + qloc[ct]) * ucols + slot * GB + j] = l2 * kLn2;
                 }
             }
         }

@@ -60,12 +60,16 @@ __device__ __forceinline__ bf16x8 zero8h()
 
 // Load 8 consecutive elements of a bf16 or fp32 row as bf16 operand terms.
 // TERMS = 1 for bf16 sources (exact), 2 for fp32 sources (hi + lo).
+// The load is issued unconditionally and `ok` = false zeroes the result, so
+// that no branch (and no wait) surrounds the load: p must point at valid
+// memory even when ok is false (callers clamp the row index).
 template <typename T> struct Src;
 template <> struct Src<bf16> {
     static constexpr int TERMS = 1;
     __device__ __forceinline__ static void load(const bf16* p, bool ok, bf16x8& hi, bf16x8& lo)
     {
-        hi = ok ? load8h(p) : zero8h();
+        const bf16x8 v = load8h(p);
+        hi = ok ? v : zero8h();
         lo = zero8h();
     }
 };
@@ -73,12 +77,10 @@ template <> struct Src<float> {
     static constexpr int TERMS = 2;
     __device__ __forceinline__ static void load(const float* p, bool ok, bf16x8& hi, bf16x8& lo)
     {
-        if (ok) {
-            split8(load8f(p), hi, lo);
-        } else {
-            hi = zero8h();
-            lo = zero8h();
-        }
+        f32x8 v = load8f(p);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = ok ? v[k] : 0.f;
+        split8(v, hi, lo);
     }
 };
 
@@ -125,6 +127,47 @@ __device__ __forceinline__ int compact(bool keep, int& a, float& b)
     a = permute_to(dst, a);
     b = permute_to(dst, b);
     return cnt;
+}
+
+// Cross-lane moves without the LDS crossbar: DPP quad permutes (xor 1, xor 2)
+// and gfx950's permlane swaps, which exchange rows of 16 lanes (xor 16) and
+// halves of the wave (xor 32) in one VALU instruction each.
+__device__ __forceinline__ float dpp_xor1(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+// v + v of lane ^ 16, and v + v of lane ^ 32.
+__device__ __forceinline__ float add_xor16(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float v)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+// Sum over aligned groups of G adjacent lanes (G a power of two <= 16).
+__device__ __forceinline__ float sum_adjacent(float v, int G)
+{
+    if (G >= 2) v += dpp_xor1(v);
+    if (G >= 4) v += dpp_xor2(v);
+    for (int o = 4; o < G; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
 }
 
 // Maximum / sum over aligned groups of `width` lanes (width a power of two <= 64).

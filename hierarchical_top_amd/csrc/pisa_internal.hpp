@@ -92,6 +92,13 @@ struct BsaArgs {
     float* score;
 };
 
+// Level-synchronous routing: clusters of level l are keyed by (query window,
+// sequence and KV head, kept node of level l+1). Windows of 2^win_log2 query
+// positions keep the queries a cluster gathers cache-resident: small windows
+// (L2-sized) for the levels above the leaves, whose node data is tiny, and
+// large ones at the leaf level, where each node brings g * C keys.
+inline int cluster_win_log2(int level) { return level == 1 ? 15 : 11; }
+
 // Level-synchronous routing: clustered scoring of one level.
 struct ScoreArgs {
     const void* Q;            // [B][N][H_q][d]
@@ -104,13 +111,43 @@ struct ScoreArgs {
     int64_t rows_limit;       // rows that exist (nodes of level l-1, or tokens)
     int rc;                   // rows per candidate (g, or C at the leaf level)
     int qc;                   // entries per chunk
-    int64_t n_clusters;       // B * H * M_bins
+    int64_t n_clusters;       // windows * B * H * M_bins
     int64_t M_bins;           // nodes of level l+1 (cluster keys)
+    int64_t BH;               // B * H
+    int xcd;                  // 1: give each XCD a contiguous range of chunks
     const int32_t* offsets;   // [n_clusters + 1]
     const int32_t* chunk_off; // [n_clusters + 1]
+    const int32_t* chunk_cl;  // [chunks] cluster of each chunk
     const int32_t* entries;   // (t << 6) | slot
     float* u;                 // [B][H][N][K_top * g]
 };
+
+// Dense scoring of an upper level: every query tile scores the children of
+// every eligible node of level l+1 (the union of its queries' kept nodes is
+// most of them at these sizes), reading each query once per level instead of
+// once per kept node. Used for levels whose nodes number at most kDenseParents
+// and whose rows (level l-1 summaries) number at most kDenseRows, so the dense
+// work stays O(N) per level; g in {2, 4}.
+constexpr int kDenseParents = 16;
+constexpr int64_t kDenseRows = 256;
+
+struct DenseArgs {
+    const void* Q;            // [B][N][H_q][d]
+    int64_t N;
+    int B, H, H_q, G, K_top, g, causal;
+    const float* rows;        // level l-1 summaries of (b, h) at rows + b * rows_b_stride + h * rows_h_stride
+    int64_t rows_b_stride, rows_h_stride;
+    int64_t rows_limit;       // level l-1 nodes that exist
+    int par_span_log2;        // log2 of the tokens spanned by a level-(l+1) node
+    int64_t M_par;            // level l+1 nodes that exist
+    const int32_t* kept;      // [items][K_top] kept nodes of level l+1
+    float* u;                 // [items][K_top * g]
+};
+
+// Upper levels whose nodes have g * g <= 16 grandchildren: one wave per chunk
+// of kRegChunk entries, rows loaded straight into MFMA operand registers.
+constexpr int kRegChunk = 32;
+constexpr int kRegWaves = 4;
 
 // Per-item selection of one level, and counting of the next level's clusters.
 struct SelectArgs {
@@ -122,8 +159,9 @@ struct SelectArgs {
     const float* u;           // [items][K_top * g] scores of the candidates of `level`
     int32_t* kept_out;        // [items][K_top] (level > 1)
     int64_t* flags_out;       // [items] slots of kept_out whose children are scored next
-    int32_t* counts;          // [B * H][M_bins] cluster sizes for the next level (level > 1)
+    int32_t* counts;          // [windows][B * H][M_bins] cluster sizes for the next level (level > 1)
     int64_t M_bins;           // nodes of `level`
+    int win_log2;             // query window of the next level's clusters
     int32_t* idx;             // level 1: [items][K_top]
     float* score;             // level 1: [items][K_top] or null
 };
@@ -139,6 +177,8 @@ struct LevelsArgs {
     int64_t cnt_off[PISA_MAX_LEVELS + 2];
     int32_t* offsets;
     int32_t* chunk_off;
+    int32_t* chunk_cl;        // [max chunks]
+    int32_t* block_sums;      // scan partials: 2 * (max clusters / 1024 + 1)
     int32_t* entries;
     int l_top;                // highest scored level (0: nothing is scored)
 };
@@ -150,7 +190,9 @@ hipError_t launch_two_stage(const RouteArgs& a, const Stage2Args& s2, const Fina
                             const ScatterArgs& sc, int32_t* zero_base, int64_t zero_count, int dtype,
                             int d, hipStream_t s);
 hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s);
-hipError_t launch_score(const ScoreArgs& a, int dtype, int d, bool key_rows, int64_t grid, hipStream_t s);
+hipError_t launch_dense(const DenseArgs& a, int dtype, int d, hipStream_t s);
+// kind: 0 summary rows staged in LDS, 1 key rows (leaf), 2 summary rows in registers
+hipError_t launch_score(const ScoreArgs& a, int dtype, int d, int kind, int64_t grid, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_bsa(const BsaArgs& a, int dtype, int d, hipStream_t s);
 

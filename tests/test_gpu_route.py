@@ -54,7 +54,11 @@ def _gpu_route(w, Q, K, K_top, causal, mode):
     Qd, Kd = Q.cuda(), K.cuda()
     pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
     pyr.build(Kd, w.N)
-    idx, score = pisa.route_prefill(pyr, Qd, Kd, w.N, K_top, causal=causal, mode=mode, with_score=True)
+    # outputs start as a sentinel so that nothing left in reused memory can pass for a result
+    out = torch.full((w.B, w.H_kv, w.N, K_top), -7, dtype=torch.int32, device="cuda")
+    sco = torch.full((w.B, w.H_kv, w.N, K_top), 12345.0, dtype=torch.float32, device="cuda")
+    idx, score = pisa.route_prefill(pyr, Qd, Kd, w.N, K_top, causal=causal, mode=mode, with_score=True, out=out,
+                                    score_out=sco)
     torch.cuda.synchronize()
     return pyr, idx.cpu().numpy(), score.cpu().numpy()
 
