@@ -564,7 +564,9 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         // leaf: 256 entries per workgroup sharing one node's g * C staged keys; upper levels with
         // g * g <= 16 rows per node: 32 entries per wave, rows held in registers
         const bool reg_rows = !leaf && p.g * p.g <= 16;
-        const int qc = reg_rows ? kRegChunk : 256;
+        // leaf keys held in registers: bf16, g in {2, 4}, 16 / G_Q query columns per tile
+        const bool reg_keys = leaf && dtype == 1 && (p.g == 2 || p.g == 4) && r.G <= 8;
+        const int qc = reg_rows ? kRegChunk : (reg_keys ? kLeafQC : 256);
         int32_t* counts = a.counts + a.cnt_off[l];
         int32_t* cursor = a.cursor + a.cnt_off[l];
 
@@ -617,7 +619,8 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         int64_t grid = ((int64_t)BH * N * r.K_top + qc - 1) / qc + n_clusters;  // bound on the chunks
         if (reg_rows) grid = (grid + kRegWaves - 1) / kRegWaves;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, false, s);
-        if ((err = launch_score(sc2, dtype, d, leaf ? 1 : (reg_rows ? 2 : 0), grid, s)) != hipSuccess) return err;
+        if ((err = launch_score(sc2, dtype, d, reg_keys ? 3 : (leaf ? 1 : (reg_rows ? 2 : 0)), grid, s)) != hipSuccess)
+            return err;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, true, s);
 
         stage_mark(PISA_STAGE_FINAL, false, s);

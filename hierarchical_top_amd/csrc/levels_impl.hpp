@@ -575,4 +575,175 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
     }
 }
 
+// Leaf level, bf16 keys and queries, g in {2, 4}: keys resident in registers.
+// Workgroup = 4 waves on one chunk (up to kLeafQC entries) of one cluster
+// (retained level-2 node P). Wave w scores candidate leaf j = w % g (the
+// 4 / g waves of a candidate split its query tiles) and holds that leaf's C
+// keys as its MFMA A operand for the whole chunk. The chunk's queries pass
+// through LDS in sub-chunks of kLeafSub entries, double-buffered: the next
+// sub-chunk is fetched with direct global-to-LDS loads (16 bytes per lane)
+// while the current one is scored. Rows of D bf16 are stored with their 16-
+// byte pieces XOR-swizzled by row, so the 16 columns of a B operand read 16
+// distinct bank groups. The g scores of an entry are gathered in LDS and
+// written with one store.
+template <int D>
+__device__ __forceinline__ void leaf_fetch(const bf16* Qb, uint32_t qrow, const int* ents, int nsub, int G,
+                                           bf16* buf, int wave, int lane)
+{
+    constexpr int CH = D / 8;        // 16-byte pieces per row
+    constexpr int RPI = 64 / CH;     // rows per wave instruction
+    const int rows = kLeafSub * G;
+    for (int r0 = wave * RPI; r0 < rows; r0 += 4 * RPI) {
+        const int r = r0 + lane / CH, pos = lane % CH;
+        const int c = pos ^ (r & (CH - 1));  // the piece stored at this position
+        const int el = r / G, hd = r % G;
+        const int ent = ents[el < nsub ? el : nsub - 1];
+        const bf16* src = Qb + (uint64_t)((uint32_t)ent >> 6) * qrow + hd * D + 8 * c;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + r0 * D), 16, 0, 0);
+    }
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(256) void leaf_kernel(ScoreArgs a)
+{
+    constexpr int KS = D / 32;
+    constexpr int TPC = C / 16;
+    constexpr int CH = D / 8;
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
+
+    const int64_t total = a.chunk_off[a.n_clusters];
+    if ((int64_t)blockIdx.x >= total) return;
+    const int64_t chunk = blockIdx.x;
+    const int64_t cl = a.chunk_cl[chunk];
+    const int e0 = a.offsets[cl] + (int)(chunk - a.chunk_off[cl]) * a.qc;
+    const int e1 = min(a.offsets[cl + 1], e0 + a.qc);
+    const int64_t P = cl % a.M_bins;
+    const int64_t bh = (cl / a.M_bins) % a.BH;
+    const int h = (int)(bh % a.H);
+    const int b = (int)(bh / a.H);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4;
+    const int G = a.G, QT = 16 / G;
+    const int g = a.g;
+    const int wpc = 4 / g;  // waves per candidate
+    const int j = wave % g, part = wave / g;
+    const int ucols = a.K_top * g;
+
+    const size_t qbuf = (size_t)kLeafSub * G * D;                                // bf16 per buffer
+    bf16* s_q = reinterpret_cast<bf16*>(s_raw);                                   // [2][kLeafSub * G][D]
+    float* s_u = reinterpret_cast<float*>(s_raw + 2 * qbuf * 2);                   // [2][kLeafSub][4]
+    int* s_ent = reinterpret_cast<int*>(s_u + 2 * kLeafSub * 4);                  // [kLeafQC]
+
+    const bf16* Qb = reinterpret_cast<const bf16*>(a.Q) + (int64_t)b * a.N * a.H_q * D + (int64_t)h * G * D;
+    const uint32_t qrow = (uint32_t)(a.H_q * D);
+    const int nsb = (e1 - e0 + kLeafSub - 1) / kLeafSub;  // sub-chunks
+    // the chunk's entries: the first sub-chunk's straight from memory (its fetch starts at once)
+    for (int i = threadIdx.x; i < e1 - e0; i += 256) s_ent[i] = a.entries[e0 + i];
+    {
+        const int n0 = min(kLeafSub, e1 - e0);
+        // wave-uniform fetch of sub-chunk 0, its entries read from global memory
+        constexpr int RPI = 64 / CH;
+        for (int r0 = wave * RPI; r0 < kLeafSub * G; r0 += 4 * RPI) {
+            const int r = r0 + lane / CH, pos = lane % CH;
+            const int c = pos ^ (r & (CH - 1));
+            const int el = r / G, hd = r % G;
+            const int ent = a.entries[e0 + (el < n0 ? el : n0 - 1)];
+            const bf16* src = Qb + (uint64_t)((uint32_t)ent >> 6) * qrow + hd * D + 8 * c;
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(s_q + r0 * D), 16, 0, 0);
+        }
+    }
+
+    // keys of candidate j (leaf P * g + j): rows (lane & 15) of each row tile, k-chunk 8 * lg + 32 * s
+    const int64_t krow0 = (P * g + j) * (int64_t)C;
+    const int64_t krem = a.rows_limit - krow0;
+    const int lim = krem < C ? (int)krem : C;  // keys of the candidate that exist (<= 0: no candidate)
+    bf16x8 A[TPC][KS];
+    {
+        const bf16* kb = reinterpret_cast<const bf16*>(a.rows) + (int64_t)b * a.rows_b_stride +
+                         (int64_t)h * a.rows_h_stride;
+#pragma unroll
+        for (int rt = 0; rt < TPC; ++rt) {
+            const int r = rt * 16 + (lane & 15);
+            const bool ok = r < lim;
+            const bf16* kp = kb + (ok ? krow0 + r : 0) * a.row_stride + 8 * lg;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 v = load8h(kp + 32 * s);
+                A[rt][s] = ok ? v : zero8h();
+            }
+        }
+    }
+
+    const float scale = kLog2e * rsqrtf((float)D);
+    const int col = lane & 15;
+    const int qi = col / G, head = col % G;
+    float* ub = a.u + bh * a.N * ucols;
+    const int64_t nj = a.rows_limit - P * g * (int64_t)C;  // keys of P that exist
+    const int ncand = (int)((nj + C - 1) / C < g ? (nj + C - 1) / C : g);
+
+    for (int sb = 0; sb < nsb; ++sb) {
+        const int base = sb * kLeafSub;
+        const int nsub = min(kLeafSub, e1 - e0 - base);
+        bf16* cur = s_q + (sb & 1) * qbuf;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's fetches (and everything else) have landed
+        __syncthreads();                // ... and every wave's; the other buffer is free again
+        if (sb + 1 < nsb)
+            leaf_fetch<D>(Qb, qrow, s_ent + base + kLeafSub, min(kLeafSub, e1 - e0 - base - kLeafSub), G,
+                          s_q + ((sb + 1) & 1) * qbuf, wave, lane);
+        // scores of the previous sub-chunk (complete after the barrier): one store per entry
+        if (sb > 0) {
+            const float* su = s_u + ((sb - 1) & 1) * kLeafSub * 4;
+            for (int el = threadIdx.x; el < kLeafSub && base - kLeafSub + el < e1 - e0; el += 256) {
+                const int ent = s_ent[base - kLeafSub + el];
+                float* up = ub + (uint64_t)((uint32_t)ent >> 6) * (uint32_t)ucols + (ent & 63) * g;
+                if (g == 4 && ncand == 4) *reinterpret_cast<f32x4*>(up) = *reinterpret_cast<const f32x4*>(su + el * 4);
+                else for (int q = 0; q < ncand; ++q) up[q] = su[el * 4 + q];
+            }
+        }
+        if (lim > 0) {
+            float* su = s_u + (sb & 1) * kLeafSub * 4;
+            const int ntile = (nsub + QT - 1) / QT;
+            for (int tl = part; tl < ntile; tl += wpc) {
+                const int el = tl * QT + qi;  // entry of this lane's column within the sub-chunk
+                const int r = el * G + head;
+                bf16x8 B[KS];
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    B[s] = *reinterpret_cast<const bf16x8*>(cur + r * D + 8 * ((4 * s + lg) ^ (r & (CH - 1))));
+                f32x4 acc[TPC];
+#pragma unroll
+                for (int rt = 0; rt < TPC; ++rt) {
+                    acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) acc[rt] = mfma(A[rt][s], B[s], acc[rt]);
+                }
+                float l2;
+                if (lim == C) {
+                    l2 = lse2f<TPC * 4, 3>([&](int x) { return acc[x >> 2][x & 3] * scale; }, true);
+                } else {  // the tail block of the sequence: rows past its end drop out
+                    l2 = lse2f<TPC * 4, 3>(
+                        [&](int x) {
+                            const int rt = x >> 2, i = x & 3;
+                            return rt * 16 + 4 * lg + i < lim ? acc[rt][i] * scale : -INFINITY;
+                        },
+                        true);
+                }
+                l2 = sum_adjacent(l2, G);
+                if (lg == 0 && head == 0 && el < nsub) su[el * 4 + j] = l2 * kLn2;
+            }
+        }
+    }
+    // scores of the last sub-chunk
+    __syncthreads();
+    {
+        const int base = (nsb - 1) * kLeafSub;
+        const float* su = s_u + ((nsb - 1) & 1) * kLeafSub * 4;
+        for (int el = threadIdx.x; el < kLeafSub && base + el < e1 - e0; el += 256) {
+            const int ent = s_ent[base + el];
+            float* up = ub + (uint64_t)((uint32_t)ent >> 6) * (uint32_t)ucols + (ent & 63) * g;
+            if (g == 4 && ncand == 4) *reinterpret_cast<f32x4*>(up) = *reinterpret_cast<const f32x4*>(su + el * 4);
+            else for (int q = 0; q < ncand; ++q) up[q] = su[el * 4 + q];
+        }
+    }
+}
+
 }  // namespace pisa

@@ -149,6 +149,11 @@ struct DenseArgs {
 constexpr int kRegChunk = 32;
 constexpr int kRegWaves = 4;
 
+// Leaf level with bf16 keys and g in {2, 4}: chunks of kLeafQC entries whose
+// queries pass through LDS kLeafSub entries at a time.
+constexpr int kLeafQC = 256;
+constexpr int kLeafSub = 16;
+
 // Per-item selection of one level, and counting of the next level's clusters.
 struct SelectArgs {
     int B, H, c_log2, g_log2, K_top, causal;
