@@ -1,6 +1,7 @@
 """Benchmark of PISA pyramid Top-K block selection on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+    python bench.py --traffic FETCH_DIR WRITE_DIR   (no GPU: counters -> profiles/traffic.json)
 
 One step = one pass of the selection path over the 262,144-token workload
 (batch 1, 16 query heads sharing 4 KV heads, d=128, C=64, g=4, K_top=8,
@@ -43,6 +44,9 @@ MODES = {"levels": pisa.LEVELS, "two_stage": pisa.TWO_STAGE, "fused": pisa.FUSED
 STAGES_TWO = ["build", "upper", "cluster", "leaf", "final"]
 STAGES_FUSED = ["build", "route_fused"]
 ARMED = {"build": 1, "route_fused": 1, "leaf": 1, "upper": 8, "cluster": 8, "final": 8}
+# kernel (name fragment in a rocprofv3 trace) of each single-kernel stage
+STAGE_KERNEL = {"leaf": "leaf_kernel", "build": "build_l12_kernel", "route_fused": "route_query_kernel"}
+COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read and 1 GiB written
 
 
 def log(*a):
@@ -153,6 +157,61 @@ def roofline(stage, ms, w, traffic):
     ach = flops / (ms * 1e-3) / 1e12
     return dict(kernel=stage, bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=ach / PEAK_BF16_TFLOPS, traffic=traffic, algorithmic=flops, ms_per_launch=ms)
+
+
+def copy_calibration():
+    """A plain 1 GiB device-to-device copy, so that a counter run over this program
+    also holds the counters of a transfer of known size."""
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+def _counter_rows(d):
+    import csv
+    files = sorted(Path(d).rglob("*counter_collection.csv"))
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (str(f), r["Dispatch_Id"])
+            e = per.setdefault(key, {"name": r["Kernel_Name"], "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def traffic_from_counters(fetch_dir, write_dir, workload="p256k"):
+    """HBM bytes per launch of the stage kernels from two rocprofv3 --pmc runs of
+    `bench.py --quick --no-cpu --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, in
+    KiB per dispatch), each scaled so that the calibration copy reads / writes
+    exactly COPY_BYTES. Writes profiles/traffic.json; returns the records."""
+    fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
+
+    def avg(rows, frag, counter):
+        v = [r["c"][counter] for r in rows if frag in r["name"] and counter in r["c"]]
+        return (float(np.mean(v)) * 1024.0, len(v)) if v else (None, 0)
+
+    f_copy, _ = avg(fetch, "copyBuffer", "FETCH_SIZE")
+    w_copy, _ = avg(write, "copyBuffer", "WRITE_SIZE")
+    if not f_copy or not w_copy:
+        raise SystemExit("the calibration copy is missing from the counter runs")
+    kf, kw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    out_file = ROOT / "profiles" / "traffic.json"
+    recs = json.loads(out_file.read_text()) if out_file.exists() else {}
+    for stage, frag in STAGE_KERNEL.items():
+        fb, nf = avg(fetch, frag, "FETCH_SIZE")
+        wb, nw = avg(write, frag, "WRITE_SIZE")
+        if fb is None or wb is None:
+            continue
+        recs["%s/%s" % (workload, stage)] = dict(
+            kernel=frag, bytes_per_launch=fb * kf + wb * kw, fetch_bytes=fb * kf, write_bytes=wb * kw,
+            dispatches=[nf, nw], scale=dict(fetch=kf, write=kw), source_hash=source_hash())
+    out_file.write_text(json.dumps(recs, indent=1, sort_keys=True) + "\n")
+    return recs
 
 
 def sample_positions(N, C, n):
@@ -281,7 +340,14 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only (no extra workloads)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle routing to time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a 1 GiB device copy (counter calibration for --traffic)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
     args = ap.parse_args()
+    if args.traffic:
+        print(json.dumps(traffic_from_counters(*args.traffic), indent=1, sort_keys=True))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the selection path is built and timed on a single MI355X; "
@@ -320,10 +386,13 @@ def main():
     stages_ms = {s: float(np.mean([sum(a.elapsed_time(b) for a, b in e[s][:f[s]]) for e, f in zip(stage_ev, fired)]))
                  for s in stage_names}
     launches = {s: fired[0][s] for s in stage_names}
-    dom = max((s for s in stage_names), key=lambda s: stages_ms[s])
+    # the dominant kernel: the single-kernel stage with the longest launch
+    dom = max((s for s in stage_names if s in STAGE_KERNEL), key=lambda s: stages_ms[s] / max(1, launches[s]))
     log("ms/step", ms, "stages", stages_ms)
     traffic = load_traffic(dom, w.name)
     roof = roofline(dom, stages_ms[dom], w, traffic)
+    roof["kernel"] = STAGE_KERNEL[dom]
+    roof["launches_per_step"] = launches[dom]
     roof_all = {s: {k: roofline(s, stages_ms[s], w, load_traffic(s, w.name))[k]
                     for k in ("bound", "achieved", "unit", "frac")} for s in stage_names}
 
@@ -348,6 +417,9 @@ def main():
         log("cpu", cpu, parity)
     del P
     torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        copy_calibration()
 
     if not args.quick:
         for name, reps, attn in (("p16k", 10, False), ("p64k", 5, True)):

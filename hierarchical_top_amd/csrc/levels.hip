@@ -561,12 +561,15 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         const int64_t n_win = (N + ((int64_t)1 << wl) - 1) >> wl;
         const int64_t n_clusters = n_win * BH * M_bins;
         const bool leaf = l == 1;
-        // leaf: 256 entries per workgroup sharing one node's g * C staged keys; upper levels with
-        // g * g <= 16 rows per node: 32 entries per wave, rows held in registers
-        const bool reg_rows = !leaf && p.g * p.g <= 16;
-        // leaf keys held in registers: bf16, g in {2, 4}, 16 / G_Q query columns per tile
+        // otherwise: leaf, 256 entries per workgroup sharing one node's g * C staged keys; upper
+        // levels with g * g <= 16 rows per node, 32 entries per wave, rows held in registers.
+        // leaf keys held in registers: bf16, g in {2, 4}, 16 / G_Q query columns per tile; upper
+        // levels of the same shapes: 256 entries per workgroup, queries through LDS, the node's
+        // g * g grandchildren in registers
         const bool reg_keys = leaf && dtype == 1 && (p.g == 2 || p.g == 4) && r.G <= 8;
-        const int qc = reg_rows ? kRegChunk : (reg_keys ? kLeafQC : 256);
+        const bool reg_upper = !leaf && dtype == 1 && (p.g == 2 || p.g == 4) && r.G <= 8;
+        const bool reg_rows = !leaf && !reg_upper && p.g * p.g <= 16;
+        const int qc = reg_rows ? kRegChunk : ((reg_keys || reg_upper) ? kLeafQC : 256);
         int32_t* counts = a.counts + a.cnt_off[l];
         int32_t* cursor = a.cursor + a.cnt_off[l];
 
@@ -619,8 +622,8 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         int64_t grid = ((int64_t)BH * N * r.K_top + qc - 1) / qc + n_clusters;  // bound on the chunks
         if (reg_rows) grid = (grid + kRegWaves - 1) / kRegWaves;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, false, s);
-        if ((err = launch_score(sc2, dtype, d, reg_keys ? 3 : (leaf ? 1 : (reg_rows ? 2 : 0)), grid, s)) != hipSuccess)
-            return err;
+        const int kind = reg_keys ? 3 : (reg_upper ? 4 : (leaf ? 1 : (reg_rows ? 2 : 0)));
+        if ((err = launch_score(sc2, dtype, d, kind, grid, s)) != hipSuccess) return err;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, true, s);
 
         stage_mark(PISA_STAGE_FINAL, false, s);

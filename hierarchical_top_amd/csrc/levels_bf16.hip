@@ -27,15 +27,22 @@ template <int D>
 static hipError_t score_d(const ScoreArgs& a, int kind, int64_t grid, hipStream_t s)
 {
     if (kind == 2) return a.rc == 2 ? score_reg_launch<D, 2>(a, grid, s) : score_reg_launch<D, 4>(a, grid, s);
-    if (kind == 3) {  // leaf level, keys in registers (g in {2, 4})
-        const size_t lds = (size_t)2 * kLeafSub * a.G * D * 2 + 2 * kLeafSub * 4 * 4 + (size_t)kLeafQC * 4;
-        auto k = a.rc == 16 ? leaf_kernel<D, 16> : (a.rc == 32 ? leaf_kernel<D, 32> : leaf_kernel<D, 64>);
+    if (kind == 3 || kind == 4) {  // queries streamed through LDS: leaf (keys) or upper (grandchildren)
+        const size_t lds = stream_lds_bytes(D, kind == 3 ? kLeafNB : kUpperNB);
+        const void* k;
+        if (kind == 3)
+            k = a.rc == 16 ? (const void*)leaf_kernel<D, 16, kLeafNB>
+                           : (a.rc == 32 ? (const void*)leaf_kernel<D, 32, kLeafNB> : (const void*)leaf_kernel<D, 64, kLeafNB>);
+        else
+            k = a.rc == 2 ? (const void*)upper_kernel<D, 2, kUpperNB> : (const void*)upper_kernel<D, 4, kUpperNB>;
         if (lds > 65536) {
-            hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), lds, s, a);
-        return hipGetLastError();
+        ScoreArgs arg = a;
+        void* args[] = {&arg};
+        hipError_t e = hipLaunchKernel(k, dim3((unsigned)grid), dim3(256), args, lds, s);
+        return e != hipSuccess ? e : hipGetLastError();
     }
     if (kind == 1) {  // leaf level: rows per candidate = C
         switch (a.rc) {

@@ -575,40 +575,187 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
     }
 }
 
-// Leaf level, bf16 keys and queries, g in {2, 4}: keys resident in registers.
-// Workgroup = 4 waves on one chunk (up to kLeafQC entries) of one cluster
-// (retained level-2 node P). Wave w scores candidate leaf j = w % g (the
-// 4 / g waves of a candidate split its query tiles) and holds that leaf's C
-// keys as its MFMA A operand for the whole chunk. The chunk's queries pass
-// through LDS in sub-chunks of kLeafSub entries, double-buffered: the next
-// sub-chunk is fetched with direct global-to-LDS loads (16 bytes per lane)
-// while the current one is scored. Rows of D bf16 are stored with their 16-
-// byte pieces XOR-swizzled by row, so the 16 columns of a B operand read 16
-// distinct bank groups. The g scores of an entry are gathered in LDS and
-// written with one store.
-template <int D>
-__device__ __forceinline__ void leaf_fetch(const bf16* Qb, uint32_t qrow, const int* ents, int nsub, int G,
-                                           bf16* buf, int wave, int lane)
+// Streaming of a chunk's query rows through LDS (leaf_kernel, upper_kernel).
+// Sub-chunk k holds LDS rows r = entry * G + head for its kSubRows / G
+// entries; row r's 16-byte pieces are XOR-swizzled by (r mod D / 8), so the 16
+// columns of a B operand read distinct bank groups. Rows are fetched with
+// global_load_lds (lane l writes 16 bytes at the wave-uniform base + 16 * l),
+// each wave issuing exactly NI instructions per sub-chunk, which lets a wave
+// wait for one sub-chunk with an exact vmcnt while later ones are in flight
+// (loads complete in order; the loop issues no other memory instruction that
+// counts there).
+template <int N>
+__device__ __forceinline__ void wait_vm()
 {
-    constexpr int CH = D / 8;        // 16-byte pieces per row
-    constexpr int RPI = 64 / CH;     // rows per wave instruction
-    const int rows = kLeafSub * G;
-    for (int r0 = wave * RPI; r0 < rows; r0 += 4 * RPI) {
-        const int r = r0 + lane / CH, pos = lane % CH;
-        const int c = pos ^ (r & (CH - 1));  // the piece stored at this position
-        const int el = r / G, hd = r % G;
-        const int ent = ents[el < nsub ? el : nsub - 1];
-        const bf16* src = Qb + (uint64_t)((uint32_t)ent >> 6) * qrow + hd * D + 8 * c;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + r0 * D), 16, 0, 0);
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at their maxima
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D>
+struct StreamGeom {
+    static constexpr int CH = D / 8;                    // 16-byte pieces per row
+    static constexpr int RPI = 64 / CH;                 // rows per wave instruction
+    static constexpr int STEP = 4 * RPI;                // rows between a wave's instructions
+    static constexpr int NI = kSubRows / STEP;          // instructions per wave and sub-chunk
+    static_assert(STEP % 16 == 0 && 16 % CH == 0, "instructions repeat head and swizzle per lane");
+};
+
+// This lane's part of every fetch: instruction i writes LDS row
+// wave * RPI + i * STEP + lane / CH, which (G <= 16 dividing STEP) holds
+// entry el0 + i * STEP / G, head hd, and the piece `off` addresses.
+struct StreamLane {
+    int el0;  // entry of instruction 0's row within the sub-chunk
+    int off;  // element offset within the entry's G * D query elements: hd * D + 8 * piece
+};
+template <int D>
+__device__ __forceinline__ StreamLane stream_lane(int wave, int lane, int glog)
+{
+    using S = StreamGeom<D>;
+    const int r = wave * S::RPI + lane / S::CH;
+    const int c = (lane % S::CH) ^ (r & (S::CH - 1));  // the piece stored at this lane's position
+    return StreamLane{r >> glog, (r & ((1 << glog) - 1)) * D + 8 * c};
+}
+
+// Issue this wave's NI fetches of one sub-chunk; ent[i] = entry of instruction i.
+template <int D>
+__device__ __forceinline__ void stream_issue(const bf16* Qb, uint32_t qrow, const int* ent, const StreamLane& sl,
+                                             bf16* buf, int wave)
+{
+    using S = StreamGeom<D>;
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i) {
+        const bf16* src = Qb + (uint64_t)((uint32_t)ent[i] >> 6) * qrow + sl.off;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (wave * S::RPI + i * S::STEP) * D),
+                                         16, 0, 0);
     }
 }
 
-template <int D, int C>
-__global__ __launch_bounds__(256) void leaf_kernel(ScoreArgs a)
+// Fetch one sub-chunk (nvalid = its entries; rows past them repeat its last
+// entry), the entry ids read from ents (LDS) before any fetch issues.
+template <int D>
+__device__ __forceinline__ void stream_fetch(const bf16* Qb, uint32_t qrow, const int* ents, int nvalid,
+                                             const StreamLane& sl, int glog, bf16* buf, int wave)
+{
+    using S = StreamGeom<D>;
+    int ent[S::NI];
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i) {
+        const int el = sl.el0 + ((i * S::STEP) >> glog);
+        ent[i] = ents[el < nvalid ? el : nvalid - 1];
+    }
+    stream_issue<D>(Qb, qrow, ent, sl, buf, wave);
+}
+
+// Start of a chunk: the entry ids of its first NB - 1 sub-chunks and of the
+// whole chunk (for the LDS copy) are loaded from memory together, then
+// stream_prologue_issue starts the fetches; the caller's A operand loads
+// follow them.
+template <int D, int NB>
+struct StreamPrologue {
+    int ent[NB - 1][StreamGeom<D>::NI];
+    int own;  // entry e0 + threadIdx.x (if any), copied to LDS
+};
+template <int D, int NB>
+__device__ __forceinline__ void stream_prologue_load(StreamPrologue<D, NB>& pr, const int* entries, int n, int SE,
+                                                     const StreamLane& sl, int glog)
+{
+    static_assert(kLeafQC <= 256, "one entry per thread");
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k)
+#pragma unroll
+        for (int i = 0; i < StreamGeom<D>::NI; ++i) {
+            const int el = k * SE + sl.el0 + ((i * StreamGeom<D>::STEP) >> glog);
+            const int lim = min(n, (k + 1) * SE) - 1;  // last entry of sub-chunk k (k < nsb)
+            pr.ent[k][i] = entries[max(0, min(el, lim))];
+        }
+    pr.own = entries[min((int)threadIdx.x, n - 1)];
+}
+template <int D, int NB>
+__device__ __forceinline__ void stream_prologue_issue(const StreamPrologue<D, NB>& pr, int* lds_ent,
+                                                      const bf16* Qb, uint32_t qrow, const StreamLane& sl, bf16* ring,
+                                                      int wave)
+{
+    wait_vm<0>();  // the entry ids: nothing else outstanding from here on
+    // branch-free: sub-chunks past the chunk's end refetch its last entry into buffers no
+    // tile reads (the last sub-chunk's wait, vmcnt(0), covers them before the chunk ends)
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k) stream_issue<D>(Qb, qrow, pr.ent[k], sl, ring + k * kSubRows * D, wave);
+    lds_ent[threadIdx.x] = pr.own;  // slots past n hold copies of the last entry
+}
+
+// Wait until this wave's fetch of the current sub-chunk has landed, `later`
+// (wave-uniform, <= NB - 2) sub-chunks having been issued after it.
+template <int D, int NB>
+__device__ __forceinline__ void stream_wait(int later)
+{
+    constexpr int NI = StreamGeom<D>::NI;
+    static_assert(NB >= 2 && NB <= 4, "ring depth");
+    if constexpr (NB >= 4) {
+        if (later >= 2) { wait_vm<2 * NI>(); return; }
+    }
+    if constexpr (NB >= 3) {
+        if (later >= 1) { wait_vm<NI>(); return; }
+    }
+    wait_vm<0>();
+}
+
+// Workgroup barrier after this wave's LDS reads and writes have completed.
+// The streamed fetches are waited for explicitly (stream_wait), and nothing
+// written to global memory is read back by the workgroup, so no vmcnt wait is
+// wanted here (a fence would drain the fetches still in flight: they write
+// LDS). The memory clobber keeps the compiler from moving accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS layout shared by both kernels: [NB][kSubRows][D] bf16 ring, then
+// kLeafQC entries, then kLeafQC x 4 scores.
+struct StreamLds {
+    bf16* q;
+    int* ent;
+    float* u;
+};
+template <int D, int NB>
+__device__ __forceinline__ StreamLds stream_lds(unsigned char* raw)
+{
+    StreamLds L;
+    L.q = reinterpret_cast<bf16*>(raw);
+    L.ent = reinterpret_cast<int*>(raw + (size_t)NB * kSubRows * D * 2);
+    L.u = reinterpret_cast<float*>(L.ent + kLeafQC);
+    return L;
+}
+
+// Scores gathered in LDS, written after the chunk: u[.][t][slot * g + c] for
+// the ncand candidates that exist.
+__device__ __forceinline__ void stream_write_scores(const StreamLds& L, float* ub, int n, int ucols, int g,
+                                                    int ncand)
+{
+    for (int el = threadIdx.x; el < n; el += 256) {
+        const int ent = L.ent[el];
+        float* up = ub + (uint64_t)((uint32_t)ent >> 6) * (uint32_t)ucols + (ent & 63) * g;
+        if (g == 4 && ncand == 4) *reinterpret_cast<f32x4*>(up) = *reinterpret_cast<const f32x4*>(L.u + el * 4);
+        else
+            for (int q = 0; q < ncand; ++q) up[q] = L.u[el * 4 + q];
+    }
+}
+
+// Leaf level, bf16 keys, g in {2, 4}: a workgroup scores a chunk of up to
+// kLeafQC entries of one cluster (window, sequence x KV head, level-2 node P)
+// against P's g leaf candidates. The C keys of candidate j are held in the
+// registers of the waves w with w % g == j (A operand, C / 16 row tiles);
+// the queries stream through the LDS ring (B operand, 16 columns = 16 / G
+// entries x G heads per tile). Per (query column, candidate) the C scores are
+// reduced to log2-sum-exp in registers and across the 4 lane groups, the G
+// heads summed with DPP, and the natural-log score kept in LDS.
+template <int D, int C, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 3 : 4))) void leaf_kernel(ScoreArgs a)
 {
     constexpr int KS = D / 32;
     constexpr int TPC = C / 16;
     constexpr int CH = D / 8;
+    static_assert(16 % CH == 0, "a row tile spans whole swizzle periods");
     extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
 
     const int64_t total = a.chunk_off[a.n_clusters];
@@ -617,40 +764,28 @@ __global__ __launch_bounds__(256) void leaf_kernel(ScoreArgs a)
     const int64_t cl = a.chunk_cl[chunk];
     const int e0 = a.offsets[cl] + (int)(chunk - a.chunk_off[cl]) * a.qc;
     const int e1 = min(a.offsets[cl + 1], e0 + a.qc);
+    const int n = e1 - e0;
     const int64_t P = cl % a.M_bins;
     const int64_t bh = (cl / a.M_bins) % a.BH;
     const int h = (int)(bh % a.H);
     const int b = (int)(bh / a.H);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lg = lane >> 4;
-    const int G = a.G, QT = 16 / G;
+    const int lane = threadIdx.x & 63, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar branches below
+    const int G = a.G, QT = 16 / G, SE = kSubRows / G;  // entries per tile / per sub-chunk
+    const int glog = __builtin_ctz(G);                   // G is a power of two
     const int g = a.g;
     const int wpc = 4 / g;  // waves per candidate
     const int j = wave % g, part = wave / g;
     const int ucols = a.K_top * g;
-
-    const size_t qbuf = (size_t)kLeafSub * G * D;                                // bf16 per buffer
-    bf16* s_q = reinterpret_cast<bf16*>(s_raw);                                   // [2][kLeafSub * G][D]
-    float* s_u = reinterpret_cast<float*>(s_raw + 2 * qbuf * 2);                   // [2][kLeafSub][4]
-    int* s_ent = reinterpret_cast<int*>(s_u + 2 * kLeafSub * 4);                  // [kLeafQC]
+    const StreamLds L = stream_lds<D, NB>(s_raw);
 
     const bf16* Qb = reinterpret_cast<const bf16*>(a.Q) + (int64_t)b * a.N * a.H_q * D + (int64_t)h * G * D;
     const uint32_t qrow = (uint32_t)(a.H_q * D);
-    const int nsb = (e1 - e0 + kLeafSub - 1) / kLeafSub;  // sub-chunks
-    // the chunk's entries: the first sub-chunk's straight from memory (its fetch starts at once)
-    for (int i = threadIdx.x; i < e1 - e0; i += 256) s_ent[i] = a.entries[e0 + i];
-    {
-        const int n0 = min(kLeafSub, e1 - e0);
-        // wave-uniform fetch of sub-chunk 0, its entries read from global memory
-        constexpr int RPI = 64 / CH;
-        for (int r0 = wave * RPI; r0 < kLeafSub * G; r0 += 4 * RPI) {
-            const int r = r0 + lane / CH, pos = lane % CH;
-            const int c = pos ^ (r & (CH - 1));
-            const int el = r / G, hd = r % G;
-            const int ent = a.entries[e0 + (el < n0 ? el : n0 - 1)];
-            const bf16* src = Qb + (uint64_t)((uint32_t)ent >> 6) * qrow + hd * D + 8 * c;
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(s_q + r0 * D), 16, 0, 0);
-        }
-    }
+    const int nsb = (n + SE - 1) / SE;  // sub-chunks
+    StreamPrologue<D, NB> pr;
+    const StreamLane sl = stream_lane<D>(wave, lane, glog);
+    stream_prologue_load<D, NB>(pr, a.entries + e0, n, SE, sl, glog);
+    stream_prologue_issue<D, NB>(pr, L.ent, Qb, qrow, sl, L.q, wave);
 
     // keys of candidate j (leaf P * g + j): rows (lane & 15) of each row tile, k-chunk 8 * lg + 32 * s
     const int64_t krow0 = (P * g + j) * (int64_t)C;
@@ -676,39 +811,32 @@ __global__ __launch_bounds__(256) void leaf_kernel(ScoreArgs a)
     const float scale = kLog2e * rsqrtf((float)D);
     const int col = lane & 15;
     const int qi = col / G, head = col % G;
-    float* ub = a.u + bh * a.N * ucols;
+    // column col of row tile tl is LDS row tl * 16 + col (entry tl * QT + qi, head `head`), so the
+    // swizzled position of its k-chunk 4 * s + lg is fixed per lane: byte offsets hoisted here
+    int boff[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) boff[s] = (col * D + 8 * ((4 * s + lg) ^ (col & (CH - 1)))) * 2;
     const int64_t nj = a.rows_limit - P * g * (int64_t)C;  // keys of P that exist
     const int ncand = (int)((nj + C - 1) / C < g ? (nj + C - 1) / C : g);
 
     for (int sb = 0; sb < nsb; ++sb) {
-        const int base = sb * kLeafSub;
-        const int nsub = min(kLeafSub, e1 - e0 - base);
-        bf16* cur = s_q + (sb & 1) * qbuf;
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's fetches (and everything else) have landed
-        __syncthreads();                // ... and every wave's; the other buffer is free again
-        if (sb + 1 < nsb)
-            leaf_fetch<D>(Qb, qrow, s_ent + base + kLeafSub, min(kLeafSub, e1 - e0 - base - kLeafSub), G,
-                          s_q + ((sb + 1) & 1) * qbuf, wave, lane);
-        // scores of the previous sub-chunk (complete after the barrier): one store per entry
-        if (sb > 0) {
-            const float* su = s_u + ((sb - 1) & 1) * kLeafSub * 4;
-            for (int el = threadIdx.x; el < kLeafSub && base - kLeafSub + el < e1 - e0; el += 256) {
-                const int ent = s_ent[base - kLeafSub + el];
-                float* up = ub + (uint64_t)((uint32_t)ent >> 6) * (uint32_t)ucols + (ent & 63) * g;
-                if (g == 4 && ncand == 4) *reinterpret_cast<f32x4*>(up) = *reinterpret_cast<const f32x4*>(su + el * 4);
-                else for (int q = 0; q < ncand; ++q) up[q] = su[el * 4 + q];
-            }
+        const int base = sb * SE;
+        const int nsub = min(SE, n - base);
+        stream_wait<D, NB>(min(NB - 2, nsb - 1 - sb));
+        lds_barrier();  // every wave's part has landed; the buffer of sub-chunk sb - 1 is free again
+        if (sb + NB - 1 < nsb) {
+            const int nb = sb + NB - 1;
+            stream_fetch<D>(Qb, qrow, L.ent + nb * SE, min(SE, n - nb * SE), sl, glog, L.q + (nb % NB) * kSubRows * D,
+                            wave);
         }
         if (lim > 0) {
-            float* su = s_u + (sb & 1) * kLeafSub * 4;
-            const int ntile = (nsub + QT - 1) / QT;
-            for (int tl = part; tl < ntile; tl += wpc) {
+            const unsigned char* cur = reinterpret_cast<const unsigned char*>(L.q + (sb % NB) * kSubRows * D);
+            for (int tl = part; tl < kSubRows / 16; tl += wpc) {
                 const int el = tl * QT + qi;  // entry of this lane's column within the sub-chunk
-                const int r = el * G + head;
+                const unsigned char* tb = cur + tl * (16 * D * 2);
                 bf16x8 B[KS];
 #pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    B[s] = *reinterpret_cast<const bf16x8*>(cur + r * D + 8 * ((4 * s + lg) ^ (r & (CH - 1))));
+                for (int s = 0; s < KS; ++s) B[s] = *reinterpret_cast<const bf16x8*>(tb + boff[s]);
                 f32x4 acc[TPC];
 #pragma unroll
                 for (int rt = 0; rt < TPC; ++rt) {
@@ -728,22 +856,124 @@ __global__ __launch_bounds__(256) void leaf_kernel(ScoreArgs a)
                         true);
                 }
                 l2 = sum_adjacent(l2, G);
-                if (lg == 0 && head == 0 && el < nsub) su[el * 4 + j] = l2 * kLn2;
+                if (lg == 0 && head == 0 && el < nsub) L.u[(base + el) * 4 + j] = l2 * kLn2;
             }
         }
     }
-    // scores of the last sub-chunk
-    __syncthreads();
+    lds_barrier();
+    stream_write_scores(L, a.u + bh * a.N * ucols, n, ucols, g, ncand);
+}
+
+// Upper levels with g in {2, 4} (g * g <= 16 grandchildren per node), bf16
+// queries. A workgroup scores a chunk of up to kLeafQC entries of one cluster
+// (window, sequence x KV head, node P). P's g * g grandchild summaries (fp32,
+// split into two bf16 terms) form one 16-row A tile that every wave keeps in
+// registers; the chunk's query rows stream through the LDS ring, each wave
+// taking one 16-column tile per sub-chunk. Tile rows 4 * lg .. 4 * lg + 3 hold
+// 4 / RC whole candidates, so a lane reduces its candidates without crossing
+// lanes; the G heads of a query sit in adjacent lanes and are summed with DPP.
+// RC = g rows per candidate.
+template <int D, int RC, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void upper_kernel(ScoreArgs a)
+{
+    static_assert(RC == 2 || RC == 4, "g in {2, 4}");
+    constexpr int KS = D / 32;
+    constexpr int CH = D / 8;
+    constexpr int CPL = 4 / RC;  // candidates per lane
+    static_assert(16 % CH == 0, "a row tile spans whole swizzle periods");
+    static_assert(kSubRows == 64, "one tile per wave and sub-chunk");
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
+
+    const int64_t total = a.chunk_off[a.n_clusters];
+    if ((int64_t)blockIdx.x >= total) return;
+    const int64_t chunk = a.xcd ? xcd_chunk(blockIdx.x, total) : (int64_t)blockIdx.x;
+    const int64_t cl = a.chunk_cl[chunk];
+    const int e0 = a.offsets[cl] + (int)(chunk - a.chunk_off[cl]) * a.qc;
+    const int e1 = min(a.offsets[cl + 1], e0 + a.qc);
+    const int n = e1 - e0;
+    const int64_t P = cl % a.M_bins;
+    const int64_t bh = (cl / a.M_bins) % a.BH;
+    const int h = (int)(bh % a.H);
+    const int b = (int)(bh / a.H);
+    const int lane = threadIdx.x & 63, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = a.G, QT = 16 / G, SE = kSubRows / G;
+    const int glog = __builtin_ctz(G);  // G is a power of two
+    const int ucols = a.K_top * RC;
+    const StreamLds L = stream_lds<D, NB>(s_raw);
+
+    const bf16* Qb = reinterpret_cast<const bf16*>(a.Q) + (int64_t)b * a.N * a.H_q * D + (int64_t)h * G * D;
+    const uint32_t qrow = (uint32_t)(a.H_q * D);
+    const int nsb = (n + SE - 1) / SE;
+    StreamPrologue<D, NB> pr;
+    const StreamLane sl = stream_lane<D>(wave, lane, glog);
+    stream_prologue_load<D, NB>(pr, a.entries + e0, n, SE, sl, glog);
+    stream_prologue_issue<D, NB>(pr, L.ent, Qb, qrow, sl, L.q, wave);
+
+    // A operand: row (lane & 15) of P's grandchildren, k-chunk 8 * lg + 32 * s, as hi / lo bf16 terms
+    constexpr int nrows = RC * RC;
+    const int64_t row0 = P * nrows;
+    const int64_t rem = a.rows_limit - row0;
+    const int lim_rows = rem < nrows ? (int)rem : nrows;  // >= 1: P's first grandchild exists
+    bf16x8 ah[KS], al[KS];
     {
-        const int base = (nsb - 1) * kLeafSub;
-        const float* su = s_u + ((nsb - 1) & 1) * kLeafSub * 4;
-        for (int el = threadIdx.x; el < kLeafSub && base + el < e1 - e0; el += 256) {
-            const int ent = s_ent[base + el];
-            float* up = ub + (uint64_t)((uint32_t)ent >> 6) * (uint32_t)ucols + (ent & 63) * g;
-            if (g == 4 && ncand == 4) *reinterpret_cast<f32x4*>(up) = *reinterpret_cast<const f32x4*>(su + el * 4);
-            else for (int q = 0; q < ncand; ++q) up[q] = su[el * 4 + q];
+        const int r = lane & 15;
+        const bool ok = r < lim_rows;
+        const float* rp = reinterpret_cast<const float*>(a.rows) + (int64_t)b * a.rows_b_stride +
+                          (int64_t)h * a.rows_h_stride + (row0 + (ok ? r : 0)) * a.row_stride + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) Src<float>::load(rp + 32 * s, ok, ah[s], al[s]);
+    }
+
+    const float scale = kLog2e * rsqrtf((float)D);
+    const int col = lane & 15;
+    const int qi = col / G, head = col % G;
+    int boff[KS];  // byte offset of this lane's B piece within a row tile (as in leaf_kernel)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) boff[s] = (col * D + 8 * ((4 * s + lg) ^ (col & (CH - 1)))) * 2;
+    const int ncand = (lim_rows + RC - 1) / RC;  // children of P that exist
+
+    for (int sb = 0; sb < nsb; ++sb) {
+        const int base = sb * SE;
+        const int nsub = min(SE, n - base);
+        stream_wait<D, NB>(min(NB - 2, nsb - 1 - sb));
+        lds_barrier();
+        if (sb + NB - 1 < nsb) {
+            const int nb = sb + NB - 1;
+            stream_fetch<D>(Qb, qrow, L.ent + nb * SE, min(SE, n - nb * SE), sl, glog, L.q + (nb % NB) * kSubRows * D,
+                            wave);
+        }
+        const int el = wave * QT + qi;  // this wave's tile is row tile `wave` of the sub-chunk
+        const unsigned char* tb =
+            reinterpret_cast<const unsigned char*>(L.q + (sb % NB) * kSubRows * D) + wave * (16 * D * 2);
+        bf16x8 B[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) B[s] = *reinterpret_cast<const bf16x8*>(tb + boff[s]);
+        f32x4 acc_h = f32x4{0.f, 0.f, 0.f, 0.f}, acc_l = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            acc_h = mfma(ah[s], B[s], acc_h);
+            acc_l = mfma(al[s], B[s], acc_l);
+        }
+        float z[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = (acc_h[i] + acc_l[i]) * scale;
+        if (lim_rows < 16) {  // padding rows (g = 2), or a tail node with missing grandchildren
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * lg + i >= lim_rows) z[i] = -INFINITY;
+        }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            const int rfirst = 4 * lg + k * RC;
+            const bool exists = rfirst < lim_rows;
+            float l2 = lse2<RC, 0>(z + k * RC, exists);
+            l2 = sum_adjacent(l2, G);
+            if (head == 0 && exists && el < nsub) L.u[(base + el) * 4 + rfirst / RC] = l2 * kLn2;
         }
     }
+    lds_barrier();
+    stream_write_scores(L, a.u + bh * a.N * ucols, n, ucols, RC, ncand);
 }
 
 }  // namespace pisa

@@ -97,7 +97,7 @@ struct BsaArgs {
 // positions keep the queries a cluster gathers cache-resident: small windows
 // (L2-sized) for the levels above the leaves, whose node data is tiny, and
 // large ones at the leaf level, where each node brings g * C keys.
-inline int cluster_win_log2(int level) { return level == 1 ? 15 : 11; }
+inline int cluster_win_log2(int level) { return level == 1 ? 15 : (level == 2 ? 13 : 11); }
 
 // Level-synchronous routing: clustered scoring of one level.
 struct ScoreArgs {
@@ -149,10 +149,15 @@ struct DenseArgs {
 constexpr int kRegChunk = 32;
 constexpr int kRegWaves = 4;
 
-// Leaf level with bf16 keys and g in {2, 4}: chunks of kLeafQC entries whose
-// queries pass through LDS kLeafSub entries at a time.
+// Leaf and upper levels with bf16 queries and g in {2, 4}: chunks of kLeafQC
+// entries whose query rows (entry x head) stream through a ring of LDS
+// buffers kSubRows rows at a time, kLeafNB / kUpperNB buffers deep.
 constexpr int kLeafQC = 256;
-constexpr int kLeafSub = 16;
+constexpr int kSubRows = 64;
+constexpr int kLeafNB = 2;
+constexpr int kUpperNB = 3;
+// LDS bytes of one such workgroup: the ring, the chunk's entries and its scores
+inline size_t stream_lds_bytes(int d, int nb) { return (size_t)nb * kSubRows * d * 2 + (size_t)kLeafQC * (4 + 16); }
 
 // Per-item selection of one level, and counting of the next level's clusters.
 struct SelectArgs {
@@ -196,7 +201,8 @@ hipError_t launch_two_stage(const RouteArgs& a, const Stage2Args& s2, const Fina
                             int d, hipStream_t s);
 hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_dense(const DenseArgs& a, int dtype, int d, hipStream_t s);
-// kind: 0 summary rows staged in LDS, 1 key rows (leaf), 2 summary rows in registers
+// kind: 0 summary rows staged in LDS, 1 key rows (leaf), 2 summary rows in registers,
+// 3 leaf keys in registers with queries through LDS (bf16), 4 upper levels likewise (bf16)
 hipError_t launch_score(const ScoreArgs& a, int dtype, int d, int kind, int64_t grid, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_bsa(const BsaArgs& a, int dtype, int d, hipStream_t s);

@@ -1,5 +1,7 @@
 """GPU parity of the pyramid build and of prefill routing (fused and two-stage)
 against the CPU oracle, through the C ABI (hierarchical_top_amd.pisa)."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -34,9 +36,14 @@ CASES = {
     # fp32 with two-head groups
     "f32_g2": synth.Workload("f32g2", 1, 777, 4, 2, 64, 16, 2, 6, "f32", 0, 24, False),
     "p16k": custom("p16k"),
+    # large enough that the level router scores an upper level sparsely (more than 16 parents)
+    "sparse64k": synth.Workload("s64k", 1, 65536, 8, 2, 128, 64, 4, 8, "bf16", 0, 26, False),
+    # ragged length: sparse levels 3 and 2 with tail nodes missing grandchildren, two-head groups
+    "ragged_big": synth.Workload("rbig", 1, 70001, 4, 2, 128, 64, 4, 8, "bf16", 0, 25, False),
 }
 
 
+@functools.lru_cache(maxsize=1)  # the routers of one case run back to back
 def _inputs(w):
     Q, K, V, _ = synth.make_prefill(w)
     return Q, K
@@ -98,6 +105,8 @@ def _positions(w, sample):
     ("paper_shape", 8, True, None),
     ("f32_g2", 6, True, None),
     ("p16k", 8, True, None),
+    ("sparse64k", 8, True, 600),
+    ("ragged_big", 8, True, 600),
 ])
 def test_route_matches_oracle(mode, case, K_top, causal, sample):
     w = CASES[case]
