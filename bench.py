@@ -319,10 +319,18 @@ def prefill_extra(name, reps, with_attn=False):
     out["build_ms"] = bms
     out["speedup_vs_bsa"] = (out["bsa_ms"] + bms) / best
     if with_attn:
-        P.step(pisa.TWO_STAGE)
+        P.step(pisa.LEVELS)
         O = torch.empty_like(P.Q)
-        ms = time_fn(lambda: pisa.sparse_attn(P.Q, P.K, P.V, P.idx, w.C, w.N, out=O), reps)
         aw = workcount.attn_work(w.B, w.N, w.H_q, w.d, w.C, w.K_top)
+        ws = torch.empty(pisa.sparse_attn_workspace_bytes(w.B, w.N, w.N, w.H_q, w.H_kv, w.d, w.C, w.K_top),
+                         dtype=torch.uint8, device="cuda")
+        ms_rows = time_fn(lambda: pisa.sparse_attn(P.Q, P.K, P.V, P.idx, w.C, w.N, out=O), max(2, reps // 2))
+        ms_cl = time_fn(lambda: pisa.sparse_attn_clustered(P.Q, P.K, P.V, P.idx, w.C, w.N, workspace=ws, out=O),
+                        reps)
+        del ws
+        ms = min(ms_rows, ms_cl)
+        out["attn_ms_per_row"] = ms_rows
+        out["attn_ms_clustered"] = ms_cl
         out["attn_ms"] = ms
         out["attn_tflops"] = 2 * aw["mac"] / (ms * 1e-3) / 1e12
         out["attn_mfma_frac"] = out["attn_tflops"] / PEAK_BF16_TFLOPS

@@ -482,6 +482,60 @@ pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_d
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn");
 }
 
+static pisa_status check_attn_cl(int32_t B, int64_t N_q, int64_t N_alloc, int32_t H_q, int32_t H_kv, int32_t d,
+                                 int32_t C, int32_t K_top)
+{
+    if (B < 1 || N_q < 1 || N_alloc < 1) return fail(PISA_EINVAL, "need B >= 1, N_q >= 1, N_alloc >= 1");
+    if (H_kv < 1 || H_q < 1 || H_q % H_kv) return fail(PISA_EINVAL, "H_q must be a positive multiple of H_kv");
+    const int G = H_q / H_kv;
+    if (d != 64 && d != 128) return fail(PISA_EUNSUPPORTED, "d=%d (supported: 64, 128)", d);
+    if (C != 16 && C != 32 && C != 64) return fail(PISA_EUNSUPPORTED, "C=%d (supported: 16, 32, 64)", C);
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return fail(PISA_EUNSUPPORTED, "G_Q=%d", G);
+    if (K_top < 1 || K_top > 64) return fail(PISA_EUNSUPPORTED, "clustered attention: K_top=%d outside [1, 64]", K_top);
+    if (N_q >= ((int64_t)1 << 25)) return fail(PISA_EUNSUPPORTED, "clustered attention needs N_q < 2^25");
+    return PISA_OK;
+}
+
+pisa_status pisa_sparse_attn_workspace(int32_t B, int64_t N_q, int64_t N_alloc, int32_t H_q, int32_t H_kv, int32_t d,
+                                       int32_t C, int32_t K_top, size_t* bytes)
+{
+    if (!bytes) return fail(PISA_EINVAL, "bytes must be non-NULL");
+    pisa_status st = check_attn_cl(B, N_q, N_alloc, H_q, H_kv, d, C, K_top);
+    if (st != PISA_OK) return st;
+    *bytes = attn_cl_layout(B, N_q, N_alloc, H_kv, H_q / H_kv, d, C, K_top).bytes;
+    return ok();
+}
+
+pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void* V, pisa_dtype dt, int32_t B,
+                                       int64_t N_q, int64_t N_kv, int64_t N_alloc, int32_t H_q, int32_t H_kv,
+                                       int32_t d, int32_t C, const int32_t* block_idx, int32_t K_top, int32_t causal,
+                                       const int64_t* kv_len, void* O, float* lse, void* ws, size_t ws_bytes,
+                                       void* stream)
+{
+    if (!dtype_ok(dt)) return fail(PISA_EINVAL, "dtype %d is not PISA_F32 or PISA_BF16", (int)dt);
+    if (dt != PISA_BF16) return fail(PISA_EUNSUPPORTED, "clustered attention takes bf16 inputs");
+    if (!Q || !K || !V || !block_idx || !O || !ws)
+        return fail(PISA_EINVAL, "Q, K, V, block_idx, O and ws must be non-NULL");
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+        return fail(PISA_EINVAL, "Q, K, V and O must be 16-byte aligned");
+    if (((uintptr_t)ws & 255) != 0) return fail(PISA_EINVAL, "ws must be 256-byte aligned");
+    if (N_kv < 1 || N_alloc < N_kv || N_q > N_kv) return fail(PISA_EINVAL, "need 1 <= N_q <= N_kv <= N_alloc");
+    pisa_status st = check_attn_cl(B, N_q, N_alloc, H_q, H_kv, d, C, K_top);
+    if (st != PISA_OK) return st;
+    const AttnClLayout L = attn_cl_layout(B, N_q, N_alloc, H_kv, H_q / H_kv, d, C, K_top);
+    if (ws_bytes < L.bytes)
+        return fail(PISA_ENOSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.bytes);
+    AttnClArgs a;
+    memset(&a, 0, sizeof(a));
+    a.Q = Q; a.K = K; a.V = V; a.B = B; a.H_q = H_q; a.H_kv = H_kv; a.G = H_q / H_kv; a.C = C; a.K_top = K_top;
+    a.causal = causal ? 1 : 0; a.N_q = N_q; a.N_kv = N_kv; a.N_alloc = N_alloc; a.idx = block_idx;
+    a.kv_len = kv_len; a.O = O; a.lse = lse;
+    stage_mark(PISA_STAGE_ATTN, false, (hipStream_t)stream);
+    hipError_t e = launch_attn_clustered(a, d, (char*)ws, (hipStream_t)stream);
+    stage_mark(PISA_STAGE_ATTN, true, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn_clustered");
+}
+
 pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt, int64_t N, int32_t H_q,
                             int32_t K_top, int32_t causal, int32_t gqa_group, int32_t* idx, float* score,
                             void* stream)

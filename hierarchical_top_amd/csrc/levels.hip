@@ -448,6 +448,24 @@ __global__ void fill_zero_lv_kernel(int32_t* p, int64_t n)
         p[i] = 0;
 }
 
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(fill_zero_lv_kernel, dim3(256), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_chunks(const int32_t* counts, int64_t n, int qc, int32_t* block_sums, int32_t* offsets,
+                              int32_t* chunk_off, int32_t* chunk_cl, hipStream_t s)
+{
+    const unsigned nsb = (unsigned)((n + 1023) / 1024);
+    hipLaunchKernelGGL(scan_totals_kernel, dim3(nsb), dim3(1024), 0, s, counts, n, qc, block_sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_final_kernel, dim3(nsb), dim3(1024), 0, s, counts, n, qc, block_sums, offsets, chunk_off,
+                       chunk_cl);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 static int64_t nodes_n(int64_t n, int c_log2, int g_log2, int l)
 {

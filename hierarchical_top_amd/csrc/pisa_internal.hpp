@@ -83,6 +83,46 @@ struct AttnArgs {
     float* lse;
 };
 
+// Clustered attention (attn_cl.hip): arguments as in AttnArgs plus the
+// workspace sections (attn_cl_layout).
+struct AttnClArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    int B, H_q, H_kv, G, C, K_top, causal;
+    int64_t N_q, N_kv, N_alloc;
+    const int32_t* idx;
+    const int64_t* kv_len;
+    void* O;
+    float* lse;
+    int64_t M_blk;       // blocks per sequence: ceil(N_alloc / C)
+    int64_t n_clusters;  // B * H_kv * M_blk
+    int qc;              // entries per chunk
+    int32_t* counts;
+    int32_t* cursor;
+    int32_t* offsets;
+    int32_t* chunk_off;
+    int32_t* chunk_cl;
+    int32_t* block_sums;
+    int32_t* entries;    // (row << 6) | slot
+    float* part_lse;     // [B][H_kv][N_q][K_top][G][2]: base-2 log-sum-exp of the block's scaled scores, exponent e
+    void* part_o;        // [B][H_kv][N_q][K_top][G][d] fp16: the block's normalised output times 2^-e
+};
+
+struct AttnClLayout {
+    int64_t M_blk, n_clusters, n_items, max_chunks, n_sums;
+    size_t counts, offsets, chunk_off, chunk_cl, block_sums, entries, part_lse, part_o, bytes;
+};
+AttnClLayout attn_cl_layout(int64_t B, int64_t N_q, int64_t N_alloc, int H_kv, int G, int d, int C, int K_top);
+hipError_t launch_attn_clustered(AttnClArgs a, int d, char* ws, hipStream_t s);
+
+// Shared clustering steps (levels.hip): zero n ints; exclusive scans of n
+// cluster sizes into offsets, chunks of qc entries per cluster into chunk_off
+// and the chunk -> cluster map.
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s);
+hipError_t launch_scan_chunks(const int32_t* counts, int64_t n, int qc, int32_t* block_sums, int32_t* offsets,
+                              int32_t* chunk_off, int32_t* chunk_cl, hipStream_t s);
+
 struct BsaArgs {
     PyrArgs p;
     const void* Q;

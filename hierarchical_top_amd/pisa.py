@@ -61,6 +61,10 @@ def lib():
             "pisa_route_decode": [P, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_sparse_attn": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p,
                                  c_i32, c_i32, c_p, c_p, c_p, c_p],
+            "pisa_sparse_attn_workspace": [c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                           ctypes.POINTER(c_size)],
+            "pisa_sparse_attn_clustered": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                           c_i32, c_p, c_i32, c_i32, c_p, c_p, c_p, c_p, c_size, c_p],
             "pisa_bsa_select": [P, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_time_stage": [c_i32, c_p, c_p],
             "pisa_time_stage_pending": [c_i32],
@@ -80,7 +84,8 @@ def lib():
 
 
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
-           "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_bsa_select", "pisa_time_stage",
+           "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_sparse_attn_workspace",
+           "pisa_sparse_attn_clustered", "pisa_bsa_select", "pisa_time_stage",
            "pisa_time_stage_pending",
            "pisa_status_str", "pisa_last_error", "pisa_abi_version"]
 
@@ -207,6 +212,31 @@ def sparse_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, block_idx: to
     _check(lib().pisa_sparse_attn(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, N_q, N_kv, N_alloc, H_q, H_kv, d, C,
                                   _ptr(block_idx), K_top, 1 if causal else 0, _ptr(kv_len), _ptr(O), _ptr(lse),
                                   _stream()))
+    return (O, lse) if with_lse else O
+
+
+def sparse_attn_workspace_bytes(B: int, N_q: int, N_alloc: int, H_q: int, H_kv: int, d: int, C: int,
+                                K_top: int) -> int:
+    n = c_size(0)
+    _check(lib().pisa_sparse_attn_workspace(B, N_q, N_alloc, H_q, H_kv, d, C, K_top, ctypes.byref(n)))
+    return int(n.value)
+
+
+def sparse_attn_clustered(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, block_idx: torch.Tensor, C: int,
+                          N_kv: int, causal: bool = True, kv_len: torch.Tensor | None = None, with_lse: bool = False,
+                          workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """Block-sparse attention clustered by selected block (bf16); same results as sparse_attn."""
+    _dev(Q, K, V, block_idx, kv_len)
+    B, N_q, H_q, d = Q.shape
+    N_alloc, H_kv = K.shape[1], K.shape[2]
+    K_top = block_idx.shape[-1]
+    need = sparse_attn_workspace_bytes(B, N_q, N_alloc, H_q, H_kv, d, C, K_top)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=Q.device)
+    O = out if out is not None else torch.empty_like(Q)
+    lse = torch.empty(B, H_q, N_q, dtype=torch.float32, device=Q.device) if with_lse else None
+    _check(lib().pisa_sparse_attn_clustered(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, N_q, N_kv, N_alloc, H_q, H_kv, d,
+                                            C, _ptr(block_idx), K_top, 1 if causal else 0, _ptr(kv_len), _ptr(O),
+                                            _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return (O, lse) if with_lse else O
 
 

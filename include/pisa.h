@@ -181,6 +181,30 @@ pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_d
                              float* lse, void* stream);
 
 /*
+ * Block-sparse attention forward for many query rows (prefill), clustered by
+ * selected block: same arguments, layouts and results as pisa_sparse_attn
+ * (section 3.1 eq 6, appendix B masking), computed as one partial softmax per
+ * (row, selected block) -- each block's keys and values read once per chunk
+ * of up to 256 rows that selected it -- merged per row with the partials'
+ * log-sum-exp weights (the softmax factorisation over disjoint key sets).
+ * Partial outputs are stored in fp16 scaled by a power of two (11
+ * significant bits) before the merge.
+ * ws: device workspace of at least pisa_sparse_attn_workspace() bytes,
+ * 256-byte aligned, owned by the caller, contents on entry ignored; calls
+ * sharing a workspace must not overlap.
+ * Supported: dt = PISA_BF16, d in {64, 128}, C in {16, 32, 64}, G_Q in
+ * {1, 2, 4, 8, 16}, K_top <= 64, N_q < 2^25.
+ * Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE (ws too small), PISA_EHIP.
+ */
+pisa_status pisa_sparse_attn_workspace(int32_t B, int64_t N_q, int64_t N_alloc, int32_t H_q, int32_t H_kv,
+                                       int32_t d, int32_t C, int32_t K_top, size_t* bytes);
+pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void* V, pisa_dtype dt,
+                                       int32_t B, int64_t N_q, int64_t N_kv, int64_t N_alloc, int32_t H_q,
+                                       int32_t H_kv, int32_t d, int32_t C, const int32_t* block_idx,
+                                       int32_t K_top, int32_t causal, const int64_t* kv_len, void* O,
+                                       float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Exhaustive single-level selector in the style of BSA (section 3.1 eq 2-5),
  * the comparison point: every eligible leaf (start <= t when causal) except
  * the forced ones is scored by z = q_{t,h'} . kbar_i / sqrt(d) with the level-1

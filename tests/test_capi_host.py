@@ -157,6 +157,33 @@ def test_attention_and_bsa_validation(lib):
     assert b(ctypes.byref(desc), FAKE, pisa.BF16, 5000, 16, 8, 1, 4, FAKE, None, None) == ENOSPACE
 
 
+def test_clustered_attention_validation(lib):
+    n = pisa.c_size(0)
+    w = lib.pisa_sparse_attn_workspace
+    assert w(1, 65536, 65536, 32, 8, 128, 64, 8, ctypes.byref(n)) == OK
+    big = n.value
+    # entries, partial outputs (G x d fp16) and log-sum-exps + exponents per (row, slot), plus the cluster tables
+    assert big >= 65536 * 8 * 8 * (4 + 4 * 8 + 4 * 128 * 2)
+    assert w(1, 1024, 65536, 32, 8, 128, 64, 8, ctypes.byref(n)) == OK and n.value < big
+    assert w(1, 1024, 1024, 32, 8, 128, 64, 65, ctypes.byref(n)) == EUNSUPPORTED
+    assert w(1, 1024, 1024, 32, 8, 96, 64, 8, ctypes.byref(n)) == EUNSUPPORTED
+    assert w(1, 1024, 1024, 32, 8, 128, 64, 8, None) == EINVAL
+    assert w(1, 1024, 1024, 30, 8, 128, 64, 8, ctypes.byref(n)) == EINVAL
+    a = lib.pisa_sparse_attn_clustered
+    WS = ctypes.c_void_p(0x100000)  # 256-byte aligned, never dereferenced: rejected before any launch
+    need = pisa.sparse_attn_workspace_bytes(1, 10, 10, 8, 2, 128, 64, 8)
+    args = [FAKE, FAKE, FAKE, pisa.BF16, 1, 10, 10, 10, 8, 2, 128, 64, FAKE, 8, 1, None, FAKE, None]
+    assert a(*args, WS, need - 1, None) == ENOSPACE
+    assert a(*args, None, need, None) == EINVAL
+    assert a(*args, ctypes.c_void_p(0x100010), need, None) == EINVAL  # misaligned workspace
+    f32 = list(args)
+    f32[3] = pisa.F32
+    assert a(*f32, WS, need, None) == EUNSUPPORTED
+    k65 = list(args)
+    k65[13] = 65
+    assert a(*k65, WS, 1 << 40, None) == EUNSUPPORTED
+
+
 def test_time_stage_validation(lib):
     assert lib.pisa_time_stage(10, None, None) == EINVAL
     assert lib.pisa_time_stage(-1, None, None) == EINVAL

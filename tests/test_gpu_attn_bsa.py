@@ -36,19 +36,29 @@ def _positions(w, sample):
                                      np.arange(w.N - w.C, w.N)]))
 
 
+def _attn(entry, *args, **kw):
+    """The per-row entry point or the one clustered by selected block (bf16)."""
+    fn = pisa.sparse_attn if entry == "rows" else pisa.sparse_attn_clustered
+    return fn(*args, **kw)
+
+
+@pytest.mark.parametrize("entry", ["rows", "clustered"])
 @pytest.mark.parametrize("case,causal,sample,dense", [
     ("tiny", True, None, False),
     ("tiny", True, None, True),
     ("tiny", False, None, False),
     ("ragged", True, None, False),
+    ("ragged", False, None, False),
     ("c32_b2", True, None, False),
     ("paper_shape", True, 1024, False),
     ("f32_g4", True, None, False),
     ("p64k", True, 1024, False),
 ])
-def test_sparse_attention_matches_oracle(case, causal, sample, dense):
+def test_sparse_attention_matches_oracle(case, causal, sample, dense, entry):
     w = W[case]
-    print("case", case, "causal", causal, "dense", dense, flush=True)
+    if entry == "clustered" and w.dtype != "bf16":
+        pytest.skip("the clustered entry point takes bf16 inputs")
+    print("case", case, "causal", causal, "dense", dense, "entry", entry, flush=True)
     Q, K, V, _ = synth.make_prefill(w)
     t = _positions(w, sample)
     M1 = -(-w.N // w.C)
@@ -63,11 +73,11 @@ def test_sparse_attention_matches_oracle(case, causal, sample, dense):
             sel = oracle.route(opyr, Q[b, t].float().numpy(), [b] * len(t), t, K_top, causal=causal)["idx"]
         want = oracle.sparse_attn(Q[b, t].float().numpy(), [0] * len(t), t, Kf[b:b + 1], Vf[b:b + 1], w.N, w.C,
                                   sel, causal=causal)
-        # GPU: full [B][H][N][K] index tensor, rows outside the sample get the same blocks as row t[0]
+        # GPU: full [B][H][N][K] index tensor, rows outside the sample select nothing
         full = np.full((w.B, w.H_kv, w.N, K_top), -1, np.int32)
         full[b][:, t] = sel.transpose(1, 0, 2)
         idx = torch.from_numpy(full).cuda()
-        O, lse = pisa.sparse_attn(Qd, Kd, Vd, idx, w.C, w.N, causal=causal, with_lse=True)
+        O, lse = _attn(entry, Qd, Kd, Vd, idx, w.C, w.N, causal=causal, with_lse=True)
         torch.cuda.synchronize()
         got = O[b, t].float().cpu().numpy()
         err = np.abs(got - want["out"]).max()
@@ -77,7 +87,8 @@ def test_sparse_attention_matches_oracle(case, causal, sample, dense):
         np.testing.assert_allclose(gl, want["lse"], atol=1e-3 if w.dtype == "bf16" else 1e-4)
 
 
-def test_attention_decode_rows_and_empty_rows():
+@pytest.mark.parametrize("entry", ["rows", "clustered"])
+def test_attention_decode_rows_and_empty_rows(entry):
     """N_q = 1 with per-sequence lengths (decode shape); a row whose blocks are all
     masked or absent returns zeros and lse = -inf."""
     w = synth.Workload("dec", 3, 700, 8, 2, 64, 16, 4, 6, "bf16", 0, 35, True)
@@ -96,15 +107,15 @@ def test_attention_decode_rows_and_empty_rows():
                                        V[b:b + 1].float().numpy(), n, w.C, r["idx"]))
     sel_d = torch.from_numpy(sel).cuda()
     kv = torch.from_numpy(lens.astype(np.int64)).cuda()
-    O, lse = pisa.sparse_attn(q.unsqueeze(1).contiguous().cuda(), K.cuda(), V.cuda(), sel_d, w.C, w.N,
-                              kv_len=kv, with_lse=True)
+    O, lse = _attn(entry, q.unsqueeze(1).contiguous().cuda(), K.cuda(), V.cuda(), sel_d, w.C, w.N,
+                   kv_len=kv, with_lse=True)
     torch.cuda.synchronize()
     for b in range(3):
         np.testing.assert_allclose(O[b, 0].float().cpu().numpy(), want[b]["out"][0], atol=2e-2)
     # empty selection -> zeros, -inf
     none = torch.full_like(sel_d, -1)
-    O2, lse2 = pisa.sparse_attn(q.unsqueeze(1).contiguous().cuda(), K.cuda(), V.cuda(), none, w.C, w.N,
-                                kv_len=kv, with_lse=True)
+    O2, lse2 = _attn(entry, q.unsqueeze(1).contiguous().cuda(), K.cuda(), V.cuda(), none, w.C, w.N,
+                     kv_len=kv, with_lse=True)
     torch.cuda.synchronize()
     assert (O2 == 0).all() and torch.isneginf(lse2).all()
 
