@@ -33,7 +33,8 @@ constexpr int kClRowsPerThread = 4;
 constexpr int kClThreads = 256;
 constexpr int kClRowsPerBlock = kClThreads * kClRowsPerThread;
 constexpr int kClLdsBins = 8192;  // blocks per sequence aggregated in LDS (more: global atomics)
-constexpr int kAttnNB = 2;        // LDS ring depth (the kernel's stores count in vmcnt: wait for all)
+constexpr int kAttnNB = 3;        // LDS ring depth with the fetch wave
+constexpr bool kAttnFW = false;   // a dedicated fetch wave (costs a workgroup per CU in occupancy)
 
 struct RowGeom {
     int64_t nb;   // keys of the sequence
@@ -143,8 +144,8 @@ __device__ __forceinline__ int vt_pos(int key)
     return (key & ~31) + 8 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
 }
 
-template <int D, int C, int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_cl_kernel(AttnClArgs a)
+template <int D, int C, int NB, bool FW>
+__global__ __launch_bounds__(FW ? 320 : 256) __attribute__((amdgpu_waves_per_eu(3))) void attn_cl_kernel(AttnClArgs a)
 {
     constexpr int KS = D / 32;         // k-steps of S = K Q^T
     constexpr int TPC = C / 16;        // key row tiles
@@ -152,6 +153,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     constexpr int DT = D / 16;         // d tiles of O
     constexpr int CH = D / 8;
     constexpr int VLD = PS * 32 + 8;   // transposed value row stride (bf16)
+    constexpr int NI = StreamGeom<D>::NI;
     static_assert(16 % CH == 0, "a row tile spans whole swizzle periods");
     extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
     bf16* s_ring = reinterpret_cast<bf16*>(s_raw);                                  // [NB][kSubRows][D]
@@ -170,7 +172,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const int h = (int)(bh % a.H_kv);
     const int b = (int)(bh / a.H_kv);
     const int lane = threadIdx.x & 63, lg = lane >> 4;
+    // FW: waves 0-3 compute and wave 4 fetches the query rows: it alone issues and waits for
+    // the global-to-LDS loads, so its vmcnt counts nothing else and the compute waves' stores
+    // never stall on them. Otherwise every compute wave fetches its own share of each sub-chunk
+    // and waits for everything it issued (NB = 2).
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool fetcher = FW && wave == 4;
+    static_assert(FW || NB == 2, "without the fetch wave the stores count in vmcnt: wait for all");
     const int G = a.G, QT = 16 / G, SE = kSubRows / G;
     const int glog = __builtin_ctz(G);
     const RowGeom g0 = row_geom(a, b, 0);
@@ -181,48 +189,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const bf16* Qb = reinterpret_cast<const bf16*>(a.Q) + (int64_t)b * a.N_q * a.H_q * D + (int64_t)h * G * D;
     const uint32_t qrow = (uint32_t)(a.H_q * D);
     const int nsb = (n + SE - 1) / SE;
-    const StreamLane sl = stream_lane<D>(wave, lane, glog);
-    StreamPrologue<D, NB> pr;
-    stream_prologue_load<D, NB>(pr, a.entries + e0, n, SE, sl, glog);
 
-    const int64_t kvstride = (int64_t)a.H_kv * D;
-    const bf16* kb = reinterpret_cast<const bf16*>(a.K) + ((int64_t)b * a.N_alloc + k0) * kvstride + (int64_t)h * D;
-    const bf16* vb = reinterpret_cast<const bf16*>(a.V) + ((int64_t)b * a.N_alloc + k0) * kvstride + (int64_t)h * D;
-    // values: thread t loads 16-byte pieces (key, 8 d) of the padded block
-    constexpr int VPIECES = PS * 32 * CH;
-    constexpr int VPT = (VPIECES + 255) / 256;
-    bf16x8 vreg[VPT];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int p = threadIdx.x + 256 * i;
-        const int key = p / CH, dc = p % CH;
-        const bool ok = p < VPIECES && key < kexist;
-        const bf16x8 v = load8h(vb + (ok ? (int64_t)key * kvstride : 0) + 8 * dc);
-        vreg[i] = ok ? v : zero8h();
-    }
-    // keys: A operand rows (lane & 15) of each row tile, k-chunk 8 * lg + 32 * s
+    StreamLane sl[4];  // fetch wave: the rows of the four compute waves' shares
     bf16x8 A[TPC][KS];
-#pragma unroll
-    for (int rt = 0; rt < TPC; ++rt) {
-        const int key = rt * 16 + (lane & 15);
-        const bool ok = key < kexist;
-        const bf16* kp = kb + (ok ? (int64_t)key * kvstride : 0) + 8 * lg;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 v = load8h(kp + 32 * s);
-            A[rt][s] = ok ? v : zero8h();
-        }
+    StreamPrologue<D, NB> pr;  // without the fetch wave: this wave's share
+    if (!FW) {
+        sl[0] = stream_lane<D>(wave, lane, glog);
+        stream_prologue_load<D, NB>(pr, a.entries + e0, n, SE, sl[0], glog);
+        stream_prologue_issue<D, NB>(pr, s_ent, Qb, qrow, sl[0], s_ring, wave);
     }
-    stream_prologue_issue<D, NB>(pr, s_ent, Qb, qrow, sl, s_ring, wave);
-    // transposed values in LDS (made visible by the first barrier of the loop)
+    if (fetcher) {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int p = threadIdx.x + 256 * i;
-        if (p < VPIECES) {
+        for (int w = 0; w < 4; ++w) sl[w] = stream_lane<D>(w, lane, glog);
+        int pe[NB - 1][4][NI];
+#pragma unroll
+        for (int k = 0; k < NB - 1; ++k)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int el = k * SE + sl[w].el0 + ((i * StreamGeom<D>::STEP) >> glog);
+                    const int lim = min(n, (k + 1) * SE) - 1;
+                    pe[k][w][i] = a.entries[e0 + max(0, min(el, lim))];
+                }
+        wait_vm<0>();
+        // branch-free: sub-chunks past the end refetch the last entry into buffers no tile reads
+#pragma unroll
+        for (int k = 0; k < NB - 1; ++k)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) stream_issue<D>(Qb, qrow, pe[k][w], sl[w], s_ring + k * kSubRows * D, w);
+    } else {
+        if (FW) s_ent[threadIdx.x] = a.entries[e0 + min((int)threadIdx.x, n - 1)];  // slots past n: copies
+        const int64_t kvstride = (int64_t)a.H_kv * D;
+        const bf16* kb = reinterpret_cast<const bf16*>(a.K) + ((int64_t)b * a.N_alloc + k0) * kvstride + (int64_t)h * D;
+        const bf16* vb = reinterpret_cast<const bf16*>(a.V) + ((int64_t)b * a.N_alloc + k0) * kvstride + (int64_t)h * D;
+        // values: thread t loads 16-byte pieces (key, 8 d) of the padded block, then writes them transposed
+        constexpr int VPIECES = PS * 32 * CH;
+        constexpr int VPT = (VPIECES + 255) / 256;
+        bf16x8 vreg[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int p = threadIdx.x + 256 * i;
             const int key = p / CH, dc = p % CH;
-            const int vp = vt_pos(key);
+            const bool ok = p < VPIECES && key < kexist;
+            const bf16x8 v = load8h(vb + (ok ? (int64_t)key * kvstride : 0) + 8 * dc);
+            vreg[i] = ok ? v : zero8h();
+        }
+        // keys: A operand rows (lane & 15) of each row tile, k-chunk 8 * lg + 32 * s
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s_vt[(8 * dc + j) * VLD + vp] = vreg[i][j];
+        for (int rt = 0; rt < TPC; ++rt) {
+            const int key = rt * 16 + (lane & 15);
+            const bool ok = key < kexist;
+            const bf16* kp = kb + (ok ? (int64_t)key * kvstride : 0) + 8 * lg;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 v = load8h(kp + 32 * s);
+                A[rt][s] = ok ? v : zero8h();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            if (p < VPIECES) {
+                const int key = p / CH, dc = p % CH;
+                const int vp = vt_pos(key);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s_vt[(8 * dc + j) * VLD + vp] = vreg[i][j];
+            }
         }
     }
 
@@ -236,113 +269,132 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     for (int sb = 0; sb < nsb; ++sb) {
         const int base = sb * SE;
         const int nsub = min(SE, n - base);
-        stream_wait<D, NB>(min(NB - 2, nsb - 1 - sb));
-        lds_barrier();
-        if (sb + NB - 1 < nsb) {
-            const int nx = sb + NB - 1;
-            stream_fetch<D>(Qb, qrow, s_ent + nx * SE, min(SE, n - nx * SE), sl, glog, s_ring + (nx % NB) * kSubRows * D,
-                            wave);
+        if (!FW) stream_wait<D, NB>(0);
+        if (fetcher) {
+            // sub-chunk sb has landed once at most the later sub-chunks' fetches are outstanding
+            const int later = min(NB - 2, nsb - 1 - sb);
+            if (NB >= 4 && later >= 2) wait_vm<(NB >= 4 ? 8 * NI : 0)>();
+            else if (NB >= 3 && later >= 1) wait_vm<(NB >= 3 ? 4 * NI : 0)>();
+            else wait_vm<0>();
         }
-        const unsigned char* cur = reinterpret_cast<const unsigned char*>(s_ring + (sb % NB) * kSubRows * D);
-        // one 16-column tile per wave: entries wave * QT .. of the sub-chunk
-        const int el = wave * QT + qi;
-        const int ent = s_ent[base + (el < nsub ? el : nsub - 1)];
-        const int64_t r = (uint32_t)ent >> 6;
-        const int slot = ent & 63;
-        const RowGeom gr = row_geom(a, b, r);
-        const int vis = (int)(block_end(a, gr, k0) - k0);  // visible keys of this column (>= 1)
-
-        const unsigned char* tb = cur + wave * (16 * D * 2);
-        bf16x8 B[KS];
+        lds_barrier();  // sub-chunk sb is in LDS, and the buffer of sub-chunk sb - 1 is free again
+        if (fetcher) {
+            if (sb + NB - 1 < nsb) {
+                const int nx = sb + NB - 1;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) B[s] = *reinterpret_cast<const bf16x8*>(tb + boff[s]);
-        f32x4 acc[TPC];
-#pragma unroll
-        for (int rt = 0; rt < TPC; ++rt) {
-            acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) acc[rt] = mfma(A[rt][s], B[s], acc[rt]);
-        }
-        // scaled scores (base 2) in place, keys past the column's visible end dropped
-        const bool any_masked = ballot(vis < C) != 0;
-#pragma unroll
-        for (int rt = 0; rt < TPC; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = acc[rt][i] * scale;
-                acc[rt][i] = (!any_masked || rt * 16 + 4 * lg + i < vis) ? v : -INFINITY;
+                for (int w = 0; w < 4; ++w)
+                    stream_fetch<D>(Qb, qrow, s_ent + nx * SE, min(SE, n - nx * SE), sl[w], glog,
+                                    s_ring + (nx % NB) * kSubRows * D, w);
             }
-        float m = -INFINITY;
-#pragma unroll
-        for (int rt = 0; rt < TPC; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) m = fmaxf(m, acc[rt][i]);
-        m = max_xor16(m);
-        m = max_xor32(m);
-        // probabilities, packed straight into the P V operand as two bf16 terms, and their sum
-        float l = 0.f;
-        bf16x8 pbh[PS], pbl[PS];
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int rt = 2 * ps + hf;
-#pragma unroll
+            continue;
+        }
+        if (!FW && sb + 1 < nsb)
+            stream_fetch<D>(Qb, qrow, s_ent + (sb + 1) * SE, min(SE, n - (sb + 1) * SE), sl[0], glog,
+                            s_ring + ((sb + 1) % NB) * kSubRows * D, wave);
+            const unsigned char* cur = reinterpret_cast<const unsigned char*>(s_ring + (sb % NB) * kSubRows * D);
+            // one 16-column tile per wave: entries wave * QT .. of the sub-chunk
+            const int el = wave * QT + qi;
+            const int ent = s_ent[base + (el < nsub ? el : nsub - 1)];
+            const int64_t r = (uint32_t)ent >> 6;
+            const int slot = ent & 63;
+            const RowGeom gr{nb, nb - a.N_q + r};  // no reload of kv_len: a load here would wait on the stores
+            const int vis = (int)(block_end(a, gr, k0) - k0);  // visible keys of this column (>= 1)
+
+            const unsigned char* tb = cur + wave * (16 * D * 2);
+            bf16x8 B[KS];
+    #pragma unroll
+            for (int s = 0; s < KS; ++s) B[s] = *reinterpret_cast<const bf16x8*>(tb + boff[s]);
+            f32x4 acc[TPC];
+    #pragma unroll
+            for (int rt = 0; rt < TPC; ++rt) {
+                acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                for (int s = 0; s < KS; ++s) acc[rt] = mfma(A[rt][s], B[s], acc[rt]);
+            }
+            // scaled scores (base 2) in place, keys past the column's visible end dropped
+            const bool any_masked = ballot(vis < C) != 0;
+    #pragma unroll
+            for (int rt = 0; rt < TPC; ++rt)
+    #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float pv = 0.f;
-                    if (rt < TPC) {
-                        pv = __builtin_amdgcn_exp2f(acc[rt < TPC ? rt : 0][i] - m);
-                        l += pv;
+                    const float v = acc[rt][i] * scale;
+                    acc[rt][i] = (!any_masked || rt * 16 + 4 * lg + i < vis) ? v : -INFINITY;
+                }
+            float m = -INFINITY;
+    #pragma unroll
+            for (int rt = 0; rt < TPC; ++rt)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) m = fmaxf(m, acc[rt][i]);
+            m = max_xor16(m);
+            m = max_xor32(m);
+            // probabilities, packed straight into the P V operand as two bf16 terms, and their sum
+            float l = 0.f;
+            bf16x8 pbh[PS], pbl[PS];
+    #pragma unroll
+            for (int ps = 0; ps < PS; ++ps)
+    #pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int rt = 2 * ps + hf;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float pv = 0.f;
+                        if (rt < TPC) {
+                            pv = __builtin_amdgcn_exp2f(acc[rt < TPC ? rt : 0][i] - m);
+                            l += pv;
+                        }
+                        const bf16 ph = to_bf16(pv);
+                        pbh[ps][4 * hf + i] = ph;
+                        pbl[ps][4 * hf + i] = to_bf16(pv - from_bf16(ph));
                     }
-                    const bf16 ph = to_bf16(pv);
-                    pbh[ps][4 * hf + i] = ph;
-                    pbl[ps][4 * hf + i] = to_bf16(pv - from_bf16(ph));
+                }
+            l = add_xor16(l);
+            l = add_xor32(l);
+            // O^T tile (d x column) = V^T P^T: A = transposed values (LDS), B = this lane's probabilities
+            f32x4 o[DT];
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+            for (int ps = 0; ps < PS; ++ps)
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(s_vt + (dt * 16 + (lane & 15)) * VLD + 32 * ps + 8 * lg);
+                    o[dt] = mfma(va, pbh[ps], o[dt]);
+                    o[dt] = mfma(va, pbl[ps], o[dt]);
+                }
+            // normalised row, scaled by 2^-e so that its largest |element| is below 1
+            const float inv = 1.f / l;
+            float amax = 0.f;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[dt][i]));
+            amax = max_xor16(amax);
+            amax = max_xor32(amax);
+            const int e = amax * inv > 0.f ? __builtin_amdgcn_frexp_expf(amax * inv) : 0;
+            const float sc = __builtin_ldexpf(inv, -e);
+            if (el < nsub) {
+                const int64_t row = ((bh * a.N_q + r) * a.K_top + slot) * G + head;
+                f16* op = reinterpret_cast<f16*>(a.part_o) + row * D + 4 * lg;
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    f16x4 w;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = (f16)(o[dt][i] * sc);
+                    *reinterpret_cast<f16x4*>(op + 16 * dt) = w;
+                }
+                if (lg == 0) {
+                    a.part_lse[2 * row] = m + __builtin_amdgcn_logf(l);
+                    a.part_lse[2 * row + 1] = (float)e;
                 }
             }
-        l = add_xor16(l);
-        l = add_xor32(l);
-        // O^T tile (d x column) = V^T P^T: A = transposed values (LDS), B = this lane's probabilities
-        f32x4 o[DT];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8 va = *reinterpret_cast<const bf16x8*>(s_vt + (dt * 16 + (lane & 15)) * VLD + 32 * ps + 8 * lg);
-                o[dt] = mfma(va, pbh[ps], o[dt]);
-                o[dt] = mfma(va, pbl[ps], o[dt]);
-            }
-        // normalised row, scaled by 2^-e so that its largest |element| is below 1
-        const float inv = 1.f / l;
-        float amax = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[dt][i]));
-        amax = max_xor16(amax);
-        amax = max_xor32(amax);
-        const int e = amax * inv > 0.f ? __builtin_amdgcn_frexp_expf(amax * inv) : 0;
-        const float sc = __builtin_ldexpf(inv, -e);
-        if (el < nsub) {
-            const int64_t row = ((bh * a.N_q + r) * a.K_top + slot) * G + head;
-            f16* op = reinterpret_cast<f16*>(a.part_o) + row * D + 4 * lg;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                f16x4 w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = (f16)(o[dt][i] * sc);
-                *reinterpret_cast<f16x4*>(op + 16 * dt) = w;
-            }
-            if (lg == 0) {
-                a.part_lse[2 * row] = m + __builtin_amdgcn_logf(l);
-                a.part_lse[2 * row + 1] = (float)e;
-            }
-        }
+
     }
 }
 
-// One wave per (sequence, row, KV head): lane pairs (head, 8 d) of the G x D outputs.
+// One wave per (sequence, row, KV head). The slot ids are read across the
+// lanes at once; each lane then merges pairs (head, 8 d) of the G x D outputs,
+// eight slots at a time with their loads in flight together and an online
+// maximum across the groups.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnClArgs a)
 {
@@ -355,42 +407,60 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnClArgs a)
     const int64_t bh = item / a.N_q;
     const int h = (int)(bh % a.H_kv);
     const int b = (int)(bh / a.H_kv);
-    const int G = a.G;
+    const int G = a.G, K_top = a.K_top;
     const RowGeom g = row_geom(a, b, r);
-    const int32_t* sel = a.idx + (bh * a.N_q + r) * a.K_top;
-    uint64_t valid = 0;  // slots with visible keys (K_top <= 64)
-    for (int k = 0; k < a.K_top; ++k) {
-        const int blk = sel[k];
-        if (blk < 0) continue;
+    const int64_t prow = (bh * a.N_q + r) * K_top;  // partial row of slot 0
+    bool vis = false;
+    if (lane < K_top) {
+        const int blk = a.idx[prow + lane];
         const int64_t k0 = (int64_t)blk * a.C;
-        if (k0 < g.nb && block_end(a, g, k0) > k0) valid |= 1ull << k;
+        vis = blk >= 0 && k0 < g.nb && block_end(a, g, k0) > k0;
     }
-    const int64_t prow = (bh * a.N_q + r) * a.K_top;  // partial row of slot 0
+    const uint64_t valid = ballot(vis);  // slots with visible keys (K_top <= 64)
     const f16* po = reinterpret_cast<const f16*>(a.part_o);
     bf16* O = reinterpret_cast<bf16*>(a.O);
-    for (int pair = lane; pair < G * CH; pair += 64) {
-        const int head = pair / CH, dc = pair % CH;
-        float M = -INFINITY;
-        for (uint64_t v = valid; v; v &= v - 1) {
-            const int k = __builtin_ctzll(v);
-            M = fmaxf(M, a.part_lse[2 * ((prow + k) * G + head)]);
-        }
+    for (int pair = lane; pair - lane < G * CH; pair += 64) {
+        const bool active = pair < G * CH;
+        const int head = active ? pair / CH : 0, dc = active ? pair % CH : 0;
+        float M = -INFINITY, L = 0.f;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float L = 0.f;
-        for (uint64_t v = valid; v; v &= v - 1) {
-            const int k = __builtin_ctzll(v);
-            const int64_t row = (prow + k) * G + head;
-            const float w = __builtin_amdgcn_exp2f(a.part_lse[2 * row] - M);
-            const float ws = __builtin_ldexpf(w, (int)a.part_lse[2 * row + 1]);
-            const f16x8 x = *reinterpret_cast<const f16x8*>(po + row * D + 8 * dc);
-            L += w;
+        // slots in groups of 8: log-sum-exps first, then the 8 rows' loads together
+        for (int k0 = 0; k0 < K_top; k0 += 8) {
+            const uint64_t grp = (valid >> k0) & 0xffull;
+            if (!grp) continue;
+            float lse[8], ex[8];
+            f16x8 x[8];
+            const int kfirst = k0 + __builtin_ctzll(grp);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += ws * (float)x[j];
+            for (int j = 0; j < 8; ++j) {
+                const bool ok = (grp >> j) & 1;
+                const int64_t row = (prow + (ok ? k0 + j : kfirst)) * G + head;
+                lse[j] = ok ? a.part_lse[2 * row] : -INFINITY;
+                ex[j] = a.part_lse[2 * row + 1];
+                x[j] = *reinterpret_cast<const f16x8*>(po + row * D + 8 * dc);
+            }
+            float Mn = M;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, lse[j]);
+            const float f = __builtin_amdgcn_exp2f(M - Mn);  // M = -inf on the first group: f = 0
+            L *= f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] *= f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float w = __builtin_amdgcn_exp2f(lse[j] - Mn);  // 0 for slots not in the group
+                const float ws = __builtin_ldexpf(w, (int)ex[j]);
+                L += w;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += ws * (float)x[j][i];
+            }
+            M = Mn;
         }
+        if (!active) continue;
         const float inv = L > 0.f ? 1.f / L : 0.f;
         bf16x8 out;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out[j] = to_bf16(acc[j] * inv);
+        for (int i = 0; i < 8; ++i) out[i] = to_bf16(acc[i] * inv);
         *reinterpret_cast<bf16x8*>(O + (((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head) * D + 8 * dc) = out;
         if (a.lse && dc == 0)
             a.lse[((int64_t)b * a.H_q + (int64_t)h * G + head) * a.N_q + r] =
@@ -402,13 +472,14 @@ template <int D, int C>
 static hipError_t launch_cl(const AttnClArgs& a, int64_t grid, hipStream_t s)
 {
     constexpr int PS = (C + 31) / 32;
-    const size_t lds = (size_t)kAttnNB * kSubRows * D * 2 + (size_t)D * (PS * 32 + 8) * 2 + (size_t)kLeafQC * 4;
-    auto k = attn_cl_kernel<D, C, kAttnNB>;
+    constexpr int NB = kAttnFW ? kAttnNB : 2;
+    const size_t lds = (size_t)NB * kSubRows * D * 2 + (size_t)D * (PS * 32 + 8) * 2 + (size_t)kLeafQC * 4;
+    auto k = attn_cl_kernel<D, C, NB, kAttnFW>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kAttnFW ? 320 : 256), lds, s, a);
     return hipGetLastError();
 }
 
