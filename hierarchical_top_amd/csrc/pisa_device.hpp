@@ -1,6 +1,6 @@
 // pisa_device.hpp -- device helpers for the gfx950 kernels of libpisa:
 // bf16 conversion and hi/lo splitting, the 16x16x32 bf16 MFMA, wavefront
-// primitives (shuffles, ballots, bitonic sort) and pyramid geometry.
+// primitives (shuffles, ballots, rank sorts) and pyramid geometry.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -192,52 +192,34 @@ __device__ __forceinline__ bool before(float ka, int ia, float kb, int ib)
     return ka > kb || (ka == kb && ia < ib);
 }
 
-// Bitonic sort of (key, id) over the 64 lanes into selection order: after the
-// call lane 0 holds the first element. Ids must be distinct among lanes that
-// carry equal keys (padding lanes use key -inf and distinct large ids).
-__device__ __forceinline__ void bitonic_sort(float& key, int& id)
+// Moves every lane's (key, id) to the lane of its rank in selection order:
+// each live lane counts the live lanes before it (scalar reads of their key
+// and id, one per live lane), then one permute places all lanes. Live lanes
+// come first, in selection order; the others follow in lane order. Ids must be
+// distinct among live lanes.
+__device__ __forceinline__ void rank_sort(float& key, int& id, uint64_t live)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            float ok = shfl_xor(key, j);
-            int oi = shfl_xor(id, j);
-            bool forward = (lane & k) == 0 || k == 64;
-            bool lower = (lane & j) == 0;
-            bool want_first = (lower == forward);
-            bool other_first = before(ok, oi, key, id);
-            bool take = want_first ? other_first : !other_first;
-            if (take) {
-                key = ok;
-                id = oi;
-            }
-        }
+    int rank = 0;
+    for (uint64_t m = live; m; m &= m - 1) {
+        const int j = __builtin_ctzll(m);
+        const float kj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key), j));
+        const int ij = __builtin_amdgcn_readlane(id, j);
+        rank += before(kj, ij, key, id) ? 1 : 0;
     }
+    if (!((live >> lane_id()) & 1)) rank = __popcll(live) + rank_below(~live);
+    key = __int_as_float(__builtin_amdgcn_ds_permute(rank << 2, __float_as_int(key)));
+    id = __builtin_amdgcn_ds_permute(rank << 2, id);
 }
 
-// Sort ids ascending across the wave, carrying a float payload (ids distinct;
-// padding lanes use INT_MAX - lane).
-__device__ __forceinline__ void sort_ids_ascending(int& id, float& val)
+// The live lanes' ids in ascending order in lanes 0.., carrying a float
+// payload (ids distinct among live lanes); the other lanes follow.
+__device__ __forceinline__ void rank_sort_ids(int& id, float& val, uint64_t live)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            int oi = shfl_xor(id, j);
-            float ov = shfl_xor(val, j);
-            bool forward = (lane & k) == 0 || k == 64;
-            bool lower = (lane & j) == 0;
-            bool want_small = (lower == forward);
-            bool take = want_small ? (oi < id) : (oi > id);
-            if (take) {
-                id = oi;
-                val = ov;
-            }
-        }
-    }
+    int rank = 0;
+    for (uint64_t m = live; m; m &= m - 1) rank += __builtin_amdgcn_readlane(id, __builtin_ctzll(m)) < id ? 1 : 0;
+    if (!((live >> lane_id()) & 1)) rank = __popcll(live) + rank_below(~live);
+    val = __int_as_float(__builtin_amdgcn_ds_permute(rank << 2, __float_as_int(val)));
+    id = __builtin_amdgcn_ds_permute(rank << 2, id);
 }
 
 // ---------------------------------------------------------------------------

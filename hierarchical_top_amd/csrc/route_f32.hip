@@ -7,7 +7,7 @@ template <int D, int G>
 static hipError_t route_query_dg(const RouteArgs& a, int mode, hipStream_t s)
 {
     if (mode == MODE_DECODE)
-        hipLaunchKernelGGL((route_decode_kernel<D, float, G>), dim3((unsigned)(a.p.B * a.p.H)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((route_decode_kernel<D, float, G>), dim3((unsigned)(a.p.B * a.p.H)), dim3(64 * kDecodeWaves), 0, s, a);
     else if (mode == MODE_STAGE1)
         hipLaunchKernelGGL((route_query_kernel<D, float, G, MODE_STAGE1>), dim3((unsigned)((int64_t)a.p.B * a.p.H * a.N)),
                            dim3(64), 0, s, a);

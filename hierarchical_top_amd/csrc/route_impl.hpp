@@ -12,8 +12,9 @@
 //   fp32 queries their low halves; columns = child summaries or raw keys,
 //   fp32 sources split into two bf16 terms), then a per-head log-sum-exp over
 //   each candidate's children and a sum over heads.
-//   Selection: a 64-lane bitonic sort on (score desc, id asc) with forced
-//   nodes keyed +inf; expansion and compaction with ballot / ds_permute.
+//   Selection: every candidate's rank on (score desc, id asc), forced
+//   nodes keyed +inf, then one ds_permute; expansion and compaction with
+//   ballot / ds_permute.
 //
 // stage2_kernel: leaf scoring of stage-1 survivors, clustered by retained
 //   level-2 node p. A workgroup stages p's g leaf blocks (g * C keys) in LDS
@@ -112,12 +113,104 @@ struct RouteQuery {
         }
     }
 
+    // Decode, bf16 queries (one query row per head): the same scores as
+    // score_level, with every load of a task issued before its products and
+    // the reductions kept in registers. A task is one 16-column tile of
+    // (candidate, child) columns when a candidate has nch <= 16 children, else
+    // one candidate's nch / 16 tiles; the waves share the tasks.
+    template <typename TS>
+    __device__ __forceinline__ static void score_level_regs(const TS* base, int64_t row_stride, int64_t limit,
+                                                            int nch_log2, int ns, const bf16x8* qa, const int* s_sid,
+                                                            float* s_u)
+    {
+        static_assert(TA == 1, "one query row per head");
+        constexpr int TB = Src<TS>::TERMS;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int col = lane & 15, lg = lane >> 4;
+        const int nch = 1 << nch_log2;
+        const float scale = kLog2e * rsqrtf((float)D);
+        if (nch <= 16) {
+            const int ntasks = (ns * nch + 15) >> 4;
+            for (int task = wave; task < ntasks; task += WAVES) {
+                const int cc = task * 16 + col;  // (candidate, child) column
+                const int j = cc >> nch_log2;
+                const int cand = j < ns ? s_sid[j] : -1;
+                const int64_t row = (int64_t)cand * nch + (cc & (nch - 1));
+                const bool ok = cand >= 0 && row < limit;
+                const TS* ptr = base + (ok ? row : 0) * row_stride + 8 * lg;
+                bf16x8 hi[KS], lo[KS];
+#pragma unroll
+                for (int s = 0; s < KS; ++s) Src<TS>::load(ptr + 32 * s, ok, hi[s], lo[s]);
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    c = mfma(qa[s], hi[s], c);
+                    if constexpr (TB == 2) c = mfma(qa[s], lo[s], c);
+                }
+                // rows 4 lg + i are heads; a candidate's children are nch adjacent lanes
+                float u = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float y = ok ? c[i] * scale : -INFINITY;
+                    const float m = group_max(y, nch);
+                    const float e = ok ? __builtin_amdgcn_exp2f(y - m) : 0.f;
+                    const float sum = group_sum(e, nch);
+                    if (4 * lg + i < G) u += m + __builtin_amdgcn_logf(sum);
+                }
+                u += shfl_xor(u, 16);
+                u += shfl_xor(u, 32);
+                if (lg == 0 && (cc & (nch - 1)) == 0 && j < ns) s_u[j] = u * kLn2;
+            }
+        } else {
+            const int nt = nch >> 4;  // 2 or 4 tiles per candidate
+            for (int task = wave; task < ns; task += WAVES) {
+                const int cand = s_sid[task];
+                bf16x8 hi[4][KS], lo[4][KS];
+                bool ok[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int64_t row = (int64_t)cand * nch + 16 * tt + col;
+                    ok[tt] = tt < nt && row < limit;
+                    const TS* ptr = base + (ok[tt] ? row : 0) * row_stride + 8 * lg;
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) Src<TS>::load(ptr + 32 * s, ok[tt], hi[tt][s], lo[tt][s]);
+                }
+                f32x4 c[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    c[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        c[tt] = mfma(qa[s], hi[tt][s], c[tt]);
+                        if constexpr (TB == 2) c[tt] = mfma(qa[s], lo[tt][s], c[tt]);
+                    }
+                }
+                float u = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float m = -INFINITY;
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) m = fmaxf(m, ok[tt] ? c[tt][i] * scale : -INFINITY);
+                    m = group_max(m, 16);
+                    float sum = 0.f;
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) sum += ok[tt] ? __builtin_amdgcn_exp2f(c[tt][i] * scale - m) : 0.f;
+                    sum = group_sum(sum, 16);
+                    if (4 * lg + i < G) u += m + __builtin_amdgcn_logf(sum);
+                }
+                u += shfl_xor(u, 16);
+                u += shfl_xor(u, 32);
+                if (lane == 0) s_u[task] = u * kLn2;
+            }
+        }
+    }
+
     template <int MODE>
     __device__ static void run(const RouteArgs& a)
     {
         __shared__ int s_sid[64];
         __shared__ float s_u[64];
-        __shared__ float s_zall[WAVES][16 * 65];
+        __shared__ float s_zall[WAVES][R * 65];  // the R MFMA rows in use
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         float* s_z = s_zall[wave];
         const PyrArgs& p = a.p;
@@ -185,18 +278,25 @@ struct RouteQuery {
                 const int rk = rank_below(sm);
                 if (wave == 0 && scored) s_sid[rk] = cid;
                 __syncthreads();
+                constexpr bool regs = MODE == MODE_DECODE && TA == 1;
                 if (l == 1) {
                     const T* kb = (const T*)a.K + ((int64_t)b * p.N_cap * p.H + h) * D;
-                    score_level<T>(kb, (int64_t)p.H * D, n, p.c_log2, ns, qa, s_z, s_sid, s_u);
+                    if constexpr (regs)
+                        score_level_regs<T>(kb, (int64_t)p.H * D, n, p.c_log2, ns, qa, s_sid, s_u);
+                    else
+                        score_level<T>(kb, (int64_t)p.H * D, n, p.c_log2, ns, qa, s_z, s_sid, s_u);
                 } else {
                     const float* lb = p.buf + p.off[l - 1] + ((int64_t)b * p.H + h) * p.M_cap[l - 1] * D;
-                    score_level<float>(lb, D, geo.nodes(n, l - 1), p.g_log2, ns, qa, s_z, s_sid, s_u);
+                    if constexpr (regs)
+                        score_level_regs<float>(lb, D, geo.nodes(n, l - 1), p.g_log2, ns, qa, s_sid, s_u);
+                    else
+                        score_level<float>(lb, D, geo.nodes(n, l - 1), p.g_log2, ns, qa, s_z, s_sid, s_u);
                 }
                 __syncthreads();
                 const float u = scored ? s_u[rk] : 0.f;
                 key = forced ? INFINITY : (scored ? u : -INFINITY);
                 int sid = cid >= 0 ? cid : (0x7fffffff - lane);
-                bitonic_sort(key, sid);
+                rank_sort(key, sid, ballot(cid >= 0));
                 nkept = a.K_top;
                 cid = lane < nkept ? sid : -1;
                 if (lane >= nkept) key = -INFINITY;
@@ -242,7 +342,7 @@ struct RouteQuery {
         } else {
             int id = lane < nkept ? cid : (0x7fffffff - lane);
             float val = lane < nkept ? key : -INFINITY;
-            sort_ids_ascending(id, val);
+            rank_sort_ids(id, val, ballot(lane < nkept));
             const int64_t base = (MODE == MODE_DECODE) ? ((int64_t)b * p.H + h) * a.K_top
                                                        : (((int64_t)b * p.H + h) * a.N + t) * a.K_top;
             if (lane < a.K_top) {
@@ -259,10 +359,15 @@ __global__ __launch_bounds__(64) void route_query_kernel(RouteArgs a)
     RouteQuery<D, T, G, 1>::template run<MODE>(a);
 }
 
+// Decode: one workgroup per (sequence, KV head); kDecodeWaves waves share the
+// scoring of a level's candidate groups (at the leaf level, one group per
+// candidate block), so their loads are in flight together.
+constexpr int kDecodeWaves = 8;
+
 template <int D, typename T, int G>
-__global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a)
+__global__ __launch_bounds__(64 * kDecodeWaves) void route_decode_kernel(RouteArgs a)
 {
-    RouteQuery<D, T, G, 4>::template run<MODE_DECODE>(a);
+    RouteQuery<D, T, G, kDecodeWaves>::template run<MODE_DECODE>(a);
 }
 
 // ---------------------------------------------------------------------------
