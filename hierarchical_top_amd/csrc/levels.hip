@@ -21,7 +21,7 @@
 namespace pisa {
 
 constexpr int kSelThreads = 256;
-constexpr int kSelItemsPerThread = 4;
+constexpr int kSelItemsPerThread = 1;
 constexpr int kLdsBins = 8192;  // cluster bins aggregated in LDS (larger levels use global atomics)
 
 // Eligible existing children of node P of level lp at level lp - 1, for query t.

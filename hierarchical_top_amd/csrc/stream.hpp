@@ -119,18 +119,20 @@ __device__ __forceinline__ void stream_prologue_issue(const StreamPrologue<D, NB
 
 // Wait until this wave's fetch of the current sub-chunk has landed, `later`
 // (wave-uniform, <= NB - 2) sub-chunks having been issued after it.
-template <int D, int NB>
+template <int D, int NB, int K = NB - 2>
 __device__ __forceinline__ void stream_wait(int later)
 {
     constexpr int NI = StreamGeom<D>::NI;
-    static_assert(NB >= 2 && NB <= 4, "ring depth");
-    if constexpr (NB >= 4) {
-        if (later >= 2) { wait_vm<2 * NI>(); return; }
+    static_assert(NB >= 2 && (NB - 2) * NI < 64, "ring depth within the vmcnt range");
+    if constexpr (K <= 0) {
+        wait_vm<0>();
+    } else {
+        if (later >= K) {
+            wait_vm<K * NI>();
+            return;
+        }
+        stream_wait<D, NB, K - 1>(later);
     }
-    if constexpr (NB >= 3) {
-        if (later >= 1) { wait_vm<NI>(); return; }
-    }
-    wait_vm<0>();
 }
 
 // Workgroup barrier after this wave's LDS reads and writes have completed.
