@@ -82,9 +82,17 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
         nA = elig_max + 1 < M_l ? elig_max + 1 : M_l;
     } else {
         const int32_t* kp = a.kept_in + i * K;
+        if (K == KMAX && (KMAX & 3) == 0) {  // 16-byte loads (the list starts 16-byte aligned)
 #pragma unroll
-        for (int s = 0; s < KMAX; ++s)
-            if (s < K) kin[s] = kp[s];
+            for (int v = 0; v < KMAX / 4; ++v) {
+                const int4 x = reinterpret_cast<const int4*>(kp)[v];
+                kin[4 * v] = x.x; kin[4 * v + 1] = x.y; kin[4 * v + 2] = x.z; kin[4 * v + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KMAX; ++s)
+                if (s < K) kin[s] = kp[s];
+        }
 #pragma unroll
         for (int s = 0; s < KMAX; ++s)
             if (kin[s] >= 0) nA += n_children(kin[s], g, M_l, elig_max);
@@ -181,6 +189,27 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
     if (l == 1) {
         int32_t* out = a.idx + i * K;
         float* sc = a.score ? a.score + i * K : nullptr;
+        const bool al16 = (((uintptr_t)a.idx | (uintptr_t)a.score) & 15) == 0;  // the caller's buffers
+        if (K == KMAX && (KMAX & 3) == 0 && al16) {
+#pragma unroll
+            for (int v = 0; v < KMAX / 4; ++v) {
+                int4 x;
+                x.x = 4 * v < nkept ? ids[4 * v] : -1;
+                x.y = 4 * v + 1 < nkept ? ids[4 * v + 1] : -1;
+                x.z = 4 * v + 2 < nkept ? ids[4 * v + 2] : -1;
+                x.w = 4 * v + 3 < nkept ? ids[4 * v + 3] : -1;
+                reinterpret_cast<int4*>(out)[v] = x;
+                if (sc) {
+                    float4 y;
+                    y.x = 4 * v < nkept ? val[4 * v] : -INFINITY;
+                    y.y = 4 * v + 1 < nkept ? val[4 * v + 1] : -INFINITY;
+                    y.z = 4 * v + 2 < nkept ? val[4 * v + 2] : -INFINITY;
+                    y.w = 4 * v + 3 < nkept ? val[4 * v + 3] : -INFINITY;
+                    reinterpret_cast<float4*>(sc)[v] = y;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             if (j < K) {
@@ -193,9 +222,21 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
     }
 
     int32_t* kout = a.kept_out + i * K;
+    if (K == KMAX && (KMAX & 3) == 0) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-        if (j < K) kout[j] = j < nkept ? ids[j] : -1;
+        for (int v = 0; v < KMAX / 4; ++v) {
+            int4 x;
+            x.x = 4 * v < nkept ? ids[4 * v] : -1;
+            x.y = 4 * v + 1 < nkept ? ids[4 * v + 1] : -1;
+            x.z = 4 * v + 2 < nkept ? ids[4 * v + 2] : -1;
+            x.w = 4 * v + 3 < nkept ? ids[4 * v + 3] : -1;
+            reinterpret_cast<int4*>(kout)[v] = x;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < K) kout[j] = j < nkept ? ids[j] : -1;
+    }
     if (!a.counts) return;  // the next level is scored densely: no clusters to count
 
     // next level: is it ranked for this item, and which kept nodes own ranked candidates?
