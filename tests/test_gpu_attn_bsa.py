@@ -48,6 +48,7 @@ def _attn(entry, *args, **kw):
     ("tiny", True, None, True),
     ("tiny", False, None, False),
     ("ragged", True, None, False),
+    ("ragged", True, None, True),  # bf16, every row selects all 63 blocks (clustered: 63 slots per row)
     ("ragged", False, None, False),
     ("c32_b2", True, None, False),
     ("paper_shape", True, 1024, False),
