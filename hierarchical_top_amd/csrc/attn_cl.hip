@@ -21,6 +21,8 @@
 //      K_top partials.
 // A block's keys and values are read once per chunk of up to 256 rows instead
 // of once per row.
+#include <algorithm>
+
 #include "pisa_device.hpp"
 #include "pisa_internal.hpp"
 #include "stream.hpp"
@@ -391,80 +393,85 @@ __global__ __launch_bounds__(FW ? 320 : 256) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-// One wave per (sequence, row, KV head). The slot ids are read across the
-// lanes at once; each lane then merges pairs (head, 8 d) of the G x D outputs,
-// eight slots at a time with their loads in flight together and an online
-// maximum across the groups.
+// Waves loop over (sequence, row, KV head) items with a stride of the grid; a
+// wave reads the next item's slot ids while it merges the current one. Each
+// lane merges pairs (head, 8 d) of the G x D outputs, eight slots at a time
+// with their loads in flight together and an online maximum across the groups.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnClArgs a)
 {
     constexpr int CH = D / 8;
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t total = (int64_t)a.B * a.H_kv * a.N_q;
-    if (item >= total) return;
-    const int64_t r = item % a.N_q;
-    const int64_t bh = item / a.N_q;
-    const int h = (int)(bh % a.H_kv);
-    const int b = (int)(bh / a.H_kv);
+    const int64_t stride = (int64_t)gridDim.x * 4;
     const int G = a.G, K_top = a.K_top;
-    const RowGeom g = row_geom(a, b, r);
-    const int64_t prow = (bh * a.N_q + r) * K_top;  // partial row of slot 0
-    bool vis = false;
-    if (lane < K_top) {
-        const int blk = a.idx[prow + lane];
-        const int64_t k0 = (int64_t)blk * a.C;
-        vis = blk >= 0 && k0 < g.nb && block_end(a, g, k0) > k0;
-    }
-    const uint64_t valid = ballot(vis);  // slots with visible keys (K_top <= 64)
     const f16* po = reinterpret_cast<const f16*>(a.part_o);
     bf16* O = reinterpret_cast<bf16*>(a.O);
-    for (int pair = lane; pair - lane < G * CH; pair += 64) {
-        const bool active = pair < G * CH;
-        const int head = active ? pair / CH : 0, dc = active ? pair % CH : 0;
-        float M = -INFINITY, L = 0.f;
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        // slots in groups of 8: log-sum-exps first, then the 8 rows' loads together
-        for (int k0 = 0; k0 < K_top; k0 += 8) {
-            const uint64_t grp = (valid >> k0) & 0xffull;
-            if (!grp) continue;
-            float lse[8], ex[8];
-            f16x8 x[8];
-            const int kfirst = k0 + __builtin_ctzll(grp);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const bool ok = (grp >> j) & 1;
-                const int64_t row = (prow + (ok ? k0 + j : kfirst)) * G + head;
-                lse[j] = ok ? a.part_lse[2 * row] : -INFINITY;
-                ex[j] = a.part_lse[2 * row + 1];
-                x[j] = *reinterpret_cast<const f16x8*>(po + row * D + 8 * dc);
-            }
-            float Mn = M;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, lse[j]);
-            const float f = __builtin_amdgcn_exp2f(M - Mn);  // M = -inf on the first group: f = 0
-            L *= f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] *= f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float w = __builtin_amdgcn_exp2f(lse[j] - Mn);  // 0 for slots not in the group
-                const float ws = __builtin_ldexpf(w, (int)ex[j]);
-                L += w;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += ws * (float)x[j][i];
-            }
-            M = Mn;
+    int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    int blk_next = (item < total && lane < K_top) ? a.idx[item * K_top + lane] : -1;
+    while (item < total) {
+        const int blk = blk_next;
+        const int64_t next = item + stride;
+        blk_next = (next < total && lane < K_top) ? a.idx[next * K_top + lane] : -1;
+        const int64_t r = item % a.N_q;
+        const int64_t bh = item / a.N_q;
+        const int h = (int)(bh % a.H_kv);
+        const int b = (int)(bh / a.H_kv);
+        const RowGeom g = row_geom(a, b, r);
+        const int64_t prow = item * K_top;  // partial row of slot 0: items are ordered as the index rows
+        bool vis = false;
+        if (lane < K_top) {
+            const int64_t k0 = (int64_t)blk * a.C;
+            vis = blk >= 0 && k0 < g.nb && block_end(a, g, k0) > k0;
         }
-        if (!active) continue;
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        bf16x8 out;
+        const uint64_t valid = ballot(vis);  // slots with visible keys (K_top <= 64)
+        for (int pair = lane; pair - lane < G * CH; pair += 64) {
+            const bool active = pair < G * CH;
+            const int head = active ? pair / CH : 0, dc = active ? pair % CH : 0;
+            float M = -INFINITY, L = 0.f;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 0; k0 < K_top; k0 += 8) {
+                const uint64_t grp = (valid >> k0) & 0xffull;
+                if (!grp) continue;
+                float lse[8], ex[8];
+                f16x8 x[8];
+                const int kfirst = k0 + __builtin_ctzll(grp);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = to_bf16(acc[i] * inv);
-        *reinterpret_cast<bf16x8*>(O + (((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head) * D + 8 * dc) = out;
-        if (a.lse && dc == 0)
-            a.lse[((int64_t)b * a.H_q + (int64_t)h * G + head) * a.N_q + r] =
-                L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+                for (int j = 0; j < 8; ++j) {
+                    const bool ok = (grp >> j) & 1;
+                    const int64_t row = (prow + (ok ? k0 + j : kfirst)) * G + head;
+                    lse[j] = ok ? a.part_lse[2 * row] : -INFINITY;
+                    ex[j] = a.part_lse[2 * row + 1];
+                    x[j] = *reinterpret_cast<const f16x8*>(po + row * D + 8 * dc);
+                }
+                float Mn = M;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, lse[j]);
+                const float f = __builtin_amdgcn_exp2f(M - Mn);  // M = -inf on the first group: f = 0
+                L *= f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] *= f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float w = __builtin_amdgcn_exp2f(lse[j] - Mn);  // 0 for slots not in the group
+                    const float ws = __builtin_ldexpf(w, (int)ex[j]);
+                    L += w;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] += ws * (float)x[j][i];
+                }
+                M = Mn;
+            }
+            if (!active) continue;
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            bf16x8 out;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) out[i] = to_bf16(acc[i] * inv);
+            *reinterpret_cast<bf16x8*>(O + (((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head) * D + 8 * dc) = out;
+            if (a.lse && dc == 0)
+                a.lse[((int64_t)b * a.H_q + (int64_t)h * G + head) * a.N_q + r] =
+                    L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+        }
+        item = next;
     }
 }
 
@@ -546,10 +553,11 @@ hipError_t launch_attn_clustered(AttnClArgs a, int d, char* ws, hipStream_t s)
     const int64_t grid = L.n_items / kLeafQC + L.n_clusters;  // bound on the chunks
     if ((e = (d == 64 ? launch_cl_d<64>(a, grid, s) : launch_cl_d<128>(a, grid, s))) != hipSuccess) return e;
     const int64_t items = (int64_t)a.B * a.H_kv * a.N_q;
+    const int64_t cblocks = std::min<int64_t>((items + 3) / 4, 256 * 8);  // 8 workgroups per CU, grid-stride
     if (d == 64)
-        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)cblocks), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)cblocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
