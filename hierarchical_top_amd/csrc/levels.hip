@@ -38,16 +38,15 @@ __device__ __forceinline__ int64_t n_children(int64_t P, int g, int64_t M_child,
 // leaf's ancestors), deduplicated; returns the count (0 without causal masking).
 __device__ __forceinline__ int forced_nodes(int64_t c, int shl, bool causal, int64_t F[3])
 {
-    if (!causal) return 0;
-    int n = 0;
-    F[n++] = 0;
+    // constant indices only, so that F stays in registers
     const int64_t fc = c >> shl;
-    if (fc != 0) F[n++] = fc;
-    if (c >= 1) {
-        const int64_t fp = (c - 1) >> shl;
-        if (fp != 0 && fp != fc) F[n++] = fp;
-    }
-    return n;
+    const int64_t fp = c >= 1 ? (c - 1) >> shl : 0;
+    const bool hc = fc != 0;
+    const bool hp = c >= 1 && fp != 0 && fp != fc;
+    F[0] = 0;
+    F[1] = hc ? fc : fp;
+    F[2] = fp;
+    return causal ? 1 + (hc ? 1 : 0) + (hp ? 1 : 0) : 0;
 }
 
 __device__ __forceinline__ bool in3(int64_t x, const int64_t F[3], int nF)
@@ -179,7 +178,9 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
                 }
             }
         }
-        for (int k = 0; k < nF; ++k) put((int)F[k], INFINITY);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            if (k < nF) put((int)F[k], INFINITY);
 #pragma unroll
         for (int q = 0; q < KMAX; ++q)
             if (q < R) put(bi[q], bu[q]);
@@ -258,7 +259,8 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
                 const int64_t P = ids[j];
                 const int64_t nc = n_children(P, g, M_c, em_c);
                 int64_t nforced = 0;
-                for (int k = 0; k < nF2; ++k) nforced += (F2[k] >= P * g && F2[k] < P * g + nc) ? 1 : 0;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) nforced += (k < nF2 && F2[k] >= P * g && F2[k] < P * g + nc) ? 1 : 0;
                 if (nc > nforced) {
                     mask |= (uint64_t)1 << j;
                     if (use_lds) {
