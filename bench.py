@@ -12,10 +12,12 @@ summary construction and every selection stage, not the attention).
 `value` is routed queries per second (positions x batch / step time) with
 inputs resident in HBM.
 
-Also reported (field "extra"): route-only time of both routers, the
+Also reported (field "extra"): route-only time of the routers, the
 exhaustive BSA-style selector on the same inputs, the 16K and 64K prefill
-workloads, block-sparse attention at 64K, and decode (32 sequences, 262,144
-cached tokens, 256 appended tokens: append + route microseconds per step).
+workloads, block-sparse attention at 64K, decode (32 sequences, 262,144
+cached tokens, 256 appended tokens: append + route microseconds per step),
+and a sweep of N = 4K .. 256K at the appendix's own selection-benchmark
+shape (32 query / 2 KV heads, d=64, g=2).
 
 Prints ONE JSON line. Only one GPU is used; --gpus above 1 exits with an error.
 """
@@ -339,6 +341,48 @@ def prefill_extra(name, reps, with_attn=False):
     return out
 
 
+PAPER_SWEEP_N = (4096, 8192, 16384, 32768, 65536, 131072, 262144)
+
+
+def paper_sweep(check: bool, sizes=PAPER_SWEEP_N):
+    """Build + route at the appendix's selection-benchmark shape (32 query / 2 KV heads,
+    d=64, C=64, g=2, K_top=8, random bf16 Q and K) for N = 4K .. 256K: every router, the
+    exhaustive BSA-style selector and the build alone, in ms. With check, the longest
+    sequence's level-router selection is compared with the oracle on sampled positions."""
+    out = {}
+    for N in sizes:
+        w = synth.paper_shape(N)
+        log("paper sweep", N)
+        P = Prefill(w)
+        r = {}
+        for mname, mode in MODES.items():
+            r["build_route_ms_" + mname] = time_fn(lambda: P.step(mode), 10 if mname == "levels" else 3)
+        r["build_ms"] = time_fn(lambda: P.pyr.build(P.K, N), 10)
+        r["bsa_ms"] = time_fn(P.bsa, 3)
+        best = min(r["build_route_ms_" + m] for m in MODES)
+        r["routed_queries_per_s"] = N / (best * 1e-3)
+        r["speedup_vs_bsa"] = (r["bsa_ms"] + r["build_ms"]) / best
+        rw = workcount.route_work(w.B, N, w.H_kv, w.G_Q, w.d, w.C, w.g, w.K_top)
+        r["levels_tflops"] = 2 * (rw["upper_mac"] + rw["leaf_mac"]) / (r["build_route_ms_levels"] * 1e-3) / 1e12
+        if check and N == sizes[-1]:
+            import oracle  # test infrastructure: sampled parity of the sweep's longest run
+            P.step(pisa.LEVELS)
+            torch.cuda.synchronize()
+            t = sample_positions(N, w.C, 256)
+            opyr = oracle.Pyramid(P.K_cpu.float().numpy(), N, w.C, w.g)
+            orc = oracle.route(opyr, P.Q_cpu[0, t].float().numpy(), [0] * len(t), t, w.K_top, causal=True,
+                               threads=max(1, min(len(os.sched_getaffinity(0)), 16)))
+            gi = P.idx.cpu().numpy()[0][:, t].transpose(1, 0, 2)
+            same = (gi == orc["idx"]).all(-1)
+            outside = orc["gap"] >= 1e-3
+            r["parity"] = dict(sampled_positions=int(len(t)), items=int(same.size), identical=int(same.sum()),
+                               mismatches_outside_band=int((~same & outside).sum()), band=1e-3)
+        out[str(N)] = r
+        del P
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,6 +479,9 @@ def main():
             extra[name] = prefill_extra(name, reps, with_attn=attn)
         log("extra decode")
         extra["decode"] = decode_bench(256)
+        extra["paper_shape_sweep"] = dict(
+            shape="B=1, H_q=32, H_kv=2, d=64, C=64, g=2, K_top=8, causal, random bf16 Q/K (seed 40)",
+            by_N=paper_sweep(check=not args.no_cpu))
 
     line = {
         "metric": METRIC,

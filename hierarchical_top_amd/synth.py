@@ -11,6 +11,10 @@ from a fixed seed. The workloads below follow that recipe at five shapes:
   decode  32 sequences x 262144-token cache, 32 / 8 heads, d=128, C=64, g=4,
           K_top=8, bf16, no planting, 256 appended tokens
 
+and at the appendix's own selection-benchmark shape (``paper_shape``): batch 1,
+32 query heads sharing 2 KV heads, d=64, C=64, g=2, K_top=8, bf16, no planting,
+at any length N (the appendix sweeps 4K to 256K tokens).
+
 Every tensor is drawn as float32 N(0, 1) from a torch generator seeded per
 workload, in the order Q, K, V, planted ids, then rounded to bf16 with
 round-to-nearest-even (``.to(torch.bfloat16)``) for the bf16 workloads.
@@ -60,6 +64,12 @@ WORKLOADS = {
     "p256k": Workload("p256k", 1, 262144, 16, 4, 128, 64, 4, 8, "bf16", 32, 4, False),
     "decode": Workload("decode", 32, 262144, 32, 8, 128, 64, 4, 8, "bf16", 0, 5, True, 256),
 }
+
+
+def paper_shape(N: int, seed: int = 40) -> Workload:
+    """The appendix B selection-benchmark shape at N tokens (random Q and K)."""
+    return Workload("paper%dk" % (N // 1024) if N % 1024 == 0 else "paper%d" % N,
+                    1, N, 32, 2, 64, 64, 2, 8, "bf16", 0, seed, False)
 
 
 def workload(name: str, **over) -> Workload:

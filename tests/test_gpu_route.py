@@ -38,6 +38,8 @@ CASES = {
     "p16k": custom("p16k"),
     # large enough that the level router scores an upper level sparsely (more than 16 parents)
     "sparse64k": synth.Workload("s64k", 1, 65536, 8, 2, 128, 64, 4, 8, "bf16", 0, 26, False),
+    # the page's benchmark shape at a length whose upper levels are scored sparsely
+    "paper64k": synth.paper_shape(65536, seed=27),
     # ragged length: sparse levels 3 and 2 with tail nodes missing grandchildren, two-head groups
     "ragged_big": synth.Workload("rbig", 1, 70001, 4, 2, 128, 64, 4, 8, "bf16", 0, 25, False),
 }
@@ -107,6 +109,7 @@ def _positions(w, sample):
     ("p16k", 8, True, None),
     ("sparse64k", 8, True, 600),
     ("ragged_big", 8, True, 600),
+    ("paper64k", 8, True, 600),
 ])
 def test_route_matches_oracle(mode, case, K_top, causal, sample):
     w = CASES[case]
