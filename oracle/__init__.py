@@ -58,6 +58,9 @@ def _load():
         lib.orc_route.argtypes = [P, P, P, i64, P, P, P, i32, i64, i64, i32, i32, i32, i32,
                                   i32, i32, i32, P, P, P, P, i32]
         lib.orc_route.restype = i32
+        lib.orc_route_scored.argtypes = [P, P, P, i64, P, P, P, i32, i64, i64, i32, i32, i32, i32,
+                                         i32, i32, i32, i32, P, P, P, P, i32]
+        lib.orc_route_scored.restype = i32
         lib.orc_bsa.argtypes = [P, P, P, i64, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
                                 i32, P, P, P, i32]
         lib.orc_bsa.restype = i32
@@ -67,6 +70,9 @@ def _load():
         lib.orc_score.argtypes = [P, i64, i32, i32, i64, P, P, P, i32, i64, i64, i32, i32, i32,
                                   i32]
         lib.orc_score.restype = dbl
+        lib.orc_score_kind.argtypes = [P, i64, i32, i32, i64, P, P, P, i32, i64, i64, i32, i32,
+                                       i32, i32, i32]
+        lib.orc_score_kind.restype = dbl
         _lib = lib
     return _lib
 
@@ -123,9 +129,14 @@ def _items(item_b, item_t):
             np.ascontiguousarray(item_t, dtype=np.int64))
 
 
+# block scores (section 4.4): PISA's log-sum-exp, PISA-1 (mean), PISA-2 (mean + var / 2)
+SCORE_KINDS = {"lse": 0, "mean": 1, "mean_var": 2}
+
+
 def route(pyr: Pyramid, Qi, item_b, item_t, K_top: int, causal: bool = True,
-          trace: bool = False, threads: int | None = None):
-    """PISA route of queries Qi [n][H_q][d] at positions item_t of sequences item_b.
+          trace: bool = False, threads: int | None = None, score_kind: str = "lse"):
+    """PISA route of queries Qi [n][H_q][d] at positions item_t of sequences item_b,
+    with block score score_kind ("lse", or the PISA-1 / PISA-2 scores "mean", "mean_var").
 
     Returns dict(idx [n][H][K_top] int32, score [n][H][K_top] f64, gap [n][H] f64,
     trace [n][H][L+1][2] int32 or None).
@@ -138,10 +149,10 @@ def route(pyr: Pyramid, Qi, item_b, item_t, K_top: int, causal: bool = True,
     score = np.empty((n, H, K_top), dtype=np.float64)
     gap = np.empty((n, H), dtype=np.float64)
     tr = np.zeros((n, H, pyr.L + 1, 2), dtype=np.int32) if trace else None
-    rc = _load().orc_route(_ptr(Qi), _ptr(b), _ptr(t), n, _ptr(pyr.K), _ptr(pyr.buf),
-                           _ptr(pyr.off), pyr.B, pyr.N_alloc, pyr.N, H, H_q, d, pyr.C, pyr.g,
-                           int(K_top), int(bool(causal)), _ptr(idx), _ptr(score), _ptr(gap),
-                           _ptr(tr), threads or default_threads())
+    rc = _load().orc_route_scored(_ptr(Qi), _ptr(b), _ptr(t), n, _ptr(pyr.K), _ptr(pyr.buf),
+                                  _ptr(pyr.off), pyr.B, pyr.N_alloc, pyr.N, H, H_q, d, pyr.C, pyr.g,
+                                  int(K_top), int(bool(causal)), SCORE_KINDS[score_kind], _ptr(idx),
+                                  _ptr(score), _ptr(gap), _ptr(tr), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle route rejected its arguments")
     return dict(idx=idx, score=score, gap=gap, trace=tr)
@@ -184,9 +195,10 @@ def sparse_attn(Qi, item_b, item_t, K, V, N: int, C: int, sel, causal: bool = Tr
     return dict(out=out, lse=lse)
 
 
-def score(pyr: Pyramid, q, b: int, h: int, l: int, i: int) -> float:
-    """s^(l)_{t,i} (eq 21) of one query head q [d] against node i of level l."""
+def score(pyr: Pyramid, q, b: int, h: int, l: int, i: int, kind: str = "lse") -> float:
+    """s^(l)_{t,i} of one query head q [d] against node i of level l: the LSE of eq 21,
+    or with kind "mean" / "mean_var" the PISA-1 / PISA-2 score of eq 33-34."""
     q = _f32(q)
-    return float(_load().orc_score(_ptr(q), int(b), int(h), int(l), int(i), _ptr(pyr.K),
-                                   _ptr(pyr.buf), _ptr(pyr.off), pyr.B, pyr.N_alloc, pyr.N,
-                                   pyr.H, pyr.d, pyr.C, pyr.g))
+    return float(_load().orc_score_kind(_ptr(q), int(b), int(h), int(l), int(i), _ptr(pyr.K),
+                                        _ptr(pyr.buf), _ptr(pyr.off), pyr.B, pyr.N_alloc, pyr.N,
+                                        pyr.H, pyr.d, pyr.C, pyr.g, SCORE_KINDS[kind]))

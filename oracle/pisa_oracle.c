@@ -119,6 +119,7 @@ typedef struct {
     const double *pyr;      /* levels 1..L, layout above */
     const int64_t *off;
     int B, H, H_q, d, C, g, K_top, causal;
+    int score_kind;         /* 0 PISA (LSE), 1 PISA-1 (mean), 2 PISA-2 (mean + var / 2) */
     int64_t N, N_alloc;
     int64_t M[ORC_MAX_LEVELS + 1];
     int L;
@@ -158,6 +159,33 @@ static double logsumexp(const double *z, int64_t n)
     return m + log(s);
 }
 
+/* Mean of n >= 1 values (section 4.4 eq 33, appendix A.2 eq 43). */
+static double mean_of(const double *z, int64_t n)
+{
+    double s = 0.0;
+    for (int64_t j = 0; j < n; j++) s += z[j];
+    return s / (double)n;
+}
+
+/* Population variance of n >= 1 values about their mean (appendix A.2 eq 44). */
+static double var_of(const double *z, int64_t n)
+{
+    double mu = mean_of(z, n), s = 0.0;
+    for (int64_t j = 0; j < n; j++) s += (z[j] - mu) * (z[j] - mu);
+    return s / (double)n;
+}
+
+/* The block score from the valid logits z[0..n) of one candidate and head:
+ * PISA's log-sum-exp (eq 21 / eq 50), or the truncations of its expansion
+ * about the mean with log m dropped (section 4.4 eq 33-34, appendix A.2
+ * eq 51-52): PISA-1 keeps the mean, PISA-2 the mean plus half the variance. */
+static double reduce_logits(int kind, const double *z, int64_t n)
+{
+    if (kind == 1) return mean_of(z, n);
+    if (kind == 2) return mean_of(z, n) + 0.5 * var_of(z, n);
+    return logsumexp(z, n);
+}
+
 /* ---------------------------------------------------------------------------
  * LSE block score of one candidate for one query head. Section 3.2,
  * "LogSumExp block scoring", eq 21:
@@ -165,6 +193,7 @@ static double logsumexp(const double *z, int64_t n)
  * For l = 1 the children are the raw keys of leaf block i (kbar^(0) = k), so
  * a leaf gets its exact raw-key LSE; for l >= 2 they are the existing level-(l-1)
  * summaries. q points at one query head's d values; h is its KV head.
+ * With score_kind 1 or 2 the same logits are reduced by reduce_logits instead.
  * ------------------------------------------------------------------------- */
 double orc_lse_score(const orc_problem *P, int64_t b, int h, const float *q, int l,
                      int64_t i)
@@ -182,7 +211,7 @@ double orc_lse_score(const orc_problem *P, int64_t b, int h, const float *q, int
         int64_t lo = i * P->g, hi = i * P->g + P->g < P->M[l - 1] ? i * P->g + P->g : P->M[l - 1];
         for (int64_t r = lo; r < hi; r++) z[n++] = dot_fd(q, src + r * P->d, P->d) * scale;
     }
-    return logsumexp(z, n);
+    return reduce_logits(P->score_kind, z, n);
 }
 
 /* Grouped-query sum, section 3.3 eq 22 and appendix A.3 eq 53: the LSE scores
@@ -509,18 +538,33 @@ static int setup(orc_problem *P, const float *Q, const int64_t *item_b, const in
     return 0;
 }
 
+/* Route n_items queries for every KV head with block score score_kind (0 PISA,
+ * 1 PISA-1, 2 PISA-2; the hierarchy, forced set and expansion are the same for
+ * all three, section 4.4). Returns 0, or -1 on bad input. */
+int orc_route_scored(const float *Q, const int64_t *item_b, const int64_t *item_t, int64_t n_items,
+                     const float *K, const double *pyr, const int64_t *off, int B, int64_t N_alloc,
+                     int64_t N, int H, int H_q, int d, int C, int g, int K_top, int causal,
+                     int score_kind, int32_t *idx, double *score, double *gap, int32_t *trace,
+                     int nthreads)
+{
+    orc_problem P;
+    if (score_kind < 0 || score_kind > 2) return -1;
+    if (setup(&P, Q, item_b, item_t, n_items, K, pyr, off, B, N_alloc, N, H, H_q, d, C, g,
+              K_top, causal, nthreads)) return -1;
+    P.score_kind = score_kind;
+    P.idx = idx; P.score = score; P.gap = gap; P.trace = trace;
+    run_pool(&P, 0);
+    return 0;
+}
+
 /* Route n_items queries for every KV head (PISA). Returns 0, or -1 on bad input. */
 int orc_route(const float *Q, const int64_t *item_b, const int64_t *item_t, int64_t n_items,
               const float *K, const double *pyr, const int64_t *off, int B, int64_t N_alloc,
               int64_t N, int H, int H_q, int d, int C, int g, int K_top, int causal,
               int32_t *idx, double *score, double *gap, int32_t *trace, int nthreads)
 {
-    orc_problem P;
-    if (setup(&P, Q, item_b, item_t, n_items, K, pyr, off, B, N_alloc, N, H, H_q, d, C, g,
-              K_top, causal, nthreads)) return -1;
-    P.idx = idx; P.score = score; P.gap = gap; P.trace = trace;
-    run_pool(&P, 0);
-    return 0;
+    return orc_route_scored(Q, item_b, item_t, n_items, K, pyr, off, B, N_alloc, N, H, H_q, d, C,
+                            g, K_top, causal, 0, idx, score, gap, trace, nthreads);
 }
 
 /* Exhaustive BSA-style selection for n_items queries. Returns 0 or -1. */
@@ -552,16 +596,26 @@ int orc_sparse_attn(const float *Q, const int64_t *item_b, const int64_t *item_t
     return 0;
 }
 
-/* One LSE score s^(l)_{t,i} for one query head (eq 21); exposed so tests can
- * check the score definition itself. q: d floats of one query head. */
+/* One block score s^(l)_{t,i} for one query head: kind 0 the LSE of eq 21,
+ * kind 1 / 2 the PISA-1 / PISA-2 scores of eq 33-34; exposed so tests can check
+ * the score definitions themselves. q: d floats of one query head. */
+double orc_score_kind(const float *q, int64_t b, int h, int l, int64_t i, const float *K,
+                      const double *pyr, const int64_t *off, int B, int64_t N_alloc, int64_t N,
+                      int H, int d, int C, int g, int kind)
+{
+    orc_problem P;
+    int64_t zero = 0;
+    if (kind < 0 || kind > 2) return NAN;
+    if (setup(&P, q, &zero, &zero, 0, K, pyr, off, B, N_alloc, N, H, H, d, C, g, 3, 0, 1))
+        return NAN;
+    if (l < 1 || l > P.L || i < 0 || i >= P.M[l]) return NAN;
+    P.score_kind = kind;
+    return orc_lse_score(&P, b, h, q, l, i);
+}
+
 double orc_score(const float *q, int64_t b, int h, int l, int64_t i, const float *K,
                  const double *pyr, const int64_t *off, int B, int64_t N_alloc, int64_t N,
                  int H, int d, int C, int g)
 {
-    orc_problem P;
-    int64_t zero = 0;
-    if (setup(&P, q, &zero, &zero, 0, K, pyr, off, B, N_alloc, N, H, H, d, C, g, 3, 0, 1))
-        return NAN;
-    if (l < 1 || l > P.L || i < 0 || i >= P.M[l]) return NAN;
-    return orc_lse_score(&P, b, h, q, l, i);
+    return orc_score_kind(q, b, h, l, i, K, pyr, off, B, N_alloc, N, H, d, C, g, 0);
 }

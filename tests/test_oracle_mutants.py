@@ -34,6 +34,12 @@ MUTANTS = [
     ("wrong_children", "int64_t lo = I[k] * P->g;", "int64_t lo = I[k] * P->g + 1;"),
     ("transposed_operand", "for (int e = 0; e < d; e++) s += (double)q[e] * k[e];",
      "for (int e = 0; e < d; e++) s += (double)q[e] * k[d - 1 - e];"),
+    ("pisa1_sum_not_mean", "    return s / (double)n;\n}\n\n/* Population", "    return s;\n}\n\n/* Population"),
+    ("pisa2_sample_variance", "s += (z[j] - mu) * (z[j] - mu);\n    return s / (double)n;",
+     "s += (z[j] - mu) * (z[j] - mu);\n    return s / (double)(n > 1 ? n - 1 : 1);"),
+    ("pisa2_whole_variance", "return mean_of(z, n) + 0.5 * var_of(z, n);", "return mean_of(z, n) + var_of(z, n);"),
+    ("pisa1_normalised_lse", "if (kind == 1) return mean_of(z, n);",
+     "if (kind == 1) return logsumexp(z, n) - log((double)n);"),
     ("ascending_scores", "if (x->u > y->u) return -1;\n    if (x->u < y->u) return 1;",
      "if (x->u < y->u) return -1;\n    if (x->u > y->u) return 1;"),
 ]

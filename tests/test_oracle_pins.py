@@ -200,8 +200,15 @@ def test_group_scores_are_sums_of_head_scores():
 # kept whole, so K_top >= M_2 turns PISA into exhaustive leaf LSE selection)
 # --------------------------------------------------------------------------
 
-def exhaustive_lse(K, Q, t, C, Kt, causal=True):
-    """Brute force: score every eligible non-forced leaf by summed raw-key LSE."""
+# numpy's routines for the three block scores of section 4.4 (eq 50-52): np.var is the
+# population variance (ddof=0), as eq 44 defines it
+REDUCERS = {"lse": logsumexp, "mean": np.mean, "mean_var": lambda z: np.mean(z) + 0.5 * np.var(z)}
+
+
+def exhaustive_lse(K, Q, t, C, Kt, causal=True, kind="lse"):
+    """Brute force: score every eligible non-forced leaf by the summed raw-key score
+    (LSE, or the PISA-1 / PISA-2 reductions of the same logits)."""
+    red = REDUCERS[kind]
     N, H, d = K.shape[1], K.shape[2], K.shape[3]
     Hq = Q.shape[1]
     G = Hq // H
@@ -220,7 +227,7 @@ def exhaustive_lse(K, Q, t, C, Kt, causal=True):
             u = []
             for i in S:
                 Kb = K[0, i * C:min(i * C + C, N), h].astype(np.float64)
-                u.append(sum(logsumexp(Kb @ Q[n, h * G + j].astype(np.float64) / math.sqrt(d))
+                u.append(sum(red(Kb @ Q[n, h * G + j].astype(np.float64) / math.sqrt(d))
                              for j in range(G)))
             order = sorted(range(len(S)), key=lambda k: (-u[k], S[k]))
             row.append(sorted(F + [S[k] for k in order[:Kt - len(F)]]))
@@ -248,7 +255,8 @@ def test_reduction_to_exhaustive_on_tiny(Kt):
         assert r["trace"][:, 0, 2:, 1].sum() == 0 and r["trace"][-1, 0, 1].tolist() == [64, 61]
 
 
-def test_reduction_to_exhaustive_grouped_noncausal():
+@pytest.mark.parametrize("kind", ["lse", "mean", "mean_var"])
+def test_reduction_to_exhaustive_grouped_noncausal(kind):
     rng = np.random.default_rng(6)
     N, C, g, d, H, Hq = 200, 8, 4, 8, 2, 4
     K = rng.standard_normal((1, N, H, d)).astype(np.float32)
@@ -256,8 +264,8 @@ def test_reduction_to_exhaustive_grouped_noncausal():
     pyr = oracle.Pyramid(K, N, C, g)
     Kt = pyr.M[2]  # every level above the leaves is kept whole
     t = np.arange(10) * 19
-    r = oracle.route(pyr, Q, [0] * 10, t, Kt, causal=False)
-    want = exhaustive_lse(K, Q, t, C, Kt, causal=False)
+    r = oracle.route(pyr, Q, [0] * 10, t, Kt, causal=False, score_kind=kind)
+    want = exhaustive_lse(K, Q, t, C, Kt, causal=False, kind=kind)
     for n in range(10):
         for h in range(H):
             assert [int(x) for x in r["idx"][n, h] if x >= 0] == want[n][h]
@@ -439,3 +447,102 @@ def test_attention_matches_sdpa(causal):
         emp = empty.permute(1, 0).numpy()
         np.testing.assert_allclose(r["out"][~emp], want[~emp], atol=1e-10)
         assert (r["out"][emp] == 0).all() and np.isneginf(r["lse"][emp]).all()
+
+
+# --------------------------------------------------------------------------
+# PISA-1 / PISA-2 block scores (section 4.4 eq 32-34, appendix A.2 eq 43-52)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N", [64, 56])
+def test_pisa12_closed_forms_on_arithmetic_logits(N):
+    """Keys whose first coordinate is the token index r and a query (8, 0, ..) with
+    d = 64 give the logits z_r = 8 r / sqrt(64) = r. A run of n consecutive integers
+    has mean (first + last) / 2 and population variance (n^2 - 1) / 12; two values a < b
+    have variance (b - a)^2 / 4. Leaves hold C = 16 tokens (the last one 8 when N = 56),
+    g = 2."""
+    d, C, g = 64, 16, 2
+    K = np.zeros((1, N, 1, d), np.float32)
+    K[0, :, 0, 0] = np.arange(N)
+    q = np.zeros(d, np.float32)
+    q[0] = 8.0
+    pyr = oracle.Pyramid(K, N, C, g)
+    leaf_mean = []
+    for i in range(pyr.M[1]):
+        lo, hi = i * C, min(i * C + C, N)
+        n = hi - lo
+        mean, var = (lo + hi - 1) / 2, (n * n - 1) / 12
+        leaf_mean.append(mean)
+        assert oracle.score(pyr, q, 0, 0, 1, i, kind="mean") == pytest.approx(mean, abs=1e-12)
+        assert oracle.score(pyr, q, 0, 0, 1, i, kind="mean_var") == pytest.approx(mean + var / 2, abs=1e-12)
+    # level 2: the logits are the two leaf means (unweighted, eq 14-15)
+    node_mean = []
+    for j in range(pyr.M[2]):
+        a, b = leaf_mean[2 * j], leaf_mean[2 * j + 1]
+        node_mean.append((a + b) / 2)
+        assert oracle.score(pyr, q, 0, 0, 2, j, kind="mean") == pytest.approx((a + b) / 2, abs=1e-12)
+        assert oracle.score(pyr, q, 0, 0, 2, j, kind="mean_var") == pytest.approx(
+            (a + b) / 2 + (b - a) ** 2 / 8, abs=1e-12)
+    a, b = node_mean
+    assert oracle.score(pyr, q, 0, 0, 3, 0, kind="mean_var") == pytest.approx((a + b) / 2 + (b - a) ** 2 / 8,
+                                                                              abs=1e-12)
+
+
+def test_pisa12_are_the_taylor_truncations_of_normalised_lse():
+    """Appendix A.2 eq 45-49: with phi(lam) = LSE(lam z) - log m, phi(0) = 0,
+    phi'(0) = mean and phi''(0) = variance. Scaling the query by lam scales every logit
+    by lam, so PISA-1(lam q) = lam mean and PISA-2(lam q) = lam mean + lam^2 var / 2 must
+    approach phi(lam) to second and third order as lam -> 0."""
+    rng = np.random.default_rng(31)
+    N, C, g, d = 256, 16, 4, 16
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    q = rng.standard_normal(d).astype(np.float32)
+    for l, i, m in ((1, 3, C), (2, 1, g), (3, 0, g)):
+        err1, err2 = [], []
+        for lam in (1 / 16, 1 / 32, 1 / 64):
+            ql = (q * np.float32(lam)).astype(np.float32)  # exact: power-of-two scaling
+            phi = oracle.score(pyr, ql, 0, 0, l, i) - math.log(m)
+            err1.append(phi - oracle.score(pyr, ql, 0, 0, l, i, kind="mean"))
+            err2.append(phi - oracle.score(pyr, ql, 0, 0, l, i, kind="mean_var"))
+        # second order: halving lam quarters the gap (to within its own O(lam) correction)
+        assert err1[0] > 0 and 3.5 < err1[0] / err1[1] < 4.5 and 3.7 < err1[1] / err1[2] < 4.3
+        # third order: halving lam divides the remaining gap by about 8
+        assert abs(err2[1]) < abs(err1[1]) / 10
+        assert 6.5 < err2[0] / err2[1] < 9.5 and 7.2 < err2[1] / err2[2] < 8.8
+
+
+def test_pisa12_jensen_and_variance_bounds():
+    """Eq 40: the mean logit is at most the normalised LSE (equality when the logits are
+    equal); the variance is non-negative, so PISA-2 >= PISA-1."""
+    rng = np.random.default_rng(32)
+    N, C, g, d = 200, 8, 2, 8
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    K[0, 0:C, 0] = K[0, 0, 0]  # leaf 0: identical keys, so identical logits
+    pyr = oracle.Pyramid(K, N, C, g)
+    q = rng.standard_normal(d).astype(np.float32)
+    for l in range(1, pyr.L + 1):
+        for i in range(pyr.M[l]):
+            m = min(C, N - i * C) if l == 1 else min(g, pyr.M[l - 1] - i * g)
+            s0 = oracle.score(pyr, q, 0, 0, l, i) - math.log(m)
+            s1 = oracle.score(pyr, q, 0, 0, l, i, kind="mean")
+            s2 = oracle.score(pyr, q, 0, 0, l, i, kind="mean_var")
+            assert s1 <= s0 + 1e-12 and s1 <= s2
+    assert oracle.score(pyr, q, 0, 0, 1, 0, kind="mean") == pytest.approx(
+        oracle.score(pyr, q, 0, 0, 1, 0) - math.log(C), abs=1e-12)
+    assert oracle.score(pyr, q, 0, 0, 1, 0, kind="mean_var") == oracle.score(pyr, q, 0, 0, 1, 0, kind="mean")
+
+
+@pytest.mark.parametrize("kind", ["mean", "mean_var"])
+def test_pisa12_route_reduces_to_exhaustive_on_tiny(kind):
+    """K_top = 32 at N = 1024, C = 16: every level above the leaves is kept whole, so
+    the route is the exhaustive leaf selection by the summed PISA-1 / PISA-2 scores."""
+    rng = np.random.default_rng(33)
+    N, C, g, d = 1024, 16, 2, 64
+    K = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    Q = rng.standard_normal((N, 2, d)).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    t = np.arange(0, N, 11)
+    r = oracle.route(pyr, Q[t], [0] * len(t), t, 32, causal=True, score_kind=kind)
+    want = exhaustive_lse(K, Q[t], t, C, 32, kind=kind)
+    for n in range(len(t)):
+        assert [int(x) for x in r["idx"][n, 0] if x >= 0] == want[n][0], "t=%d" % t[n]
