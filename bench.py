@@ -77,7 +77,7 @@ class Prefill:
         self.idx = torch.empty(w.B, w.H_kv, w.N, w.K_top, dtype=torch.int32, device="cuda")
         self.bidx = torch.empty_like(self.idx)
 
-    def step(self, mode, stage_events=None):
+    def step(self, mode, stage_events=None, score_kind="lse"):
         """Pyramid build + routing of every position. stage_events: {stage: [(start, stop), ...]}
         armed for this step; returns {stage: number of pairs the step consumed}."""
         w = self.w
@@ -86,7 +86,8 @@ class Prefill:
                 for a, b in pairs:
                     pisa.time_stage(name, a, b)
         self.pyr.build(self.K, w.N)
-        pisa.route_prefill(self.pyr, self.Q, self.K, w.N, w.K_top, mode=mode, workspace=self.ws, out=self.idx)
+        pisa.route_prefill(self.pyr, self.Q, self.K, w.N, w.K_top, mode=mode, workspace=self.ws, out=self.idx,
+                           score_kind=score_kind)
         fired = {}
         if stage_events:
             for name, pairs in stage_events.items():
@@ -458,6 +459,11 @@ def main():
     G = w.H_q // w.H_kv
     bw = workcount.bsa_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.K_top)
     extra["bsa_alg_tflops_one_pass"] = 2 * bw["mac"] / (extra["bsa_ms"] * 1e-3) / 1e12
+
+    # the section 4.4 ablations on the same inputs: PISA-1 (mean) and PISA-2 (mean + var / 2)
+    # block scores in the level router, build + route
+    extra["score_kinds_build_route_ms"] = {k: time_fn(lambda: P.step(pisa.LEVELS, score_kind=k), 10)
+                                           for k in ("lse", "mean", "mean_var")}
 
     # the headline selection is left in P.idx for the parity check below
     P.step(mode)

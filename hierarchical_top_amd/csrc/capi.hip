@@ -329,6 +329,19 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
                                int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group, int32_t mode,
                                int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream)
 {
+    return pisa_route_prefill_scored(p, Q, K, dt, N, H_q, K_top, causal, gqa_group, mode, PISA_SCORE_LSE, idx, score,
+                                     ws, ws_bytes, stream);
+}
+
+pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, const void* K, pisa_dtype dt, int64_t N,
+                                      int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group, int32_t mode,
+                                      int32_t score_kind, int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                                      void* stream)
+{
+    if (score_kind != PISA_SCORE_LSE && score_kind != PISA_SCORE_MEAN && score_kind != PISA_SCORE_MEAN_VAR)
+        return fail(PISA_EINVAL, "score_kind=%d", score_kind);
+    if (score_kind != PISA_SCORE_LSE && mode != PISA_ROUTE_LEVELS)
+        return fail(PISA_EUNSUPPORTED, "PISA-1 / PISA-2 scores need mode PISA_ROUTE_LEVELS");
     pisa_status s = check_pyramid(p);
     if (s != PISA_OK) return s;
     if (N < 1) return fail(PISA_EINVAL, "N=%lld < 1", (long long)N);
@@ -347,6 +360,7 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
     r.p = pyr_args(p);
     r.Q = Q; r.K = K; r.N = N; r.seqlen = nullptr;
     r.H_q = H_q; r.G = gqa_group; r.K_top = K_top; r.causal = causal ? 1 : 0;
+    r.score_kind = score_kind;
     r.idx = idx; r.score = score;
     const int dti = dt == PISA_F32 ? 0 : 1;
     hipStream_t st = (hipStream_t)stream;

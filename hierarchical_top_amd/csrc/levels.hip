@@ -598,6 +598,7 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
             da.par_span_log2 = p.c_log2 + l * p.g_log2;
             da.M_par = nodes_n(N, p.c_log2, p.g_log2, l + 1);
             da.kept = a.kept[cur];
+            da.sk = r.score_kind;
             da.u = a.u;
             stage_mark(PISA_STAGE_UPPER, false, s);
             if ((err = launch_dense(da, dtype, d, s)) != hipSuccess) return err;
@@ -680,6 +681,7 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         sc2.xcd = leaf ? 0 : 1;
         sc2.offsets = a.offsets; sc2.chunk_off = a.chunk_off; sc2.chunk_cl = a.chunk_cl; sc2.entries = a.entries;
         sc2.u = a.u;
+        sc2.sk = r.score_kind;
         int64_t grid = ((int64_t)BH * N * r.K_top + qc - 1) / qc + n_clusters;  // bound on the chunks
         if (reg_rows) grid = (grid + kRegWaves - 1) / kRegWaves;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, false, s);

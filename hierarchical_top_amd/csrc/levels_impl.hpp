@@ -109,9 +109,58 @@ __device__ __forceinline__ float lse2(const float* z, bool exists)
     return l2;
 }
 
+// Block score of one candidate and query head from its logits in base-2
+// units (z log2(e), rows that do not exist = -inf), returned in base-2 units
+// (the caller multiplies by ln 2). SK selects the score (section 4.4, appendix
+// A.2): 0 = log-sum-exp (PISA, eq 21); 1 = the mean of the valid logits
+// (PISA-1, eq 33); 2 = that mean plus half their population variance
+// (PISA-2, eq 34), the variance taken about the mean in a second pass. The
+// variance of base-2 logits is ln 2^-2 times the natural one, hence the ln 2
+// factor on it. XMASK as in lse2f: the candidate's rows span those lanes.
+template <int SK, int N, int XMASK, typename F>
+__device__ __forceinline__ float block_score2f(F zf, bool exists)
+{
+    if constexpr (SK == 0) {
+        return lse2f<N, XMASK>(zf, exists);
+    } else {
+        float s = 0.f, c = 0.f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float z = zf(i);
+            const bool v = z > -INFINITY;
+            s += v ? z : 0.f;
+            c += v ? 1.f : 0.f;
+        }
+        if constexpr (XMASK & 1) { s = add_xor16(s); c = add_xor16(c); }
+        if constexpr (XMASK & 2) { s = add_xor32(s); c = add_xor32(c); }
+        const float mu = c > 0.f ? s / c : 0.f;
+        if constexpr (SK == 1) {
+            return c > 0.f ? mu : -INFINITY;
+        } else {
+            float q = 0.f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const float z = zf(i);
+                const float dz = z - mu;
+                q += z > -INFINITY ? dz * dz : 0.f;
+            }
+            if constexpr (XMASK & 1) q = add_xor16(q);
+            if constexpr (XMASK & 2) q = add_xor32(q);
+            return c > 0.f ? mu + (0.5f * kLn2) * (q / c) : -INFINITY;
+        }
+    }
+}
+
+template <int SK, int N, int XMASK>
+__device__ __forceinline__ float block_score2(const float* z, bool exists)
+{
+    if constexpr (SK == 0) return lse2<N, XMASK>(z, exists);
+    else return block_score2f<SK, N, XMASK>([&](int i) { return z[i]; }, exists);
+}
+
 // RC: rows per candidate (g for summary rows, C for key rows), a compile-time
 // constant in {2, 4, 8, 16, 32, 64}. WAVES: waves per workgroup.
-template <int D, typename T, typename TS, int RC, int WAVES>
+template <int D, typename T, typename TS, int RC, int WAVES, int SK>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(ScoreArgs a)
 {
     constexpr int TA = Src<T>::TERMS;   // query terms
@@ -225,7 +274,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
                         const float zz = acc[rt][qt][i] * scale;
                         return (tail && rt * 16 + 4 * lg + i >= lim) ? -INFINITY : zz;
                     };
-                    float l2 = lse2f<TPC * 4, 3>(zf, true);
+                    float l2 = block_score2f<SK, TPC * 4, 3>(zf, true);
                     l2 = sum_adjacent(l2, G);  // heads are adjacent columns
                     if (has[qt] && writer_col) up[qt][j] = l2 * kLn2;
                 }
@@ -272,7 +321,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
                     for (int k = 0; k < CPL; ++k) {
                         const int rfirst = rt * 16 + 4 * lg + k * RPL;  // first row of this candidate part
                         const bool exists = rfirst < lim_rows;
-                        float l2 = lse2<RPL, RC == 8 ? 1 : 0>(z + k * RPL, exists);
+                        float l2 = block_score2<SK, RPL, RC == 8 ? 1 : 0>(z + k * RPL, exists);
                         l2 = sum_adjacent(l2, G);
                         const int j = rfirst / RC;  // candidate (child of P)
                         const bool owner = RC == 8 ? (lg & 1) == 0 : true;
@@ -320,7 +369,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
 // one wave per chunk of kRegChunk entries, no LDS and no workgroup barrier.
 // The wave loads P's rows (fp32 summaries, as two bf16 terms) straight into
 // its A operand registers; RC = g rows per candidate.
-template <int D, typename T, int RC>
+template <int D, typename T, int RC, int SK>
 __global__ __launch_bounds__(64 * kRegWaves) void score_reg_kernel(ScoreArgs a)
 {
     constexpr int TA = Src<T>::TERMS;
@@ -427,7 +476,7 @@ __global__ __launch_bounds__(64 * kRegWaves) void score_reg_kernel(ScoreArgs a)
             for (int k = 0; k < CPL; ++k) {
                 const int rfirst = 4 * lg + k * RPL;
                 const bool exists = rfirst < lim_rows;
-                float l2 = lse2<RPL, 0>(z + k * RPL, exists);
+                float l2 = block_score2<SK, RPL, 0>(z + k * RPL, exists);
                 l2 = sum_adjacent(l2, G);
                 if (has[qt] && head == 0 && term == 0 && exists) up[qt][rfirst / RC] = l2 * kLn2;
             }
@@ -459,7 +508,7 @@ __global__ __launch_bounds__(64 * kRegWaves) void score_reg_kernel(ScoreArgs a)
 constexpr int kDenseBatch = 4;
 constexpr int kDenseQW = 64;  // queries per workgroup (at most)
 
-template <int D, typename T, int GB>
+template <int D, typename T, int GB, int SK>
 __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
 {
     constexpr int TA = Src<T>::TERMS;
@@ -565,7 +614,7 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
                 for (int kk = 0; kk < CPL; ++kk) {
                     const int r0 = rfirst + kk * GB;  // first row of the candidate
                     const bool exists = r0 < nrows && r0 < a.rows_limit;
-                    float l2 = lse2<GB, 0>(z + kk * GB, exists);
+                    float l2 = block_score2<SK, GB, 0>(z + kk * GB, exists);
                     l2 = sum_adjacent(l2, G);
                     const int j = (r0 % RP) / GB;  // candidate = child j of P
                     if (qok[ct] && head == 0 && term == 0 && exists && slot != 0xFF)
@@ -615,7 +664,7 @@ __device__ __forceinline__ void stream_write_scores(const StreamLds& L, float* u
 // entries x G heads per tile). Per (query column, candidate) the C scores are
 // reduced to log2-sum-exp in registers and across the 4 lane groups, the G
 // heads summed with DPP, and the natural-log score kept in LDS.
-template <int D, int C, int NB>
+template <int D, int C, int NB, int SK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 3 : 4))) void leaf_kernel(ScoreArgs a)
 {
     constexpr int KS = D / 32;
@@ -712,9 +761,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 3
                 }
                 float l2;
                 if (lim == C) {
-                    l2 = lse2f<TPC * 4, 3>([&](int x) { return acc[x >> 2][x & 3] * scale; }, true);
+                    l2 = block_score2f<SK, TPC * 4, 3>([&](int x) { return acc[x >> 2][x & 3] * scale; }, true);
                 } else {  // the tail block of the sequence: rows past its end drop out
-                    l2 = lse2f<TPC * 4, 3>(
+                    l2 = block_score2f<SK, TPC * 4, 3>(
                         [&](int x) {
                             const int rt = x >> 2, i = x & 3;
                             return rt * 16 + 4 * lg + i < lim ? acc[rt][i] * scale : -INFINITY;
@@ -739,7 +788,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 3
 // 4 / RC whole candidates, so a lane reduces its candidates without crossing
 // lanes; the G heads of a query sit in adjacent lanes and are summed with DPP.
 // RC = g rows per candidate.
-template <int D, int RC, int NB>
+template <int D, int RC, int NB, int SK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void upper_kernel(ScoreArgs a)
 {
     static_assert(RC == 2 || RC == 4, "g in {2, 4}");
@@ -833,7 +882,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void u
         for (int k = 0; k < CPL; ++k) {
             const int rfirst = 4 * lg + k * RC;
             const bool exists = rfirst < lim_rows;
-            float l2 = lse2<RC, 0>(z + k * RC, exists);
+            float l2 = block_score2<SK, RC, 0>(z + k * RC, exists);
             l2 = sum_adjacent(l2, G);
             if (head == 0 && exists && el < nsub) L.u[(base + el) * 4 + rfirst / RC] = l2 * kLn2;
         }

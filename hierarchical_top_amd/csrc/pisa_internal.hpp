@@ -27,6 +27,7 @@ struct RouteArgs {
     int64_t N;            // prefill sequence length (unused for decode)
     const int64_t* seqlen;  // decode: per-sequence length; null for prefill
     int H_q, G, K_top, causal;
+    int score_kind;       // level-synchronous router: 0 LSE, 1 mean (PISA-1), 2 mean + var / 2 (PISA-2)
     int32_t* idx;         // fused / decode output
     float* score;         // nullable
     // stage 1 outputs
@@ -155,6 +156,7 @@ struct ScoreArgs {
     int64_t M_bins;           // nodes of level l+1 (cluster keys)
     int64_t BH;               // B * H
     int xcd;                  // 1: give each XCD a contiguous range of chunks
+    int sk;                   // block score: 0 LSE, 1 mean (PISA-1), 2 mean + var / 2 (PISA-2)
     const int32_t* offsets;   // [n_clusters + 1]
     const int32_t* chunk_off; // [n_clusters + 1]
     const int32_t* chunk_cl;  // [chunks] cluster of each chunk
@@ -180,6 +182,7 @@ struct DenseArgs {
     int64_t rows_limit;       // level l-1 nodes that exist
     int par_span_log2;        // log2 of the tokens spanned by a level-(l+1) node
     int64_t M_par;            // level l+1 nodes that exist
+    int sk;                   // block score, as in ScoreArgs
     const int32_t* kept;      // [items][K_top] kept nodes of level l+1
     float* u;                 // [items][K_top * g]
 };

@@ -19,6 +19,8 @@ LIB_PATH = Path(__file__).resolve().parent / "libpisa.so"
 MAX_LEVELS = 32
 F32, BF16 = 0, 1
 TWO_STAGE, FUSED, LEVELS = 0, 1, 2
+# block scores (pisa_score_kind): PISA's LSE, PISA-1 (mean), PISA-2 (mean + var / 2)
+SCORE_KINDS = {"lse": 0, "mean": 1, "mean_var": 2}
 
 c_i32, c_i64, c_p, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -58,6 +60,8 @@ def lib():
             "pisa_route_prefill_workspace": [P, c_i64, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)],
             "pisa_route_prefill": [P, c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p,
                                    c_size, c_p],
+            "pisa_route_prefill_scored": [P, c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_p,
+                                          c_p, c_p, c_size, c_p],
             "pisa_route_decode": [P, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_sparse_attn": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p,
                                  c_i32, c_i32, c_p, c_p, c_p, c_p],
@@ -84,7 +88,7 @@ def lib():
 
 
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
-           "pisa_route_prefill", "pisa_route_decode", "pisa_sparse_attn", "pisa_sparse_attn_workspace",
+           "pisa_route_prefill", "pisa_route_prefill_scored", "pisa_route_decode", "pisa_sparse_attn", "pisa_sparse_attn_workspace",
            "pisa_sparse_attn_clustered", "pisa_bsa_select", "pisa_time_stage",
            "pisa_time_stage_pending",
            "pisa_status_str", "pisa_last_error", "pisa_abi_version"]
@@ -164,8 +168,12 @@ def route_workspace_bytes(pyr: Pyramid, N: int, H_q: int, K_top: int, mode: int 
 
 def route_prefill(pyr: Pyramid, Q: torch.Tensor, K: torch.Tensor, N: int, K_top: int, causal: bool = True,
                   mode: int = TWO_STAGE, with_score: bool = False, workspace: torch.Tensor | None = None,
-                  out: torch.Tensor | None = None, score_out: torch.Tensor | None = None):
-    """Route every position of Q [B][N][H_q][d]; returns idx [B][H_kv][N][K_top] (and scores)."""
+                  out: torch.Tensor | None = None, score_out: torch.Tensor | None = None,
+                  score_kind: str = "lse"):
+    """Route every position of Q [B][N][H_q][d]; returns idx [B][H_kv][N][K_top] (and scores).
+
+    score_kind: "lse" (PISA), "mean" (PISA-1) or "mean_var" (PISA-2); the last two
+    run on the level-synchronous router only."""
     _dev(Q, K)
     B, Nq, H_q, d = Q.shape
     assert Nq == N and K.dtype == Q.dtype
@@ -178,9 +186,9 @@ def route_prefill(pyr: Pyramid, Q: torch.Tensor, K: torch.Tensor, N: int, K_top:
     ws = workspace
     if need and (ws is None or ws.numel() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().pisa_route_prefill(ctypes.byref(pyr.desc), _ptr(Q), _ptr(K), _dt(Q), N, H_q, K_top,
-                                    1 if causal else 0, H_q // pyr.H_kv, mode, _ptr(idx), _ptr(score),
-                                    _ptr(ws) if need else None, need, _stream()))
+    _check(lib().pisa_route_prefill_scored(ctypes.byref(pyr.desc), _ptr(Q), _ptr(K), _dt(Q), N, H_q, K_top,
+                                           1 if causal else 0, H_q // pyr.H_kv, mode, SCORE_KINDS[score_kind],
+                                           _ptr(idx), _ptr(score), _ptr(ws) if need else None, need, _stream()))
     return (idx, score) if with_score else idx
 
 

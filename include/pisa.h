@@ -150,6 +150,36 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
                                float* score, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Block scores (section 4.4 eq 33-34, appendix A.2). PISA scores a candidate
+ * by the log-sum-exp of its m valid child logits z_1..z_m (eq 21). Expanding
+ * that LSE about the mean zbar gives log m + zbar + Var(z) / 2 + ...;
+ * dropping log m and truncating after the first or the second term gives the
+ * two ablations of section 4.4, which share PISA's hierarchy, forced set,
+ * expansion rule and grouped-query sum (eq 22) and change only the score:
+ *   PISA_SCORE_MEAN     (PISA-1): s = zbar = (1/m) sum_j z_j
+ *   PISA_SCORE_MEAN_VAR (PISA-2): s = zbar + (1/(2m)) sum_j (z_j - zbar)^2
+ * with z_j = q . kbar_j / sqrt(d) over the existing children (raw keys for a
+ * leaf, only the keys present in a partial leaf).
+ */
+typedef enum pisa_score_kind {
+    PISA_SCORE_LSE = 0,
+    PISA_SCORE_MEAN = 1,
+    PISA_SCORE_MEAN_VAR = 2
+} pisa_score_kind;
+
+/* pisa_route_prefill with the block score chosen by score_kind (a
+ * pisa_score_kind); pisa_route_prefill is this call with PISA_SCORE_LSE.
+ * Score outputs hold the chosen score. PISA_SCORE_MEAN and
+ * PISA_SCORE_MEAN_VAR need mode PISA_ROUTE_LEVELS (PISA_EUNSUPPORTED
+ * otherwise); an unknown score_kind is PISA_EINVAL. Everything else as in
+ * pisa_route_prefill. */
+pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, const void* K,
+                                      pisa_dtype dt, int64_t N, int32_t H_q, int32_t K_top,
+                                      int32_t causal, int32_t gqa_group, int32_t mode,
+                                      int32_t score_kind, int32_t* idx, float* score, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/*
  * Decode routing (section 3.3, "Decoding"): the single-program selector that
  * continues from the top level down to the leaves, for the newest token of
  * each sequence (position seqlen[b] - 1, sequence length seqlen[b]), causal,

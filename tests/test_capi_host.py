@@ -121,6 +121,24 @@ def test_route_prefill_validation(lib):
     assert m.value == 0
 
 
+def test_route_prefill_scored_validation(lib):
+    desc = fake_pyramid(lib)
+
+    def scored(kind, mode=pisa.LEVELS, K_top=8):
+        return lib.pisa_route_prefill_scored(ctypes.byref(desc), FAKE, FAKE, pisa.BF16, 4096, 16, K_top, 1, 4, mode,
+                                             kind, FAKE, None, None, 0, None)
+
+    assert scored(3) == EINVAL
+    assert scored(-1) == EINVAL
+    # PISA-1 / PISA-2 scores run on the level-synchronous router only
+    assert scored(pisa.SCORE_KINDS["mean"], mode=pisa.TWO_STAGE) == EUNSUPPORTED
+    assert scored(pisa.SCORE_KINDS["mean_var"], mode=pisa.FUSED) == EUNSUPPORTED
+    # past the score checks, the usual validation applies: no workspace was given
+    for kind in (0, 1, 2):
+        assert scored(kind) == ENOSPACE
+        assert scored(kind, K_top=2) == EINVAL
+
+
 def test_descriptor_must_come_from_plan(lib):
     desc = fake_pyramid(lib)
     desc.off[2] += 64
