@@ -117,17 +117,28 @@ def time_fn(fn, reps, warm=2):
     return a.elapsed_time(b) / reps
 
 
-def source_hash() -> str:
+# the sources each counted kernel is compiled from (its file, the headers it includes and
+# the host code that launches it): a counter record stays valid while these are unchanged
+_COMMON_SRC = ("pisa_device.hpp", "pisa_internal.hpp", "capi.hip")
+STAGE_SOURCES = {
+    "build": ("pyramid.hip",),
+    "leaf": ("levels.hip", "levels_impl.hpp", "levels_bf16.hip", "stream.hpp"),
+    "route_fused": ("route.hip", "route_impl.hpp", "route_bf16.hip"),
+}
+
+
+def source_hash(stage: str) -> str:
     h = hashlib.sha256()
-    for p in sorted((ROOT / "hierarchical_top_amd" / "csrc").glob("*")):
-        h.update(p.name.encode())
+    for name in sorted(_COMMON_SRC + STAGE_SOURCES[stage]):
+        p = ROOT / "hierarchical_top_amd" / "csrc" / name
+        h.update(name.encode())
         h.update(p.read_bytes())
     return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload: str):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources (else None)."""
+    """HBM traffic per launch of stage `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on that kernel's current sources (else None)."""
     f = ROOT / "profiles" / "traffic.json"
     if not f.exists():
         return None
@@ -135,7 +146,7 @@ def load_traffic(kernel: str, workload: str):
         rec = json.loads(f.read_text()).get("%s/%s" % (workload, kernel))
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_hash") != source_hash():
+    if not rec or kernel not in STAGE_SOURCES or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -212,7 +223,7 @@ def traffic_from_counters(fetch_dir, write_dir, workload="p256k"):
             continue
         recs["%s/%s" % (workload, stage)] = dict(
             kernel=frag, bytes_per_launch=fb * kf + wb * kw, fetch_bytes=fb * kf, write_bytes=wb * kw,
-            dispatches=[nf, nw], scale=dict(fetch=kf, write=kw), source_hash=source_hash())
+            dispatches=[nf, nw], scale=dict(fetch=kf, write=kw), source_hash=source_hash(stage))
     out_file.write_text(json.dumps(recs, indent=1, sort_keys=True) + "\n")
     return recs
 
@@ -461,9 +472,11 @@ def main():
     extra["bsa_alg_tflops_one_pass"] = 2 * bw["mac"] / (extra["bsa_ms"] * 1e-3) / 1e12
 
     # the section 4.4 ablations on the same inputs: PISA-1 (mean) and PISA-2 (mean + var / 2)
-    # block scores in the level router, build + route
-    extra["score_kinds_build_route_ms"] = {k: time_fn(lambda: P.step(pisa.LEVELS, score_kind=k), 10)
-                                           for k in ("lse", "mean", "mean_var")}
+    # block scores in the level router, build + route (not under --quick, whose kernel trace and
+    # counters must hold the headline's kernels only)
+    if not args.quick:
+        extra["score_kinds_build_route_ms"] = {k: time_fn(lambda: P.step(pisa.LEVELS, score_kind=k), 10)
+                                               for k in ("lse", "mean", "mean_var")}
 
     # the headline selection is left in P.idx for the parity check below
     P.step(mode)

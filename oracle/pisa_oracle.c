@@ -128,6 +128,10 @@ typedef struct {
     double *score;          /* [n_items][H][K_top] */
     double *gap;            /* [n_items][H] (may be NULL) */
     int32_t *trace;         /* [n_items][H][L+1][2]: |A| after filter, #scored (may be NULL) */
+    /* attention backward */
+    const float *dO;        /* [n_items][H_q][d] gradient of the loss w.r.t. the output */
+    double *dQ;             /* [n_items][H_q][d] */
+    double *dK, *dV;        /* [B][N_alloc][H][d], accumulated */
     const int32_t *sel;     /* attention: selected blocks [n_items][H][K_top] */
     int sel_k;
     double *out;            /* attention: [n_items][H_q][d] */
@@ -477,11 +481,87 @@ static void attn_one(const orc_problem *P, int64_t item, int hq)
 }
 
 /* ---------------------------------------------------------------------------
+ * Backward of block-sparse attention (section 3.1 eq 6; section 3.3: during
+ * training the gradients flow through attention on the selected entries only,
+ * the selection itself is not differentiated). For one query head with token
+ * set T (as in attn_one), z_j = q . k_j / sqrt(d), p = softmax(z) over T,
+ * o = sum_j p_j v_j and an upstream gradient dO of o:
+ *   dv_j += p_j dO                          (o is linear in v)
+ *   dp_j  = dO . v_j
+ *   dz_j  = p_j (dp_j - sum_{k in T} p_k dp_k)   (Jacobian of the softmax)
+ *   dq   += sum_j dz_j k_j / sqrt(d)
+ *   dk_j += dz_j q / sqrt(d)
+ * Every (item, query head) of KV head h of sequence b adds into the same dK,
+ * dV rows, so one task owns one (b, h) and visits its items in increasing
+ * order and the G_Q query heads in increasing order.
+ * ------------------------------------------------------------------------- */
+static void attn_bwd_one(const orc_problem *P, int64_t item, int hq)
+{
+    int G = P->H_q / P->H;
+    int h = hq / G;
+    int64_t t = P->item_t[item], b = P->item_b[item];
+    const float *q = P->Q + (item * P->H_q + hq) * P->d;
+    const float *dO = P->dO + (item * P->H_q + hq) * P->d;
+    const int32_t *sel = P->sel + (item * P->H + h) * (int64_t)P->sel_k;
+    double scale = 1.0 / sqrt((double)P->d);
+    int64_t cap = (int64_t)P->sel_k * P->C;
+    double *z = malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+    double *dp = malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+    int64_t *tok = malloc(sizeof(int64_t) * (size_t)(cap > 0 ? cap : 1));
+    int64_t n = 0;
+    for (int k = 0; k < P->sel_k; k++) {
+        int64_t i = sel[k];
+        if (i < 0) continue;
+        int64_t lo = i * P->C, hi = i * P->C + P->C < P->N ? i * P->C + P->C : P->N;
+        for (int64_t j = lo; j < hi; j++) {
+            if (P->causal && t < j) continue;  /* future token */
+            tok[n] = j;
+            z[n] = dot_ff(q, P->K + ((b * P->N_alloc + j) * P->H + h) * (int64_t)P->d, P->d) * scale;
+            n++;
+        }
+    }
+    double *dq = P->dQ + (item * P->H_q + hq) * P->d;
+    for (int e = 0; e < P->d; e++) dq[e] = 0.0;
+    if (n > 0) {
+        double lz = logsumexp(z, n);
+        double pdp = 0.0;  /* sum_k p_k dp_k */
+        for (int64_t k = 0; k < n; k++) {
+            const float *v = P->V + ((b * P->N_alloc + tok[k]) * P->H + h) * (int64_t)P->d;
+            dp[k] = dot_ff(dO, v, P->d);
+            pdp += exp(z[k] - lz) * dp[k];
+        }
+        for (int64_t k = 0; k < n; k++) {
+            double p = exp(z[k] - lz);
+            double dz = p * (dp[k] - pdp);
+            int64_t row = ((b * P->N_alloc + tok[k]) * P->H + h) * (int64_t)P->d;
+            const float *kk = P->K + row;
+            for (int e = 0; e < P->d; e++) {
+                P->dV[row + e] += p * (double)dO[e];
+                P->dK[row + e] += dz * scale * (double)q[e];
+                dq[e] += dz * scale * (double)kk[e];
+            }
+        }
+    }
+    free(z);
+    free(dp);
+    free(tok);
+}
+
+static void attn_bwd_group(const orc_problem *P, int64_t b, int h)
+{
+    int G = P->H_q / P->H;
+    for (int64_t item = 0; item < P->n_items; item++) {
+        if (P->item_b[item] != b) continue;
+        for (int hq = h * G; hq < h * G + G; hq++) attn_bwd_one(P, item, hq);
+    }
+}
+
+/* ---------------------------------------------------------------------------
  * Thread pool: task k of n is handled by thread k % nthreads.
  * ------------------------------------------------------------------------- */
 typedef struct {
     const orc_problem *P;
-    int which;   /* 0 route, 1 bsa, 2 attention */
+    int which;   /* 0 route, 1 bsa, 2 attention, 3 attention backward */
     int tid;
 } worker_arg;
 
@@ -489,6 +569,11 @@ static void *worker(void *p)
 {
     worker_arg *w = p;
     const orc_problem *P = w->P;
+    if (w->which == 3) {  /* attention backward: one task per (sequence, KV head) */
+        for (int64_t k = w->tid; k < (int64_t)P->B * P->H; k += P->nthreads)
+            attn_bwd_group(P, k / P->H, (int)(k % P->H));
+        return NULL;
+    }
     int per = w->which == 2 ? P->H_q : P->H;
     int64_t n = P->n_items * per;
     for (int64_t k = w->tid; k < n; k += P->nthreads) {
@@ -593,6 +678,29 @@ int orc_sparse_attn(const float *Q, const int64_t *item_b, const int64_t *item_t
               3, 0, nthreads)) return -1;
     P.V = V; P.sel = sel; P.sel_k = sel_k; P.causal = causal; P.out = out; P.lse = lse;
     run_pool(&P, 2);
+    return 0;
+}
+
+/* Backward of block-sparse attention for n_items queries over sel [n_items][H][sel_k],
+ * given dO [n_items][H_q][d]. Writes dQ [n_items][H_q][d]; dK and dV
+ * [B][N_alloc][H][d] are set to zero and then accumulate every item's part. */
+int orc_sparse_attn_bwd(const float *Q, const int64_t *item_b, const int64_t *item_t,
+                        int64_t n_items, const float *K, const float *V, const float *dO, int B,
+                        int64_t N_alloc, int64_t N, int H, int H_q, int d, int C,
+                        const int32_t *sel, int sel_k, int causal, double *dQ, double *dK,
+                        double *dV, int nthreads)
+{
+    orc_problem P;
+    if (setup(&P, Q, item_b, item_t, n_items, K, NULL, NULL, B, N_alloc, N, H, H_q, d, C, 2,
+              3, 0, nthreads)) return -1;
+    for (int64_t k = 0; k < n_items; k++)
+        if (item_b[k] < 0 || item_b[k] >= B) return -1;
+    P.V = V; P.sel = sel; P.sel_k = sel_k; P.causal = causal;
+    P.dO = dO; P.dQ = dQ; P.dK = dK; P.dV = dV;
+    size_t kv = (size_t)B * (size_t)N_alloc * (size_t)H * (size_t)d;
+    memset(dK, 0, kv * sizeof(double));
+    memset(dV, 0, kv * sizeof(double));
+    run_pool(&P, 3);
     return 0;
 }
 

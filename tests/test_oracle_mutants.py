@@ -40,6 +40,10 @@ MUTANTS = [
     ("pisa2_whole_variance", "return mean_of(z, n) + 0.5 * var_of(z, n);", "return mean_of(z, n) + var_of(z, n);"),
     ("pisa1_normalised_lse", "if (kind == 1) return mean_of(z, n);",
      "if (kind == 1) return logsumexp(z, n) - log((double)n);"),
+    ("bwd_no_centering", "double dz = p * (dp[k] - pdp);", "double dz = p * dp[k];"),
+    ("bwd_dk_unscaled", "P->dK[row + e] += dz * scale * (double)q[e];", "P->dK[row + e] += dz * (double)q[e];"),
+    ("bwd_dv_unnormalised", "P->dV[row + e] += p * (double)dO[e];", "P->dV[row + e] += exp(z[k]) * (double)dO[e];"),
+    ("bwd_mask_self", "if (P->causal && t < j) continue;", "if (P->causal && t <= j) continue;"),
     ("ascending_scores", "if (x->u > y->u) return -1;\n    if (x->u < y->u) return 1;",
      "if (x->u < y->u) return -1;\n    if (x->u > y->u) return 1;"),
 ]

@@ -546,3 +546,101 @@ def test_pisa12_route_reduces_to_exhaustive_on_tiny(kind):
     want = exhaustive_lse(K, Q[t], t, C, 32, kind=kind)
     for n in range(len(t)):
         assert [int(x) for x in r["idx"][n, 0] if x >= 0] == want[n][0], "t=%d" % t[n]
+
+
+# --------------------------------------------------------------------------
+# Backward of block-sparse attention (section 3.1 eq 6; section 3.3: gradients
+# flow through attention on the selected entries)
+# --------------------------------------------------------------------------
+def _grid(rng, shape, lim=2.0):
+    """Values on the 2^-10 grid: x and x +- 2^-10 are exact in float32."""
+    return (np.round(rng.uniform(-lim, lim, shape) * 1024) / 1024).astype(np.float32)
+
+
+def _random_selection(rng, N, H, C, K_top, causal):
+    M1 = -(-N // C)
+    sel = np.full((N, H, K_top), -1, np.int32)
+    for n in range(N):
+        hi = (n // C + 1) if causal else M1
+        for h in range(H):
+            k = int(rng.integers(0, min(K_top, hi) + 1))
+            sel[n, h, :k] = np.sort(rng.choice(hi, size=k, replace=False))
+    return sel
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_bwd_matches_central_differences(causal):
+    """Every gradient entry against (L(x + eps) - L(x - eps)) / (2 eps) of the forward oracle's
+    loss L = sum dO . o, eps = 2^-10 (error O(eps^2)); rows with no visible key included."""
+    rng = np.random.default_rng(41 + causal)
+    N, C, H, Hq, d, Kt = 14, 4, 2, 4, 4, 3
+    Q, K, V = _grid(rng, (N, Hq, d)), _grid(rng, (1, N, H, d)), _grid(rng, (1, N, H, d))
+    dO = _grid(rng, (N, Hq, d))
+    sel = _random_selection(rng, N, H, C, Kt, causal)
+    t = np.arange(N)
+    g = oracle.sparse_attn_bwd(Q, [0] * N, t, K, V, dO, N, C, sel, causal=causal, threads=1)
+
+    def loss(Qx, Kx, Vx):
+        o = oracle.sparse_attn(Qx, [0] * N, t, Kx, Vx, N, C, sel, causal=causal, threads=1)["out"]
+        return float((o * dO.astype(np.float64)).sum())
+
+    eps = 2.0 ** -10
+    for name, arr, grad in (("Q", Q, g["dQ"]), ("K", K, g["dK"]), ("V", V, g["dV"])):
+        fd = np.zeros(arr.size)
+        for k in range(arr.size):
+            hi, lo = arr.copy(), arr.copy()
+            hi.reshape(-1)[k] += eps
+            lo.reshape(-1)[k] -= eps
+            args_hi = {"Q": (hi, K, V), "K": (Q, hi, V), "V": (Q, K, hi)}[name]
+            args_lo = {"Q": (lo, K, V), "K": (Q, lo, V), "V": (Q, K, lo)}[name]
+            fd[k] = (loss(*args_hi) - loss(*args_lo)) / (2 * eps)
+        np.testing.assert_allclose(grad.reshape(-1), fd, rtol=0, atol=2e-5, err_msg=name)
+    assert np.abs(g["dK"]).max() > 0.05 and np.abs(g["dQ"]).max() > 0.05
+
+
+def test_attn_bwd_dense_equals_torch_autograd():
+    """Selecting every block makes eq 6 dense causal softmax attention: the gradients equal
+    torch autograd (float64) of softmax(Q K^T / sqrt(d) + causal mask) V with grouped heads."""
+    rng = np.random.default_rng(43)
+    N, C, H, Hq, d = 90, 16, 2, 6, 8
+    Q = rng.standard_normal((N, Hq, d)).astype(np.float32)
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    V = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    dO = rng.standard_normal((N, Hq, d)).astype(np.float32)
+    M1 = -(-N // C)
+    sel = np.tile(np.arange(M1, dtype=np.int32), (N, H, 1))
+    g = oracle.sparse_attn_bwd(Q, [0] * N, np.arange(N), K, V, dO, N, C, sel, causal=True)
+    q = torch.from_numpy(Q).double().permute(1, 0, 2).requires_grad_()
+    k = torch.from_numpy(K[0]).double().permute(1, 0, 2).requires_grad_()
+    v = torch.from_numpy(V[0]).double().permute(1, 0, 2).requires_grad_()
+    G = Hq // H
+    s = q @ k.repeat_interleave(G, 0).transpose(1, 2) / math.sqrt(d)
+    s = s.masked_fill(~torch.ones(N, N, dtype=torch.bool).tril(), float("-inf"))
+    o = torch.softmax(s, -1) @ v.repeat_interleave(G, 0)
+    o.backward(torch.from_numpy(dO).double().permute(1, 0, 2))
+    np.testing.assert_allclose(g["dQ"], q.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(g["dK"][0], k.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(g["dV"][0], v.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-10)
+
+
+def test_attn_bwd_sum_identities():
+    """Softmax rows sum to one, so per (sequence, KV head) the key gradients sum to zero and
+    the value gradients sum to the upstream gradients of the rows that see a key."""
+    rng = np.random.default_rng(44)
+    B, N, C, H, Hq, d, Kt = 2, 150, 8, 2, 4, 16, 5
+    K = rng.standard_normal((B, N, H, d)).astype(np.float32)
+    V = rng.standard_normal((B, N, H, d)).astype(np.float32)
+    Q = rng.standard_normal((B * N, Hq, d)).astype(np.float32)
+    dO = rng.standard_normal((B * N, Hq, d)).astype(np.float32)
+    sel = np.concatenate([_random_selection(rng, N, H, C, Kt, True) for _ in range(B)])
+    ib = np.repeat(np.arange(B), N)
+    it = np.tile(np.arange(N), B)
+    g = oracle.sparse_attn_bwd(Q, ib, it, K, V, dO, N, C, sel, causal=True)
+    seen = (sel >= 0).any(-1)  # [items][H]: every selected block starts at or before t
+    G = Hq // H
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_allclose(g["dK"][b, :, h].sum(0), 0.0, atol=1e-9)
+            rows = (ib == b) & seen[:, h]
+            want = dO[rows][:, h * G:(h + 1) * G].astype(np.float64).sum((0, 1))
+            np.testing.assert_allclose(g["dV"][b, :, h].sum(0), want, atol=1e-9)
