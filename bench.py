@@ -119,7 +119,7 @@ def time_fn(fn, reps, warm=2):
 
 # the sources each counted kernel is compiled from (its file, the headers it includes and
 # the host code that launches it): a counter record stays valid while these are unchanged
-_COMMON_SRC = ("pisa_device.hpp", "pisa_internal.hpp", "capi.hip")
+_COMMON_SRC = ("pisa_device.hpp", "pisa_internal.hpp")
 STAGE_SOURCES = {
     "build": ("pyramid.hip",),
     "leaf": ("levels.hip", "levels_impl.hpp", "levels_bf16.hip", "stream.hpp"),
