@@ -23,6 +23,7 @@
 // of once per row.
 #include <algorithm>
 
+#include "attn_bwd.hpp"
 #include "pisa_device.hpp"
 #include "pisa_internal.hpp"
 #include "stream.hpp"
@@ -524,9 +525,8 @@ AttnClLayout attn_cl_layout(int64_t B, int64_t N_q, int64_t N_alloc, int H_kv, i
     return L;
 }
 
-hipError_t launch_attn_clustered(AttnClArgs a, int d, char* ws, hipStream_t s)
+hipError_t launch_attn_cluster(AttnClArgs& a, const AttnClLayout& L, char* ws, hipStream_t s)
 {
-    const AttnClLayout L = attn_cl_layout(a.B, a.N_q, a.N_alloc, a.H_kv, a.G, d, a.C, a.K_top);
     a.M_blk = L.M_blk;
     a.n_clusters = L.n_clusters;
     a.qc = kLeafQC;
@@ -537,8 +537,6 @@ hipError_t launch_attn_clustered(AttnClArgs a, int d, char* ws, hipStream_t s)
     a.chunk_cl = reinterpret_cast<int32_t*>(ws + L.chunk_cl);
     a.block_sums = reinterpret_cast<int32_t*>(ws + L.block_sums);
     a.entries = reinterpret_cast<int32_t*>(ws + L.entries);
-    a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
-    a.part_o = ws + L.part_o;
     hipError_t e;
     if ((e = launch_fill_zero(a.counts, 2 * L.n_clusters, s)) != hipSuccess) return e;
     const dim3 cgrid((unsigned)((a.N_q + kClRowsPerBlock - 1) / kClRowsPerBlock), (unsigned)(a.B * a.H_kv));
@@ -549,7 +547,16 @@ hipError_t launch_attn_clustered(AttnClArgs a, int d, char* ws, hipStream_t s)
         hipSuccess)
         return e;
     hipLaunchKernelGGL(attn_cluster_kernel, cgrid, dim3(kClThreads), clds, s, a, 1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_clustered(AttnClArgs a, int d, char* ws, hipStream_t s)
+{
+    const AttnClLayout L = attn_cl_layout(a.B, a.N_q, a.N_alloc, a.H_kv, a.G, d, a.C, a.K_top);
+    a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+    a.part_o = ws + L.part_o;
+    hipError_t e;
+    if ((e = launch_attn_cluster(a, L, ws, s)) != hipSuccess) return e;
     const int64_t grid = L.n_items / kLeafQC + L.n_clusters;  // bound on the chunks
     if ((e = (d == 64 ? launch_cl_d<64>(a, grid, s) : launch_cl_d<128>(a, grid, s))) != hipSuccess) return e;
     const int64_t items = (int64_t)a.B * a.H_kv * a.N_q;

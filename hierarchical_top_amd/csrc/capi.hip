@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "attn_bwd.hpp"
 #include "pisa_internal.hpp"
 
 using namespace pisa;
@@ -548,6 +549,48 @@ pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void*
     hipError_t e = launch_attn_clustered(a, d, (char*)ws, (hipStream_t)stream);
     stage_mark(PISA_STAGE_ATTN, true, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn_clustered");
+}
+
+pisa_status pisa_sparse_attn_bwd_workspace(int32_t B, int64_t N_q, int64_t N_alloc, int32_t H_q, int32_t H_kv,
+                                           int32_t d, int32_t C, int32_t K_top, size_t* bytes)
+{
+    if (!bytes) return fail(PISA_EINVAL, "bytes must be non-NULL");
+    pisa_status st = check_attn_cl(B, N_q, N_alloc, H_q, H_kv, d, C, K_top);
+    if (st != PISA_OK) return st;
+    *bytes = attn_bwd_layout(B, N_q, N_alloc, H_q, H_kv, d, C, K_top).bytes;
+    return ok();
+}
+
+pisa_status pisa_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                 const float* lse, pisa_dtype dt, int32_t B, int64_t N_q, int64_t N_kv,
+                                 int64_t N_alloc, int32_t H_q, int32_t H_kv, int32_t d, int32_t C,
+                                 const int32_t* block_idx, int32_t K_top, int32_t causal, const int64_t* kv_len,
+                                 float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!dtype_ok(dt)) return fail(PISA_EINVAL, "dtype %d is not PISA_F32 or PISA_BF16", (int)dt);
+    if (dt != PISA_BF16) return fail(PISA_EUNSUPPORTED, "attention backward takes bf16 inputs");
+    if (!Q || !K || !V || !O || !dO || !lse || !block_idx || !dQ || !dK || !dV || !ws)
+        return fail(PISA_EINVAL, "Q, K, V, O, dO, lse, block_idx, dQ, dK, dV and ws must be non-NULL");
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
+        !aligned16(dK) || !aligned16(dV))
+        return fail(PISA_EINVAL, "Q, K, V, O, dO, dQ, dK and dV must be 16-byte aligned");
+    if (((uintptr_t)ws & 255) != 0) return fail(PISA_EINVAL, "ws must be 256-byte aligned");
+    if (N_kv < 1 || N_alloc < N_kv || N_q > N_kv) return fail(PISA_EINVAL, "need 1 <= N_q <= N_kv <= N_alloc");
+    pisa_status st = check_attn_cl(B, N_q, N_alloc, H_q, H_kv, d, C, K_top);
+    if (st != PISA_OK) return st;
+    if ((int64_t)B * N_q * H_q >= ((int64_t)1 << 31)) return fail(PISA_EUNSUPPORTED, "B * N_q * H_q >= 2^31");
+    const AttnBwdLayout L = attn_bwd_layout(B, N_q, N_alloc, H_q, H_kv, d, C, K_top);
+    if (ws_bytes < L.bytes) return fail(PISA_ENOSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.bytes);
+    AttnBwdArgs a;
+    memset(&a, 0, sizeof(a));
+    AttnClArgs& c = a.c;
+    c.Q = Q; c.K = K; c.V = V; c.B = B; c.H_q = H_q; c.H_kv = H_kv; c.G = H_q / H_kv; c.C = C; c.K_top = K_top;
+    c.causal = causal ? 1 : 0; c.N_q = N_q; c.N_kv = N_kv; c.N_alloc = N_alloc; c.idx = block_idx; c.kv_len = kv_len;
+    a.O = O; a.dO = dO; a.lse = lse; a.dQ = dQ; a.dK = dK; a.dV = dV;
+    stage_mark(PISA_STAGE_ATTN_BWD, false, (hipStream_t)stream);
+    hipError_t e = launch_attn_bwd(a, d, (char*)ws, (hipStream_t)stream);
+    stage_mark(PISA_STAGE_ATTN_BWD, true, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn_bwd");
 }
 
 pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt, int64_t N, int32_t H_q,

@@ -69,6 +69,10 @@ def lib():
                                            ctypes.POINTER(c_size)],
             "pisa_sparse_attn_clustered": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32,
                                            c_i32, c_p, c_i32, c_i32, c_p, c_p, c_p, c_p, c_size, c_p],
+            "pisa_sparse_attn_bwd_workspace": [c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                               ctypes.POINTER(c_size)],
+            "pisa_sparse_attn_bwd": [c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32,
+                                     c_i32, c_i32, c_p, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_size, c_p],
             "pisa_bsa_select": [P, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_time_stage": [c_i32, c_p, c_p],
             "pisa_time_stage_pending": [c_i32],
@@ -89,13 +93,14 @@ def lib():
 
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
            "pisa_route_prefill", "pisa_route_prefill_scored", "pisa_route_decode", "pisa_sparse_attn", "pisa_sparse_attn_workspace",
-           "pisa_sparse_attn_clustered", "pisa_bsa_select", "pisa_time_stage",
+           "pisa_sparse_attn_clustered", "pisa_sparse_attn_bwd_workspace", "pisa_sparse_attn_bwd",
+           "pisa_bsa_select", "pisa_time_stage",
            "pisa_time_stage_pending",
            "pisa_status_str", "pisa_last_error", "pisa_abi_version"]
 
 # Stage ids of pisa_time_stage (include/pisa.h, enum pisa_stage).
 STAGES = {"build": 0, "append": 1, "route_fused": 2, "route_decode": 3, "upper": 4, "cluster": 5, "leaf": 6,
-          "final": 7, "attn": 8, "bsa": 9}
+          "final": 7, "attn": 8, "bsa": 9, "attn_bwd": 10}
 
 
 def _check(status: int):
@@ -246,6 +251,39 @@ def sparse_attn_clustered(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, blo
                                             C, _ptr(block_idx), K_top, 1 if causal else 0, _ptr(kv_len), _ptr(O),
                                             _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return (O, lse) if with_lse else O
+
+
+def sparse_attn_bwd_workspace_bytes(B: int, N_q: int, N_alloc: int, H_q: int, H_kv: int, d: int, C: int,
+                                    K_top: int) -> int:
+    n = c_size(0)
+    _check(lib().pisa_sparse_attn_bwd_workspace(B, N_q, N_alloc, H_q, H_kv, d, C, K_top, ctypes.byref(n)))
+    return int(n.value)
+
+
+def sparse_attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor,
+                    lse: torch.Tensor, block_idx: torch.Tensor, C: int, N_kv: int, causal: bool = True,
+                    kv_len: torch.Tensor | None = None, workspace: torch.Tensor | None = None, out=None):
+    """Gradients of block-sparse attention (bf16 inputs): returns fp32 (dQ, dK, dV) shaped like Q, K, V.
+
+    O and lse are the forward's output and log-normaliser [B][H_q][N_q]; out = (dQ, dK, dV) to reuse."""
+    _dev(Q, K, V, O, dO, lse, block_idx, kv_len)
+    B, N_q, H_q, d = Q.shape
+    N_alloc, H_kv = K.shape[1], K.shape[2]
+    K_top = block_idx.shape[-1]
+    assert O.shape == Q.shape and dO.shape == Q.shape and lse.dtype == torch.float32
+    need = sparse_attn_bwd_workspace_bytes(B, N_q, N_alloc, H_q, H_kv, d, C, K_top)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        torch.empty(need, dtype=torch.uint8, device=Q.device)
+    if out is None:
+        out = (torch.empty(Q.shape, dtype=torch.float32, device=Q.device),
+               torch.empty(K.shape, dtype=torch.float32, device=Q.device),
+               torch.empty(V.shape, dtype=torch.float32, device=Q.device))
+    dQ, dK, dV = out
+    _check(lib().pisa_sparse_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(lse), _dt(Q), B, N_q, N_kv,
+                                      N_alloc, H_q, H_kv, d, C, _ptr(block_idx), K_top, 1 if causal else 0,
+                                      _ptr(kv_len), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream()))
+    return dQ, dK, dV
 
 
 def bsa_select(pyr: Pyramid, Q: torch.Tensor, N: int, K_top: int, causal: bool = True, with_score: bool = False,

@@ -133,3 +133,62 @@ def make_decode(w: Workload, device, chunk_tokens: int = 1 << 16):
     v = torch.randn(w.steps, w.B, w.H_kv, w.d, generator=gen, dtype=torch.float32,
                     device=device).to(dt)
     return Kc, Vc, q, k, v
+
+
+def make_grad_out(shape, seed: int, dtype=torch.bfloat16):
+    """Upstream gradient of the attention output: N(0, 1) float32 from its own seeded
+    generator, rounded to ``dtype`` (RNE)."""
+    gen = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(dtype)
+
+
+def random_selection(seed: int, B: int, H_kv: int, N_q: int, K_top: int, C: int, kv_len, causal: bool = True,
+                     empty_rows: float = 0.0):
+    """Block ids [B][H_kv][N_q][K_top] int32 with the structure of a causal PISA
+    selection, drawn at random (no scores): row r of sequence b sits at position
+    kv_len[b] - N_q + r; under causal masking its eligible blocks are 0..c with
+    c = position // C, and when more than K_top are eligible it keeps 0, c - 1 and
+    c plus K_top - 3 distinct others, one drawn uniformly from each of K_top - 3
+    equal strata of 1..c - 2; without causal masking every row keeps K_top of the
+    ceil(kv_len / C) blocks the same way (no forced blocks). Ascending, -1 padded.
+    A fraction ``empty_rows`` of the rows selects nothing."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = np.full((B, H_kv, N_q, K_top), -1, np.int32)
+    r = np.arange(N_q)
+    for b in range(B):
+        n = int(kv_len[b])
+        M = (n + C - 1) // C
+        pos = n - N_q + r
+        for h in range(H_kv):
+            if causal:
+                c = pos // C
+                lo, span, nf = 1, c - 2, 3       # strata over 1 .. c - 2, plus 0, c - 1, c
+            else:
+                c = np.full(N_q, M - 1)
+                lo, span, nf = 0, np.full(N_q, M), 0
+            E = c + 1
+            k_free = K_top - nf
+            sel = np.full((N_q, K_top), -1, np.int64)
+            small = E <= K_top
+            if small.any():
+                ar = np.arange(K_top)[None, :]
+                sel[small] = np.where(ar < E[small, None], ar, -1)
+            big = ~small
+            if big.any() and k_free > 0:
+                sp = span[big].astype(np.int64)[:, None]
+                u = rng.random((int(big.sum()), k_free))
+                j = np.arange(k_free + 1)[None, :]
+                edge = (j * sp) // k_free                      # integer strata [edge_j, edge_j+1)
+                width = edge[:, 1:] - edge[:, :-1]             # >= 1: span >= k_free here
+                strata = edge[:, :-1] + np.minimum(np.floor(u * width).astype(np.int64), width - 1) + lo
+                if causal:
+                    cb = c[big][:, None]
+                    picks = np.concatenate([np.zeros_like(cb), strata, cb - 1, cb], axis=1)
+                else:
+                    picks = strata
+                sel[big] = np.sort(picks, axis=1)
+            if empty_rows > 0:
+                sel[rng.random(N_q) < empty_rows] = -1
+            out[b, h] = sel
+    return out

@@ -235,6 +235,38 @@ pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void*
                                        float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Backward of block-sparse attention with fixed block indices (section 3.1
+ * eq 6; section 3.3: in training, gradients flow through attention on the
+ * selected entries, the selection is not differentiated). With
+ * z_j = q . k_j / sqrt(d) over the row's visible selected keys, p = softmax(z),
+ * o = sum_j p_j v_j and the upstream gradient dO of o:
+ *   dV_j += p_j dO;  dS_j = p_j (dO . v_j - dO . o);
+ *   dQ = sum_j dS_j k_j / sqrt(d);  dK_j += dS_j q / sqrt(d).
+ * Inputs as for pisa_sparse_attn_clustered, plus O (the forward output,
+ * [B][N_q][H_q][d], dtype dt), dO (same layout and dtype) and lse (device
+ * float32 [B][H_q][N_q], the forward's natural-log normaliser). Rows with no
+ * visible key get dQ = 0. Outputs are device float32: dQ [B][N_q][H_q][d],
+ * dK and dV [B][N_alloc][H_kv][d]; the call overwrites all of them (keys no
+ * row selected get 0). The fp32 sums are accumulated with atomics, so their
+ * last bits may differ between runs.
+ * ws: device workspace of at least pisa_sparse_attn_bwd_workspace() bytes,
+ * 256-byte aligned, owned by the caller, contents on entry ignored; calls
+ * sharing a workspace must not overlap.
+ * Supported: dt = PISA_BF16, d in {64, 128}, C in {16, 32, 64}, G_Q in
+ * {1, 2, 4, 8, 16}, K_top <= 64, N_q < 2^25, B * N_q * H_q < 2^31.
+ * Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE (ws too small), PISA_EHIP.
+ */
+pisa_status pisa_sparse_attn_bwd_workspace(int32_t B, int64_t N_q, int64_t N_alloc, int32_t H_q,
+                                           int32_t H_kv, int32_t d, int32_t C, int32_t K_top,
+                                           size_t* bytes);
+pisa_status pisa_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                                 const void* dO, const float* lse, pisa_dtype dt, int32_t B,
+                                 int64_t N_q, int64_t N_kv, int64_t N_alloc, int32_t H_q,
+                                 int32_t H_kv, int32_t d, int32_t C, const int32_t* block_idx,
+                                 int32_t K_top, int32_t causal, const int64_t* kv_len, float* dQ,
+                                 float* dK, float* dV, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Exhaustive single-level selector in the style of BSA (section 3.1 eq 2-5),
  * the comparison point: every eligible leaf (start <= t when causal) except
  * the forced ones is scored by z = q_{t,h'} . kbar_i / sqrt(d) with the level-1
@@ -276,7 +308,8 @@ typedef enum pisa_stage {
     PISA_STAGE_FINAL = 7,         /* two-stage: final Select_K; level-synchronous: Select_K of one level */
     PISA_STAGE_ATTN = 8,          /* pisa_sparse_attn */
     PISA_STAGE_BSA = 9,           /* pisa_bsa_select */
-    PISA_STAGE_COUNT = 10
+    PISA_STAGE_ATTN_BWD = 10,     /* pisa_sparse_attn_bwd */
+    PISA_STAGE_COUNT = 11
 } pisa_stage;
 
 pisa_status pisa_time_stage(int32_t stage, void* start_event, void* stop_event);

@@ -61,7 +61,7 @@ def _load():
         lib.orc_route_scored.argtypes = [P, P, P, i64, P, P, P, i32, i64, i64, i32, i32, i32, i32,
                                          i32, i32, i32, i32, P, P, P, P, i32]
         lib.orc_route_scored.restype = i32
-        lib.orc_sparse_attn_bwd.argtypes = [P, P, P, i64, P, P, P, i32, i64, i64, i32, i32, i32,
+        lib.orc_sparse_attn_bwd.argtypes = [P, P, P, i64, P, P, P, P, i32, i64, i64, i32, i32, i32,
                                             i32, P, i32, i32, P, P, P, i32]
         lib.orc_sparse_attn_bwd.restype = i32
         lib.orc_bsa.argtypes = [P, P, P, i64, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
@@ -199,11 +199,13 @@ def sparse_attn(Qi, item_b, item_t, K, V, N: int, C: int, sel, causal: bool = Tr
 
 
 def sparse_attn_bwd(Qi, item_b, item_t, K, V, dO, N: int, C: int, sel, causal: bool = True,
-                    threads: int | None = None):
+                    threads: int | None = None, O=None):
     """Gradients of block-sparse attention (eq 6) for queries Qi [n][H_q][d] over
     sel [n][H][k] with upstream gradient dO [n][H_q][d]: dict(dQ [n][H_q][d],
-    dK, dV [B][N_alloc][H][d]) in float64; dK and dV hold the given items' parts."""
+    dK, dV [B][N_alloc][H][d]) in float64; dK and dV hold the given items' parts.
+    O: the saved forward output [n][H_q][d] whose dO . O replaces sum_j p_j dp_j."""
     Qi, K, V, dO = _f32(Qi), _f32(K), _f32(V), _f32(dO)
+    Os = _f32(O) if O is not None else None
     n, H_q, d = Qi.shape
     B, N_alloc, H, _ = K.shape
     sel = np.ascontiguousarray(sel, dtype=np.int32)
@@ -211,7 +213,7 @@ def sparse_attn_bwd(Qi, item_b, item_t, K, V, dO, N: int, C: int, sel, causal: b
     dQ = np.empty((n, H_q, d), dtype=np.float64)
     dK = np.empty((B, N_alloc, H, d), dtype=np.float64)
     dV = np.empty((B, N_alloc, H, d), dtype=np.float64)
-    rc = _load().orc_sparse_attn_bwd(_ptr(Qi), _ptr(b), _ptr(t), n, _ptr(K), _ptr(V), _ptr(dO), B,
+    rc = _load().orc_sparse_attn_bwd(_ptr(Qi), _ptr(b), _ptr(t), n, _ptr(K), _ptr(V), _ptr(dO), _ptr(Os), B,
                                      N_alloc, int(N), H, H_q, d, int(C), _ptr(sel), sel.shape[2],
                                      int(bool(causal)), _ptr(dQ), _ptr(dK), _ptr(dV),
                                      threads or default_threads())

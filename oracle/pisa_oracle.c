@@ -130,6 +130,7 @@ typedef struct {
     int32_t *trace;         /* [n_items][H][L+1][2]: |A| after filter, #scored (may be NULL) */
     /* attention backward */
     const float *dO;        /* [n_items][H_q][d] gradient of the loss w.r.t. the output */
+    const float *Osaved;    /* [n_items][H_q][d] saved forward output, or NULL */
     double *dQ;             /* [n_items][H_q][d] */
     double *dK, *dV;        /* [B][N_alloc][H][d], accumulated */
     const int32_t *sel;     /* attention: selected blocks [n_items][H][K_top] */
@@ -491,6 +492,9 @@ static void attn_one(const orc_problem *P, int64_t item, int hq)
  *   dz_j  = p_j (dp_j - sum_{k in T} p_k dp_k)   (Jacobian of the softmax)
  *   dq   += sum_j dz_j k_j / sqrt(d)
  *   dk_j += dz_j q / sqrt(d)
+ * Since sum_k p_k dp_k = dO . o, a backward that is handed the saved forward
+ * output O uses dO . O in its place (Osaved non-NULL): the two agree exactly
+ * when O is the exact output, and differ by dO . (O - o) when O was rounded.
  * Every (item, query head) of KV head h of sequence b adds into the same dK,
  * dV rows, so one task owns one (b, h) and visits its items in increasing
  * order and the G_Q query heads in increasing order.
@@ -530,6 +534,7 @@ static void attn_bwd_one(const orc_problem *P, int64_t item, int hq)
             dp[k] = dot_ff(dO, v, P->d);
             pdp += exp(z[k] - lz) * dp[k];
         }
+        if (P->Osaved) pdp = dot_ff(dO, P->Osaved + (item * P->H_q + hq) * P->d, P->d);
         for (int64_t k = 0; k < n; k++) {
             double p = exp(z[k] - lz);
             double dz = p * (dp[k] - pdp);
@@ -682,13 +687,14 @@ int orc_sparse_attn(const float *Q, const int64_t *item_b, const int64_t *item_t
 }
 
 /* Backward of block-sparse attention for n_items queries over sel [n_items][H][sel_k],
- * given dO [n_items][H_q][d]. Writes dQ [n_items][H_q][d]; dK and dV
+ * given dO [n_items][H_q][d] and optionally the saved forward output O (same
+ * layout, NULL: none). Writes dQ [n_items][H_q][d]; dK and dV
  * [B][N_alloc][H][d] are set to zero and then accumulate every item's part. */
 int orc_sparse_attn_bwd(const float *Q, const int64_t *item_b, const int64_t *item_t,
-                        int64_t n_items, const float *K, const float *V, const float *dO, int B,
-                        int64_t N_alloc, int64_t N, int H, int H_q, int d, int C,
-                        const int32_t *sel, int sel_k, int causal, double *dQ, double *dK,
-                        double *dV, int nthreads)
+                        int64_t n_items, const float *K, const float *V, const float *dO,
+                        const float *Osaved, int B, int64_t N_alloc, int64_t N, int H, int H_q,
+                        int d, int C, const int32_t *sel, int sel_k, int causal, double *dQ,
+                        double *dK, double *dV, int nthreads)
 {
     orc_problem P;
     if (setup(&P, Q, item_b, item_t, n_items, K, NULL, NULL, B, N_alloc, N, H, H_q, d, C, 2,
@@ -696,7 +702,7 @@ int orc_sparse_attn_bwd(const float *Q, const int64_t *item_b, const int64_t *it
     for (int64_t k = 0; k < n_items; k++)
         if (item_b[k] < 0 || item_b[k] >= B) return -1;
     P.V = V; P.sel = sel; P.sel_k = sel_k; P.causal = causal;
-    P.dO = dO; P.dQ = dQ; P.dK = dK; P.dV = dV;
+    P.dO = dO; P.Osaved = Osaved; P.dQ = dQ; P.dK = dK; P.dV = dV;
     size_t kv = (size_t)B * (size_t)N_alloc * (size_t)H * (size_t)d;
     memset(dK, 0, kv * sizeof(double));
     memset(dV, 0, kv * sizeof(double));

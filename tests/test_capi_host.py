@@ -203,7 +203,7 @@ def test_clustered_attention_validation(lib):
 
 
 def test_time_stage_validation(lib):
-    assert lib.pisa_time_stage(10, None, None) == EINVAL
+    assert lib.pisa_time_stage(11, None, None) == EINVAL
     assert lib.pisa_time_stage(-1, None, None) == EINVAL
     assert lib.pisa_time_stage(0, FAKE, None) == EINVAL
     assert lib.pisa_time_stage(0, None, None) == OK  # disarm

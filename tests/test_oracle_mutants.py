@@ -43,6 +43,7 @@ MUTANTS = [
     ("bwd_no_centering", "double dz = p * (dp[k] - pdp);", "double dz = p * dp[k];"),
     ("bwd_dk_unscaled", "P->dK[row + e] += dz * scale * (double)q[e];", "P->dK[row + e] += dz * (double)q[e];"),
     ("bwd_dv_unnormalised", "P->dV[row + e] += p * (double)dO[e];", "P->dV[row + e] += exp(z[k]) * (double)dO[e];"),
+    ("bwd_saved_output_ignored", "if (P->Osaved) pdp = dot_ff(", "if (0) pdp = dot_ff("),
     ("bwd_mask_self", "if (P->causal && t < j) continue;", "if (P->causal && t <= j) continue;"),
     ("ascending_scores", "if (x->u > y->u) return -1;\n    if (x->u < y->u) return 1;",
      "if (x->u < y->u) return -1;\n    if (x->u > y->u) return 1;"),

@@ -644,3 +644,30 @@ def test_attn_bwd_sum_identities():
             rows = (ib == b) & seen[:, h]
             want = dO[rows][:, h * G:(h + 1) * G].astype(np.float64).sum((0, 1))
             np.testing.assert_allclose(g["dV"][b, :, h].sum(0), want, atol=1e-9)
+
+
+def test_attn_bwd_saved_output_form():
+    """sum_j p_j dp_j = dO . o: handed the (float32-rounded) exact forward output, the
+    saved-output form of the backward gives the same gradients; handed a perturbed
+    output O + e, dQ moves by -dO.e * sum_j p_j k_j / sqrt(d), the attention output
+    with values k (the oracle forward with V replaced by K)."""
+    rng = np.random.default_rng(45)
+    N, C, H, Hq, d, Kt = 120, 8, 2, 4, 16, 5
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    V = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    Q = rng.standard_normal((N, Hq, d)).astype(np.float32)
+    dO = rng.standard_normal((N, Hq, d)).astype(np.float32)
+    sel = _random_selection(rng, N, H, C, Kt, True)
+    t = np.arange(N)
+    O = oracle.sparse_attn(Q, [0] * N, t, K, V, N, C, sel)["out"].astype(np.float32)
+    g0 = oracle.sparse_attn_bwd(Q, [0] * N, t, K, V, dO, N, C, sel)
+    g1 = oracle.sparse_attn_bwd(Q, [0] * N, t, K, V, dO, N, C, sel, O=O)
+    for k in ("dQ", "dK", "dV"):
+        np.testing.assert_allclose(g1[k], g0[k], rtol=0, atol=1e-5 * np.abs(g0[k]).max())
+    e = (rng.standard_normal(O.shape) * 0.01).astype(np.float32)
+    g2 = oracle.sparse_attn_bwd(Q, [0] * N, t, K, V, dO, N, C, sel, O=O + e)
+    kbar = oracle.sparse_attn(Q, [0] * N, t, K, K, N, C, sel)["out"]  # sum_j p_j k_j
+    dD = ((O + e).astype(np.float64) * dO).sum(-1) - (O.astype(np.float64) * dO).sum(-1)
+    want = g1["dQ"] - dD[..., None] * kbar / math.sqrt(d)
+    np.testing.assert_allclose(g2["dQ"], want, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(g2["dV"], g1["dV"], rtol=0, atol=1e-12)
