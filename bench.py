@@ -348,6 +348,19 @@ def prefill_extra(name, reps, with_attn=False):
         out["attn_ms"] = ms
         out["attn_tflops"] = 2 * aw["mac"] / (ms * 1e-3) / 1e12
         out["attn_mfma_frac"] = out["attn_tflops"] / PEAK_BF16_TFLOPS
+        # backward with the routed blocks fixed (dQ, dK, dV in fp32 from the forward's O and lse)
+        O, lse = pisa.sparse_attn_clustered(P.Q, P.K, P.V, P.idx, w.C, w.N, with_lse=True)
+        dO = synth.make_grad_out(P.Q.shape, 303).cuda()
+        bws = torch.empty(pisa.sparse_attn_bwd_workspace_bytes(w.B, w.N, w.N, w.H_q, w.H_kv, w.d, w.C, w.K_top),
+                          dtype=torch.uint8, device="cuda")
+        grads = tuple(torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in (P.Q, P.K, P.V))
+        bw = workcount.attn_bwd_work(w.B, w.N, w.H_q, w.d, w.C, w.K_top)
+        ms_b = time_fn(lambda: pisa.sparse_attn_bwd(P.Q, P.K, P.V, O, dO, lse, P.idx, w.C, w.N, workspace=bws,
+                                                    out=grads), reps)
+        out["attn_bwd_ms"] = ms_b
+        out["attn_bwd_tflops"] = 2 * bw["mac"] / (ms_b * 1e-3) / 1e12
+        out["attn_bwd_mfma_frac"] = out["attn_bwd_tflops"] / PEAK_BF16_TFLOPS
+        del O, lse, dO, bws, grads
     del P
     torch.cuda.empty_cache()
     return out

@@ -23,9 +23,13 @@
 //      bf16 terms, dO and Q transposed in LDS) and are added to global memory
 //      once per chunk. dQ = dS K contracts over the keys of all waves: dS goes
 //      to LDS and every wave computes some (column tile, d tile) products
-//      against K^T in LDS, added to dQ with fp32 atomics.
-// dQ, dK and dV are fp32 and are cleared first; the atomics make the order of
-// the fp32 sums, and so the last bits, vary from run to run.
+//      against K^T in LDS, stored as the (row, slot, head)'s fp32 partial dQ;
+//   4. dq_combine_kernel: one wave per (sequence, row, KV head) sums its
+//      partials in slot order into dQ (rows with no visible key get 0).
+// dK and dV are cleared first and take each chunk's part with fp32 atomics,
+// so their last bits vary from run to run; dQ is deterministic. (Atomics for dQ
+// too -- K_top per element, scattered over rows -- cost several times the
+// whole kernel.)
 #include <algorithm>
 
 #include "attn_bwd.hpp"
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     float* s_lse2 = reinterpret_cast<float*>(s_raw + Gm::OFF_META);
     float* s_dsum = s_lse2 + NCOL;
     int* s_vis = reinterpret_cast<int*>(s_dsum + NCOL);
-    int* s_dqrow = s_vis + NCOL;  // (b * N_q + r) * H_q + query head, or -1 for a padding column
+    int* s_dqrow = s_vis + NCOL;  // partial row ((bh * N_q + r) * K_top + slot) * G + head, or -1 (padding)
     int* s_ent = reinterpret_cast<int*>(s_raw + Gm::OFF_ENT);
 
     const AttnClArgs& a = A.c;
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 const int64_t pos = nb - a.N_q + r;
                 if (a.causal && kend > pos + 1) kend = pos + 1;
                 m_vis = (int)(kend - k0);
-                m_row = (int)((((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head));
+                m_row = (int)(((bh * a.N_q + r) * a.K_top + (ent & 63)) * G + head);
             } else {
                 m_lse2 = INFINITY;  // padding column: p = 2^-inf = 0
                 m_dsum = 0.f;
@@ -312,11 +316,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 q = mfma(ak, bl_, q);
             }
             const int row = s_dqrow[16 * ctq + (lane & 15)];
-            if (row >= 0) {
-                float* dq = A.dQ + (int64_t)row * D + dt * 16 + 4 * lg;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dq + i, q[i] * inv_sqrt_d);
-            }
+            if (row >= 0)
+                *reinterpret_cast<f32x4*>(A.part_dq + (int64_t)row * D + dt * 16 + 4 * lg) = q * inv_sqrt_d;
         }
         __syncthreads();  // every wave is done with this iteration's LDS
         if (it + 1 < n_it) {
@@ -335,6 +336,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 unsafeAtomicAdd(A.dV + ro + 16 * dt, accV[dt][i]);
                 unsafeAtomicAdd(A.dK + ro + 16 * dt, accK[dt][i] * inv_sqrt_d);
             }
+        }
+    }
+}
+
+// Waves loop over (sequence, row, KV head) items with a stride of the grid; lanes
+// take (head, 4 d) pieces of the G x D outputs and add the partials of the slots
+// whose block holds a visible key, in slot order.
+template <int D>
+__global__ __launch_bounds__(256) void dq_combine_kernel(AttnBwdArgs A)
+{
+    constexpr int CH4 = D / 4;
+    const AttnClArgs& a = A.c;
+    const int lane = threadIdx.x & 63;
+    const int64_t total = (int64_t)a.B * a.H_kv * a.N_q;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    const int G = a.G, K_top = a.K_top;
+    for (int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); item < total; item += stride) {
+        const int64_t r = item % a.N_q;
+        const int64_t bh = item / a.N_q;
+        const int h = (int)(bh % a.H_kv);
+        const int b = (int)(bh / a.H_kv);
+        int64_t nb = a.kv_len ? a.kv_len[b] : a.N_kv;
+        nb = nb < 0 ? 0 : (nb > a.N_alloc ? a.N_alloc : nb);
+        const int64_t pos = nb - a.N_q + r;
+        bool vis = false;
+        if (lane < K_top) {
+            const int blk = a.idx[item * K_top + lane];
+            const int64_t k0 = (int64_t)blk * a.C;
+            int64_t kend = k0 + a.C < nb ? k0 + a.C : nb;
+            if (a.causal && kend > pos + 1) kend = pos + 1;
+            vis = blk >= 0 && k0 < nb && kend > k0;
+        }
+        const uint64_t valid = ballot(vis);
+        const int64_t prow = item * K_top;  // partial row of slot 0
+        for (int pc = lane; pc < G * CH4; pc += 64) {
+            const int head = pc / CH4, dc = pc % CH4;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (uint64_t m = valid; m; m &= m - 1) {
+                const int slot = __builtin_ctzll(m);
+                acc += *reinterpret_cast<const f32x4*>(A.part_dq + ((prow + slot) * G + head) * D + 4 * dc);
+            }
+            *reinterpret_cast<f32x4*>(A.dQ + (((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head) * D + 4 * dc) =
+                acc;
         }
     }
 }
@@ -373,7 +417,8 @@ AttnBwdLayout attn_bwd_layout(int64_t B, int64_t N_q, int64_t N_alloc, int H_q, 
     AttnBwdLayout L;
     L.cl = attn_cl_layout(B, N_q, N_alloc, H_kv, H_q / H_kv, d, C, K_top);
     L.dsum = L.cl.part_lse;  // the forward's partial sections are not used here
-    L.bytes = L.dsum + (((size_t)B * H_q * N_q * 4 + 255) & ~(size_t)255);
+    L.part_dq = L.dsum + (((size_t)B * H_q * N_q * 4 + 255) & ~(size_t)255);
+    L.bytes = L.part_dq + (size_t)L.cl.n_items * (H_q / H_kv) * d * 4;
     return L;
 }
 
@@ -381,10 +426,9 @@ hipError_t launch_attn_bwd(AttnBwdArgs a, int d, char* ws, hipStream_t s)
 {
     const AttnBwdLayout L = attn_bwd_layout(a.c.B, a.c.N_q, a.c.N_alloc, a.c.H_q, a.c.H_kv, d, a.c.C, a.c.K_top);
     a.dsum = reinterpret_cast<float*>(ws + L.dsum);
+    a.part_dq = reinterpret_cast<float*>(ws + L.part_dq);
     hipError_t e;
-    const int64_t nq = (int64_t)a.c.B * a.c.N_q * a.c.H_q * d;
     const int64_t nkv = (int64_t)a.c.B * a.c.N_alloc * a.c.H_kv * d;
-    if ((e = fill_zero_f32(a.dQ, nq, s)) != hipSuccess) return e;
     if ((e = fill_zero_f32(a.dK, nkv, s)) != hipSuccess) return e;
     if ((e = fill_zero_f32(a.dV, nkv, s)) != hipSuccess) return e;
     {
@@ -397,7 +441,12 @@ hipError_t launch_attn_bwd(AttnBwdArgs a, int d, char* ws, hipStream_t s)
     }
     if ((e = launch_attn_cluster(a.c, L.cl, ws, s)) != hipSuccess) return e;
     const int64_t grid = L.cl.n_items / kLeafQC + L.cl.n_clusters;  // bound on the chunks
-    return d == 64 ? launch_bwd_d<64>(a, grid, s) : launch_bwd_d<128>(a, grid, s);
+    if ((e = (d == 64 ? launch_bwd_d<64>(a, grid, s) : launch_bwd_d<128>(a, grid, s))) != hipSuccess) return e;
+    const int64_t items = (int64_t)a.c.B * a.c.H_kv * a.c.N_q;
+    const int64_t cblocks = std::min<int64_t>((items + 3) / 4, 256 * 8);  // grid-stride, 8 workgroups per CU
+    if (d == 64) hipLaunchKernelGGL(dq_combine_kernel<64>, dim3((unsigned)cblocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(dq_combine_kernel<128>, dim3((unsigned)cblocks), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace pisa

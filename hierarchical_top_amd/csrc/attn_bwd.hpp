@@ -18,6 +18,7 @@ struct AttnBwdArgs {
     const void* dO;       // [B][N_q][H_q][d] gradient of the loss w.r.t. O
     const float* lse;     // [B][H_q][N_q] forward log-normaliser (natural log)
     float* dsum;          // [B][H_q][N_q] workspace: sum over d of dO * O
+    float* part_dq;       // [B][H_kv][N_q][K_top][G][d] workspace: dQ of each (row, slot, head)
     float* dQ;            // [B][N_q][H_q][d]
     float* dK;            // [B][N_alloc][H_kv][d]
     float* dV;            // [B][N_alloc][H_kv][d]
@@ -25,7 +26,7 @@ struct AttnBwdArgs {
 
 struct AttnBwdLayout {
     AttnClLayout cl;      // cluster tables (the forward's partial-output sections are not used)
-    size_t dsum, bytes;
+    size_t dsum, part_dq, bytes;
 };
 AttnBwdLayout attn_bwd_layout(int64_t B, int64_t N_q, int64_t N_alloc, int H_q, int H_kv, int d, int C, int K_top);
 hipError_t launch_attn_bwd(AttnBwdArgs a, int d, char* ws, hipStream_t s);

@@ -578,7 +578,8 @@ pisa_status pisa_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
     if (N_kv < 1 || N_alloc < N_kv || N_q > N_kv) return fail(PISA_EINVAL, "need 1 <= N_q <= N_kv <= N_alloc");
     pisa_status st = check_attn_cl(B, N_q, N_alloc, H_q, H_kv, d, C, K_top);
     if (st != PISA_OK) return st;
-    if ((int64_t)B * N_q * H_q >= ((int64_t)1 << 31)) return fail(PISA_EUNSUPPORTED, "B * N_q * H_q >= 2^31");
+    if ((int64_t)B * N_q * H_q * K_top >= ((int64_t)1 << 31))
+        return fail(PISA_EUNSUPPORTED, "B * N_q * H_q * K_top >= 2^31");
     const AttnBwdLayout L = attn_bwd_layout(B, N_q, N_alloc, H_q, H_kv, d, C, K_top);
     if (ws_bytes < L.bytes) return fail(PISA_ENOSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.bytes);
     AttnBwdArgs a;

@@ -113,3 +113,11 @@ def attn_work(B: int, n: int, H_q: int, d: int, C: int, K_top: int):
     keys = (np.minimum(K_top, c + 1) - 1) * C + (t - c * C + 1)
     k = int(keys.sum())
     return dict(mac=2 * B * H_q * d * k, exp=B * H_q * k, keys=B * H_q * k)
+
+
+def attn_bwd_work(B: int, n: int, H_q: int, d: int, C: int, K_top: int):
+    """Work of the attention backward for the same selection: per (query head, visible
+    key) five d-long products -- the recomputed score, dP = dO . v, and the dV, dK and
+    dQ updates -- and one exponential."""
+    f = attn_work(B, n, H_q, d, C, K_top)
+    return dict(mac=f["mac"] // 2 * 5, exp=f["exp"], keys=f["keys"])

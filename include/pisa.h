@@ -247,13 +247,15 @@ pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void*
  * float32 [B][H_q][N_q], the forward's natural-log normaliser). Rows with no
  * visible key get dQ = 0. Outputs are device float32: dQ [B][N_q][H_q][d],
  * dK and dV [B][N_alloc][H_kv][d]; the call overwrites all of them (keys no
- * row selected get 0). The fp32 sums are accumulated with atomics, so their
- * last bits may differ between runs.
+ * row selected get 0). dK and dV are accumulated with fp32 atomics, so their
+ * last bits may differ between runs; dQ is summed in a fixed order. The
+ * workspace holds an fp32 dQ per (row, selected block, query head):
+ * B * N_q * H_q * K_top * d * 4 bytes plus the block clustering tables.
  * ws: device workspace of at least pisa_sparse_attn_bwd_workspace() bytes,
  * 256-byte aligned, owned by the caller, contents on entry ignored; calls
  * sharing a workspace must not overlap.
  * Supported: dt = PISA_BF16, d in {64, 128}, C in {16, 32, 64}, G_Q in
- * {1, 2, 4, 8, 16}, K_top <= 64, N_q < 2^25, B * N_q * H_q < 2^31.
+ * {1, 2, 4, 8, 16}, K_top <= 64, N_q < 2^25, B * N_q * H_q * K_top < 2^31.
  * Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE (ws too small), PISA_EHIP.
  */
 pisa_status pisa_sparse_attn_bwd_workspace(int32_t B, int64_t N_q, int64_t N_alloc, int32_t H_q,

@@ -207,3 +207,31 @@ def test_time_stage_validation(lib):
     assert lib.pisa_time_stage(-1, None, None) == EINVAL
     assert lib.pisa_time_stage(0, FAKE, None) == EINVAL
     assert lib.pisa_time_stage(0, None, None) == OK  # disarm
+
+
+def test_attention_backward_validation(lib):
+    n = pisa.c_size(0)
+    w = lib.pisa_sparse_attn_bwd_workspace
+    assert w(1, 65536, 65536, 32, 8, 128, 64, 8, ctypes.byref(n)) == OK
+    # one fp32 dQ row of d per (row, selected block, query head), plus the clustering tables
+    assert n.value >= 65536 * 32 * 8 * 128 * 4
+    assert w(1, 1024, 1024, 32, 8, 96, 64, 8, ctypes.byref(n)) == EUNSUPPORTED
+    assert w(1, 1024, 1024, 32, 8, 128, 64, 8, None) == EINVAL
+    b = lib.pisa_sparse_attn_bwd
+    WS = ctypes.c_void_p(0x100000)
+    need = pisa.sparse_attn_bwd_workspace_bytes(1, 10, 10, 8, 2, 128, 64, 8)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, pisa.BF16, 1, 10, 10, 10, 8, 2, 128, 64, FAKE, 8, 1, None,
+            FAKE, FAKE, FAKE]
+    assert b(*args, WS, need - 1, None) == ENOSPACE
+    assert b(*args, None, need, None) == EINVAL
+    assert b(*args, ctypes.c_void_p(0x100010), need, None) == EINVAL  # misaligned workspace
+    for k in (3, 4, 5, 19):  # O, dO, lse, dQ missing
+        a2 = list(args)
+        a2[k] = None
+        assert b(*a2, WS, need, None) == EINVAL
+    f32 = list(args)
+    f32[6] = pisa.F32
+    assert b(*f32, WS, need, None) == EUNSUPPORTED
+    bad = list(args)
+    bad[9] = 5  # N_kv < N_q
+    assert b(*bad, WS, need, None) == EINVAL

@@ -188,3 +188,16 @@ def test_attention_backward_full_size_64k():
         assert np.abs(sk).max() <= 1e-3 * np.abs(dK[0, :, h]).sum(0).max(), "key gradients do not sum to zero"
         want = dOf[seen[h]][:, h * G:(h + 1) * G].sum((0, 1))
         np.testing.assert_allclose(dV[0, :, h].sum(0), want, rtol=0, atol=1e-3 * np.abs(want).max() + 1e-2)
+
+
+def test_attention_backward_dq_is_deterministic():
+    """dQ is summed over a row's blocks in slot order: two runs give identical bits (dK and
+    dV take atomics and agree to rounding)."""
+    B, N, H_q, H_kv, d, C, K_top = 1, 3000, 8, 2, 128, 64, 8
+    Q, K, V, dO = _inputs(B, N, N, H_q, H_kv, d, seed=91)
+    sel = synth.random_selection(9, B, H_kv, N, K_top, C, [N], causal=True)
+    a = _gpu_grads(Q, K, V, dO, sel, C, N, True)
+    b = _gpu_grads(Q, K, V, dO, sel, C, N, True)
+    assert np.array_equal(a[0], b[0])
+    for x, y in zip(a[1:], b[1:]):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-5 * np.abs(x).max())
