@@ -64,6 +64,9 @@ def _load():
         lib.orc_sparse_attn_bwd.argtypes = [P, P, P, i64, P, P, P, P, i32, i64, i64, i32, i32, i32,
                                             i32, P, i32, i32, P, P, P, i32]
         lib.orc_sparse_attn_bwd.restype = i32
+        lib.orc_selection_quality.argtypes = [P, P, P, i64, P, i32, i64, i64, i32, i32, i32, i32, P,
+                                              i32, P, P, P, P, P, i32]
+        lib.orc_selection_quality.restype = i32
         lib.orc_bsa.argtypes = [P, P, P, i64, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
                                 i32, P, P, P, i32]
         lib.orc_bsa.restype = i32
@@ -220,6 +223,30 @@ def sparse_attn_bwd(Qi, item_b, item_t, K, V, dO, N: int, C: int, sel, causal: b
     if rc != 0:
         raise ValueError("oracle attention backward rejected its arguments")
     return dict(dQ=dQ, dK=dK, dV=dV)
+
+
+def selection_quality(Qi, item_b, item_t, K, N: int, C: int, sel, with_mass: bool = False,
+                      threads: int | None = None):
+    """Block-selection quality of sel [n][H][K_top] against full attention (eq 35-36,
+    55-57) for causal queries Qi [n][H_q][d] at positions item_t of sequences item_b.
+    Returns dict(recall, captured, ratio [n][H] f64, ref [n][H][K_top] int32 (the
+    full-attention reference set), mass [n][H][M_1] f64 or None)."""
+    Qi, K = _f32(Qi), _f32(K)
+    n, H_q, d = Qi.shape
+    B, N_alloc, H, _ = K.shape
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    Kt = sel.shape[2]
+    b, t = _items(item_b, item_t)
+    M1 = -(-int(N) // int(C))
+    mass = np.empty((n, H, M1)) if with_mass else None
+    ref = np.empty((n, H, Kt), dtype=np.int32)
+    rec, cap, rat = (np.empty((n, H)) for _ in range(3))
+    rc = _load().orc_selection_quality(_ptr(Qi), _ptr(b), _ptr(t), n, _ptr(K), B, N_alloc, int(N), H, H_q,
+                                       d, int(C), _ptr(sel), Kt, _ptr(mass), _ptr(ref), _ptr(rec),
+                                       _ptr(cap), _ptr(rat), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle selection quality rejected its arguments")
+    return dict(recall=rec, captured=cap, ratio=rat, ref=ref, mass=mass)
 
 
 def score(pyr: Pyramid, q, b: int, h: int, l: int, i: int, kind: str = "lse") -> float:

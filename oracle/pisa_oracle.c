@@ -710,6 +710,133 @@ int orc_sparse_attn_bwd(const float *Q, const int64_t *item_b, const int64_t *it
     return 0;
 }
 
+/* ---------------------------------------------------------------------------
+ * Block-selection quality against full attention (section 4.4 eq 35-36,
+ * appendix D.2 eq 55-57), causal. For query position i of sequence b, KV head h
+ * and its query heads h', over the eligible leaf blocks E_i = {0..c}, c = i / C:
+ *   a_{h'}(B) = log sum_{t in B, t <= i} exp(q_{i,h'} . k_{t,h} / sqrt(d))   (eq 55)
+ *   P(B) = (1/G) sum_{h'} exp(a_{h'}(B)) / sum_{B' in E_i} exp(a_{h'}(B'))  (eq 56)
+ * The reference set keeps the forced blocks (first, previous, current) and
+ * fills the remaining K_top - |F| slots with the other eligible blocks of
+ * highest P (ties to the lower index); all of E_i when |E_i| <= K_top. For the
+ * selector's set I (sel, -1 entries ignored):
+ *   Recall@K = |I cap I_full| / K_top                                     (eq 35)
+ *   Captured = sum_{B in I} P(B)                                           (eq 57)
+ *   MassRatio = Captured / sum_{B in I_full} P(B)                          (eq 36)
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const float *Q, *K;
+    const int64_t *item_b, *item_t;
+    const int32_t *sel;
+    int64_t n_items, N, N_alloc;
+    int H, H_q, d, C, K_top;
+    double *mass;            /* [n_items][H][M_1] or NULL */
+    int32_t *ref;            /* [n_items][H][K_top] */
+    double *recall, *captured, *ratio;  /* [n_items][H] */
+    int nthreads;
+} orc_quality;
+
+static void quality_one(const orc_quality *P, int64_t item, int h)
+{
+    int G = P->H_q / P->H;
+    int64_t i = P->item_t[item], b = P->item_b[item];
+    int64_t c = i / P->C, nE = c + 1, M1 = (P->N + P->C - 1) / P->C;
+    double scale = 1.0 / sqrt((double)P->d);
+    double *Pm = calloc((size_t)nE, sizeof(double));
+    double *a = malloc(sizeof(double) * (size_t)nE);
+    double *z = malloc(sizeof(double) * (size_t)P->C);
+    for (int g2 = 0; g2 < G; g2++) {
+        const float *q = P->Q + (item * P->H_q + h * G + g2) * P->d;
+        for (int64_t B = 0; B < nE; B++) {
+            int64_t lo = B * P->C, hi = B * P->C + P->C;
+            if (hi > i + 1) hi = i + 1;
+            int64_t n = 0;
+            for (int64_t t = lo; t < hi; t++)
+                z[n++] = dot_ff(q, P->K + ((b * P->N_alloc + t) * P->H + h) * (int64_t)P->d, P->d) * scale;
+            a[B] = logsumexp(z, n);
+        }
+        double la = logsumexp(a, nE);
+        for (int64_t B = 0; B < nE; B++) Pm[B] += exp(a[B] - la) / (double)G;
+    }
+    int Kt = P->K_top;
+    int32_t *ref = P->ref + (item * P->H + h) * (int64_t)Kt;
+    int nr = 0;
+    if (nE <= Kt) {
+        for (int64_t B = 0; B < nE; B++) ref[nr++] = (int32_t)B;
+    } else {
+        char *in = calloc((size_t)nE, 1);
+        in[0] = 1; in[c] = 1; in[c - 1] = 1;  /* nE > K_top >= 3: c >= 3 */
+        int nF = 3;
+        for (int k = 0; k < Kt - nF; k++) {
+            int64_t best = -1;
+            for (int64_t B = 0; B < nE; B++)
+                if (!in[B] && (best < 0 || Pm[B] > Pm[best])) best = B;
+            in[best] = 1;
+        }
+        for (int64_t B = 0; B < nE; B++)
+            if (in[B]) ref[nr++] = (int32_t)B;
+        free(in);
+    }
+    for (int k = nr; k < Kt; k++) ref[k] = -1;
+    const int32_t *s = P->sel + (item * P->H + h) * (int64_t)Kt;
+    double cap = 0.0, cap_ref = 0.0;
+    int hit = 0;
+    for (int k = 0; k < Kt; k++) {
+        if (s[k] >= 0 && s[k] < nE) {
+            cap += Pm[s[k]];
+            for (int r = 0; r < nr; r++) hit += ref[r] == s[k];
+        }
+    }
+    for (int r = 0; r < nr; r++) cap_ref += Pm[ref[r]];
+    int64_t o = item * P->H + h;
+    P->recall[o] = (double)hit / (double)Kt;
+    P->captured[o] = cap;
+    P->ratio[o] = cap / cap_ref;
+    if (P->mass) {
+        double *m = P->mass + o * M1;
+        for (int64_t B = 0; B < M1; B++) m[B] = B < nE ? Pm[B] : 0.0;
+    }
+    free(Pm);
+    free(a);
+    free(z);
+}
+
+typedef struct { const orc_quality *P; int tid; } quality_arg;
+
+static void *quality_worker(void *p)
+{
+    quality_arg *w = p;
+    const orc_quality *P = w->P;
+    for (int64_t k = w->tid; k < P->n_items * P->H; k += P->nthreads)
+        quality_one(P, k / P->H, (int)(k % P->H));
+    return NULL;
+}
+
+/* Selection quality of sel [n_items][H][K_top] for causal queries at positions
+ * item_t of sequences item_b (K_top >= 3). Returns 0, or -1 on bad input. */
+int orc_selection_quality(const float *Q, const int64_t *item_b, const int64_t *item_t,
+                          int64_t n_items, const float *K, int B, int64_t N_alloc, int64_t N,
+                          int H, int H_q, int d, int C, const int32_t *sel, int K_top,
+                          double *mass, int32_t *ref, double *recall, double *captured,
+                          double *ratio, int nthreads)
+{
+    if (B < 1 || N < 1 || N > N_alloc || H < 1 || H_q < H || H_q % H || d < 1 || C < 1 || K_top < 3)
+        return -1;
+    for (int64_t k = 0; k < n_items; k++)
+        if (item_b[k] < 0 || item_b[k] >= B || item_t[k] < 0 || item_t[k] >= N) return -1;
+    orc_quality P = {Q, K, item_b, item_t, sel, n_items, N, N_alloc, H, H_q, d, C, K_top,
+                     mass, ref, recall, captured, ratio, nthreads < 1 ? 1 : nthreads};
+    if (P.nthreads > 256) P.nthreads = 256;
+    pthread_t th[256];
+    quality_arg wa[256];
+    for (int k = 0; k < P.nthreads; k++) {
+        wa[k].P = &P; wa[k].tid = k;
+        pthread_create(&th[k], NULL, quality_worker, &wa[k]);
+    }
+    for (int k = 0; k < P.nthreads; k++) pthread_join(th[k], NULL);
+    return 0;
+}
+
 /* One block score s^(l)_{t,i} for one query head: kind 0 the LSE of eq 21,
  * kind 1 / 2 the PISA-1 / PISA-2 scores of eq 33-34; exposed so tests can check
  * the score definitions themselves. q: d floats of one query head. */

@@ -44,6 +44,10 @@ MUTANTS = [
     ("bwd_dk_unscaled", "P->dK[row + e] += dz * scale * (double)q[e];", "P->dK[row + e] += dz * (double)q[e];"),
     ("bwd_dv_unnormalised", "P->dV[row + e] += p * (double)dO[e];", "P->dV[row + e] += exp(z[k]) * (double)dO[e];"),
     ("bwd_saved_output_ignored", "if (P->Osaved) pdp = dot_ff(", "if (0) pdp = dot_ff("),
+    ("quality_mass_not_normalised", "Pm[B] += exp(a[B] - la) / (double)G;", "Pm[B] += exp(a[B]) / (double)G;"),
+    ("quality_recall_denominator", "P->recall[o] = (double)hit / (double)Kt;",
+     "P->recall[o] = (double)hit / (double)(Kt + 1);"),
+    ("quality_future_key", "if (hi > i + 1) hi = i + 1;", "if (hi > i + 2) hi = i + 2;"),
     ("bwd_mask_self", "if (P->causal && t < j) continue;", "if (P->causal && t <= j) continue;"),
     ("ascending_scores", "if (x->u > y->u) return -1;\n    if (x->u < y->u) return 1;",
      "if (x->u < y->u) return -1;\n    if (x->u > y->u) return 1;"),

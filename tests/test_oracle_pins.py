@@ -671,3 +671,73 @@ def test_attn_bwd_saved_output_form():
     want = g1["dQ"] - dD[..., None] * kbar / math.sqrt(d)
     np.testing.assert_allclose(g2["dQ"], want, rtol=0, atol=1e-9)
     np.testing.assert_allclose(g2["dV"], g1["dV"], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Block-selection quality against full attention (section 4.4 eq 35-36,
+# appendix D.2 eq 55-57)
+# --------------------------------------------------------------------------
+def _quality_problem(seed, N=160, C=8, H=2, Hq=4, d=8, Kt=5):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    Q = (1.5 * rng.standard_normal((N, Hq, d))).astype(np.float32)
+    sel = _random_selection(rng, N, H, C, Kt, True)
+    return rng, Q, K, sel, N, C, H, Hq, d, Kt
+
+
+def test_block_mass_is_dense_softmax_summed_per_block():
+    """P(B) (eq 56) = the head average of each head's full causal softmax summed over the
+    block's tokens: torch float64 softmax over the whole causal prefix as the reference."""
+    _, Q, K, sel, N, C, H, Hq, d, Kt = _quality_problem(46)
+    t = np.arange(N)
+    r = oracle.selection_quality(Q, [0] * N, t, K, N, C, sel, with_mass=True)
+    G = Hq // H
+    q = torch.from_numpy(Q).double().permute(1, 0, 2)
+    k = torch.from_numpy(K[0]).double().permute(1, 0, 2).repeat_interleave(G, 0)
+    s = q @ k.transpose(1, 2) / math.sqrt(d)
+    s = s.masked_fill(~torch.ones(N, N, dtype=torch.bool).tril(), float("-inf"))
+    p = torch.softmax(s, -1).reshape(Hq, N, N // C, C).sum(-1)   # [Hq][N][M1]
+    want = p.reshape(H, G, N, N // C).mean(1).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(r["mass"], want, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["mass"].sum(-1), 1.0, atol=1e-12)
+
+
+def test_reference_set_maximises_captured_mass():
+    """The reference set (forced blocks plus the highest-mass others) captures the most
+    mass of any set of K_top blocks holding the forced ones (brute force over subsets),
+    and is the lower-index choice among equal masses; a selection equal to it has
+    Recall@K = MassRatio = 1, and known overlaps give Recall@K = overlap / K_top."""
+    import itertools
+    _, Q, K, sel, N, C, H, Hq, d, Kt = _quality_problem(47, N=88, C=8)
+    t = np.arange(N)
+    r = oracle.selection_quality(Q, [0] * N, t, K, N, C, sel, with_mass=True)
+    for n in range(0, N, 7):
+        c = n // C
+        for h in range(H):
+            ref = [x for x in r["ref"][n, h] if x >= 0]
+            if c + 1 <= Kt:
+                assert ref == list(range(c + 1))
+                continue
+            F = {0, c - 1, c}
+            others = [B for B in range(c + 1) if B not in F]
+            m = r["mass"][n, h]
+            best = max(itertools.combinations(others, Kt - 3), key=lambda S: (sum(m[list(S)]), [-x for x in S]))
+            assert ref == sorted(F | set(best))
+    r2 = oracle.selection_quality(Q, [0] * N, t, K, N, C, r["ref"])
+    np.testing.assert_allclose(r2["ratio"], 1.0, atol=1e-12)
+    full = np.array([[c + 1 > Kt for _ in range(H)] for c in t // C])
+    assert (r2["recall"][full] == 1.0).all()
+    # swap one non-forced reference block for an eligible block outside it: recall drops by 1/K
+    alt = r["ref"].copy()
+    for n in range(N):
+        c = n // C
+        if c + 1 <= Kt:
+            continue
+        for h in range(H):
+            out = [B for B in range(c + 1) if B not in alt[n, h]]
+            row = sorted([x for x in alt[n, h] if x not in (0, c - 1, c)][1:] + [0, c - 1, c, out[0]])
+            alt[n, h] = row
+    r3 = oracle.selection_quality(Q, [0] * N, t, K, N, C, alt)
+    np.testing.assert_allclose(r3["recall"][full], (Kt - 1) / Kt, atol=0)
+    assert (r3["ratio"][full] <= 1.0 + 1e-12).all()
+    np.testing.assert_allclose(r3["captured"], (r3["ratio"] * r2["captured"]), rtol=1e-12)
