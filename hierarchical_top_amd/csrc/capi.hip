@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "attn_bwd.hpp"
+#include "quality.hpp"
 #include "pisa_internal.hpp"
 
 using namespace pisa;
@@ -592,6 +593,53 @@ pisa_status pisa_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
     hipError_t e = launch_attn_bwd(a, d, (char*)ws, (hipStream_t)stream);
     stage_mark(PISA_STAGE_ATTN_BWD, true, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn_bwd");
+}
+
+static pisa_status check_quality(int32_t B, int64_t N, int32_t H_q, int32_t C)
+{
+    if (B < 1 || N < 1 || H_q < 1) return fail(PISA_EINVAL, "need B, N, H_q >= 1");
+    if (C != 16 && C != 32 && C != 64) return fail(PISA_EUNSUPPORTED, "C=%d (supported: 16, 32, 64)", C);
+    if (N > ((int64_t)1 << 20)) return fail(PISA_EUNSUPPORTED, "selection quality needs N <= 2^20");
+    return PISA_OK;
+}
+
+pisa_status pisa_selection_quality_workspace(int32_t B, int64_t N, int32_t H_q, int32_t C, size_t* bytes)
+{
+    if (!bytes) return fail(PISA_EINVAL, "bytes must be non-NULL");
+    pisa_status st = check_quality(B, N, H_q, C);
+    if (st != PISA_OK) return st;
+    *bytes = quality_workspace_bytes(B, N, H_q, C);
+    return ok();
+}
+
+pisa_status pisa_selection_quality(const void* Q, const void* K, pisa_dtype dt, int32_t B, int64_t N, int32_t H_q,
+                                   int32_t H_kv, int32_t d, int32_t C, const int32_t* sel, int32_t K_top, float* mass,
+                                   int32_t* ref, float* recall, float* captured, float* ratio, void* ws,
+                                   size_t ws_bytes, void* stream)
+{
+    if (!dtype_ok(dt)) return fail(PISA_EINVAL, "dtype %d is not PISA_F32 or PISA_BF16", (int)dt);
+    if (dt != PISA_BF16) return fail(PISA_EUNSUPPORTED, "selection quality takes bf16 inputs");
+    pisa_status st = check_quality(B, N, H_q, C);
+    if (st != PISA_OK) return st;
+    if (H_kv < 1 || H_q % H_kv) return fail(PISA_EINVAL, "H_q must be a positive multiple of H_kv");
+    const int G = H_q / H_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return fail(PISA_EUNSUPPORTED, "G_Q=%d", G);
+    if (d != 64 && d != 128) return fail(PISA_EUNSUPPORTED, "d=%d (supported: 64, 128)", d);
+    if (K_top < 3) return fail(PISA_EINVAL, "K_top=%d < 3 (the forced blocks)", K_top);
+    if (K_top > 16) return fail(PISA_EUNSUPPORTED, "selection quality supports K_top <= 16");
+    if (!Q || !K || !sel || !recall || !captured || !ratio || !ws)
+        return fail(PISA_EINVAL, "Q, K, sel, recall, captured, ratio and ws must be non-NULL");
+    if (!aligned16(Q) || !aligned16(K)) return fail(PISA_EINVAL, "Q and K must be 16-byte aligned");
+    const size_t need = quality_workspace_bytes(B, N, H_q, C);
+    if (ws_bytes < need) return fail(PISA_ENOSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+    if (((uintptr_t)ws & 15) != 0) return fail(PISA_EINVAL, "ws must be 16-byte aligned");
+    QualArgs a;
+    memset(&a, 0, sizeof(a));
+    a.Q = Q; a.K = K; a.B = B; a.H_q = H_q; a.H_kv = H_kv; a.G = G; a.C = C; a.K_top = K_top;
+    a.N = N; a.M1 = (N + C - 1) / C; a.sel = sel; a.lmass = (float*)ws; a.mass = mass; a.ref = ref;
+    a.recall = recall; a.captured = captured; a.ratio = ratio;
+    hipError_t e = launch_quality(a, d, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "pisa_selection_quality");
 }
 
 pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt, int64_t N, int32_t H_q,

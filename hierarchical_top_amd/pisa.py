@@ -73,6 +73,9 @@ def lib():
                                                ctypes.POINTER(c_size)],
             "pisa_sparse_attn_bwd": [c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32,
                                      c_i32, c_i32, c_p, c_i32, c_i32, c_p, c_p, c_p, c_p, c_p, c_size, c_p],
+            "pisa_selection_quality_workspace": [c_i32, c_i64, c_i32, c_i32, ctypes.POINTER(c_size)],
+            "pisa_selection_quality": [c_p, c_p, c_i32, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_i32, c_p,
+                                       c_p, c_p, c_p, c_p, c_p, c_size, c_p],
             "pisa_bsa_select": [P, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_time_stage": [c_i32, c_p, c_p],
             "pisa_time_stage_pending": [c_i32],
@@ -94,7 +97,7 @@ def lib():
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
            "pisa_route_prefill", "pisa_route_prefill_scored", "pisa_route_decode", "pisa_sparse_attn", "pisa_sparse_attn_workspace",
            "pisa_sparse_attn_clustered", "pisa_sparse_attn_bwd_workspace", "pisa_sparse_attn_bwd",
-           "pisa_bsa_select", "pisa_time_stage",
+           "pisa_selection_quality_workspace", "pisa_selection_quality", "pisa_bsa_select", "pisa_time_stage",
            "pisa_time_stage_pending",
            "pisa_status_str", "pisa_last_error", "pisa_abi_version"]
 
@@ -284,6 +287,29 @@ def sparse_attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.
                                       _ptr(kv_len), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream()))
     return dQ, dK, dV
+
+
+def selection_quality(Q: torch.Tensor, K: torch.Tensor, sel: torch.Tensor, C: int, with_mass: bool = False,
+                      with_ref: bool = False):
+    """Quality of the causal selection sel [B][H_kv][N][K_top] against full attention (bf16 Q, K):
+    returns dict(recall, captured, ratio [B][H_kv][N] fp32, mass [B][H_kv][N][M1] and ref
+    [B][H_kv][N][K_top] when asked)."""
+    _dev(Q, K, sel)
+    B, N, H_q, d = Q.shape
+    H_kv = K.shape[2]
+    K_top = sel.shape[-1]
+    M1 = -(-N // C)
+    n = c_size(0)
+    _check(lib().pisa_selection_quality_workspace(B, N, H_q, C, ctypes.byref(n)))
+    ws = torch.empty(max(int(n.value), 16), dtype=torch.uint8, device=Q.device)
+    f = dict(device=Q.device, dtype=torch.float32)
+    out = {k: torch.empty(B, H_kv, N, **f) for k in ("recall", "captured", "ratio")}
+    out["mass"] = torch.empty(B, H_kv, N, M1, **f) if with_mass else None
+    out["ref"] = torch.empty(B, H_kv, N, K_top, dtype=torch.int32, device=Q.device) if with_ref else None
+    _check(lib().pisa_selection_quality(_ptr(Q), _ptr(K), _dt(Q), B, N, H_q, H_kv, d, C, _ptr(sel), K_top,
+                                        _ptr(out["mass"]), _ptr(out["ref"]), _ptr(out["recall"]),
+                                        _ptr(out["captured"]), _ptr(out["ratio"]), _ptr(ws), ws.numel(), _stream()))
+    return out
 
 
 def bsa_select(pyr: Pyramid, Q: torch.Tensor, N: int, K_top: int, causal: bool = True, with_score: bool = False,

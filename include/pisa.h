@@ -286,6 +286,38 @@ pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt,
                             int32_t* idx, float* score, void* stream);
 
 /*
+ * Block-selection quality against full attention (section 4.4 eq 35-36;
+ * appendix D.2 eq 55-57), causal. For row r (position r) of sequence b and KV
+ * head h with query heads h', over the eligible leaf blocks B = 0..c, c = r / C:
+ *   a_{h'}(B) = log sum_{t in B, t <= r} exp(q_{r,h'} . k_{t,h} / sqrt(d)),
+ *   P(B) = (1/G_Q) sum_{h'} exp(a_{h'}(B)) / sum_{B'} exp(a_{h'}(B'))
+ * (the block's share of full attention, averaged over the group). The
+ * reference set keeps the first, previous and current blocks and the K_top - 3
+ * other blocks of highest P (ties to the lower index), or every eligible block
+ * when at most K_top are eligible. For the selector's blocks sel:
+ *   recall = |sel cap ref| / K_top, captured = sum_{B in sel} P(B),
+ *   ratio = captured / sum_{B in ref} P(B).
+ * Q: device bf16 [B][N][H_q][d]; K: device bf16 [B][N][H_kv][d];
+ * sel: device int32 [B][H_kv][N][K_top] (-1 entries and blocks after the row's
+ * block are ignored). Outputs (device): mass float32 [B][H_kv][N][M_1] or NULL
+ * (0 past the row's block), ref int32 [B][H_kv][N][K_top] or NULL (ascending,
+ * -1 padded), recall, captured, ratio float32 [B][H_kv][N].
+ * ws: device workspace of at least pisa_selection_quality_workspace() bytes
+ * (B * H_q * N * M_1 * 4: the log masses), contents on entry ignored.
+ * The full-attention masses cost O(N^2 d) per head: an evaluation tool for
+ * N up to about 64K, not a selector. Supported: d in {64, 128}; C in
+ * {16, 32, 64}; G_Q in {1, 2, 4, 8, 16}; 3 <= K_top <= 16.
+ * Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE, PISA_EHIP.
+ */
+pisa_status pisa_selection_quality_workspace(int32_t B, int64_t N, int32_t H_q, int32_t C,
+                                             size_t* bytes);
+pisa_status pisa_selection_quality(const void* Q, const void* K, pisa_dtype dt, int32_t B,
+                                   int64_t N, int32_t H_q, int32_t H_kv, int32_t d, int32_t C,
+                                   const int32_t* sel, int32_t K_top, float* mass, int32_t* ref,
+                                   float* recall, float* captured, float* ratio, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/*
  * Stage timing, for measurement. The library queues each call as one or more
  * kernel stages; a stage may run several times in one call (once per level).
  * pisa_time_stage appends a pair of caller-created hipEvent_t (passed as

@@ -235,3 +235,28 @@ def test_attention_backward_validation(lib):
     bad = list(args)
     bad[9] = 5  # N_kv < N_q
     assert b(*bad, WS, need, None) == EINVAL
+
+
+def test_selection_quality_validation(lib):
+    n = pisa.c_size(0)
+    w = lib.pisa_selection_quality_workspace
+    assert w(1, 16384, 16, 64, ctypes.byref(n)) == OK and n.value == 16 * 16384 * 256 * 4
+    assert w(1, 16384, 16, 48, ctypes.byref(n)) == EUNSUPPORTED
+    assert w(0, 16384, 16, 64, ctypes.byref(n)) == EINVAL
+    q = lib.pisa_selection_quality
+    WS = ctypes.c_void_p(0x100000)
+    args = [FAKE, FAKE, pisa.BF16, 1, 100, 8, 2, 128, 16, FAKE, 8, None, None, FAKE, FAKE, FAKE]
+    need = 8 * 100 * 7 * 4
+    assert q(*args, WS, need - 1, None) == ENOSPACE
+    k2 = list(args)
+    k2[10] = 2
+    assert q(*k2, WS, need, None) == EINVAL            # no room for the forced blocks
+    k17 = list(args)
+    k17[10] = 17
+    assert q(*k17, WS, need, None) == EUNSUPPORTED
+    g3 = list(args)
+    g3[6] = 3
+    assert q(*g3, WS, need, None) == EINVAL            # H_q not a multiple of H_kv
+    nul = list(args)
+    nul[13] = None
+    assert q(*nul, WS, need, None) == EINVAL
