@@ -331,6 +331,8 @@ def prefill_extra(name, reps, with_attn=False):
     # (whose level-1 means come from the same build)
     bms = time_fn(lambda: P.pyr.build(P.K, w.N), reps)
     out["build_ms"] = bms
+    if name == "p16k":
+        out["selection_quality"] = selection_quality_table(P)
     out["speedup_vs_bsa"] = (out["bsa_ms"] + bms) / best
     if with_attn:
         P.step(pisa.LEVELS)
@@ -364,6 +366,29 @@ def prefill_extra(name, reps, with_attn=False):
     del P
     torch.cuda.empty_cache()
     return out
+
+
+def selection_quality_table(P):
+    """Recall@K, captured mass and mass ratio against full attention (section 4.4, appendix
+    D.2) of PISA and its score ablations (level router) and of the exhaustive BSA-style
+    selector, averaged over the rows with more than K_top eligible blocks, as the appendix
+    does. Synthetic planted inputs: not comparable with the appendix's model activations."""
+    w = P.w
+    rows = torch.arange(w.N, device="cuda") // w.C + 1 > w.K_top
+    res = {}
+    sels = {}
+    for kind in ("lse", "mean", "mean_var"):
+        P.pyr.build(P.K, w.N)
+        pisa.route_prefill(P.pyr, P.Q, P.K, w.N, w.K_top, mode=pisa.LEVELS, workspace=P.ws, out=P.idx,
+                           score_kind=kind)
+        sels[{"lse": "pisa", "mean": "pisa1", "mean_var": "pisa2"}[kind]] = P.idx.clone()
+    P.bsa()
+    sels["bsa"] = P.bidx.clone()
+    for name, sel in sels.items():
+        q = pisa.selection_quality(P.Q, P.K, sel, w.C)
+        res[name] = {k: float(q[k][:, :, rows].double().mean()) for k in ("recall", "captured", "ratio")}
+    res["rows"] = int(rows.sum()) * w.B * w.H_kv
+    return res
 
 
 PAPER_SWEEP_N = (4096, 8192, 16384, 32768, 65536, 131072, 262144)
