@@ -104,6 +104,22 @@ class Prefill:
         pisa.bsa_select(self.pyr, self.Q, w.N, w.K_top, out=self.bidx)
 
 
+def graph_ms(fn, reps):
+    """ms per replay of fn captured in a HIP graph (torch.cuda.CUDAGraph on its stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    ms = time_fn(g.replay, reps)
+    del g
+    return ms
+
+
 def time_fn(fn, reps, warm=2):
     for _ in range(warm):
         fn()
@@ -324,6 +340,10 @@ def prefill_extra(name, reps, with_attn=False):
         out["route_ms_" + mname] = time_fn(lambda: P.route_only(mode), reps)
     best = min(out["build_route_ms_" + m] for m in MODES)
     out["routed_queries_per_s"] = w.B * w.N / (best * 1e-3)
+    # the same build + level route captured once in a HIP graph and replayed: at short
+    # lengths the route is a chain of small launches whose gaps a graph removes
+    out["build_route_ms_levels_graph"] = graph_ms(lambda: P.step(pisa.LEVELS), reps)
+    out["routed_queries_per_s_graph"] = w.B * w.N / (out["build_route_ms_levels_graph"] * 1e-3)
     out["bsa_ms"] = time_fn(P.bsa, max(2, reps // 2))
     bw = workcount.bsa_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.K_top)
     out["bsa_alg_tflops_one_pass"] = 2 * bw["mac"] / (out["bsa_ms"] * 1e-3) / 1e12
