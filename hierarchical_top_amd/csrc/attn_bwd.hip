@@ -84,20 +84,30 @@ __global__ __launch_bounds__(256) void dsum_kernel(AttnBwdArgs a)
     }
 }
 
+// Column position of (d, column) in the transposed q / dO tiles: columns are XOR-swizzled in
+// groups of four by d / 8, so that the 16-bit stores of the eight d of a 16-byte piece (one
+// piece per thread, consecutive threads on consecutive d / 8) fall in different banks while a
+// lane's four consecutive columns of one d stay one 8-byte read. Needs 32 | columns.
+__device__ __forceinline__ int tcol(int d, int col) { return col ^ (((d >> 3) & 7) << 2); }
+
 template <int D, int C>
 struct BwdGeom {
     static constexpr int KS = D / 32;          // k-steps of S = Q K^T and dP = dO V^T
     static constexpr int DT = D / 16;          // d tiles
     static constexpr int TPC = C / 16;         // key tiles
-    static constexpr int NCT = 4 / TPC;        // column tiles per iteration
+    static constexpr int NCT = 4 / TPC;        // waves per key tile
+    static constexpr int CPW = C == 64 ? 2 : 1;  // column tiles per wave and iteration
     static constexpr int PS = (C + 31) / 32;   // 32-key steps of dQ = dS K
-    static constexpr int NCOL = 16 * NCT;      // columns per iteration
+    static constexpr int NCOL = 16 * NCT * CPW;  // columns per iteration
     static constexpr int LDW = D + 8;          // [column][d] row stride (bf16)
     static constexpr int TW = NCOL + 4;        // [d][column] row stride (bf16)
     static constexpr int KW = PS * 32 + 8;     // [d][key] and [column][key] row strides (bf16)
     static constexpr int CH = D / 8;           // 16-byte pieces of a row
     static constexpr int NPT = (NCOL * CH + 255) / 256;  // pieces per thread and tensor per iteration
-    static constexpr int DQT = NCT * DT / 4;   // dQ tiles per wave per iteration
+    static constexpr int DQT = (NCOL / 16) * DT / 4;  // dQ tiles per wave per iteration
+    // loads issued two iterations ahead (two register sets) for d = 64; at d = 128 the second
+    // set does not fit in registers next to the accumulators
+    static constexpr bool PD2 = D == 64;
     // LDS: q, dO [NCOL][LDW]; q^T, dO^T [D][TW]; K^T [D][KW]; dS hi, lo [NCOL][KW]; column metadata; entries
     static constexpr size_t OFF_Q = 0;
     static constexpr size_t OFF_DO = OFF_Q + (size_t)NCOL * LDW * 2;
@@ -110,14 +120,16 @@ struct BwdGeom {
     static constexpr size_t OFF_ENT = OFF_META + (size_t)NCOL * 16;  // lse2, dsum (float), vis (int), dQ row (int)
     static constexpr size_t BYTES = OFF_ENT + (size_t)kLeafQC * 4;
     static_assert(TPC * NCT == 4, "four waves cover the key tiles times the column tiles");
-    static_assert((NCT * DT) % 4 == 0, "dQ tiles spread evenly over the waves");
+    static_assert(NCOL % 32 == 0, "the transposed tiles' column swizzle spans 32 columns");
+    static_assert(((NCOL / 16) * DT) % 4 == 0, "dQ tiles spread evenly over the waves");
 };
 
 template <int D, int C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_kernel(AttnBwdArgs A)
 {
     using Gm = BwdGeom<D, C>;
-    constexpr int KS = Gm::KS, DT = Gm::DT, TPC = Gm::TPC, PS = Gm::PS, NCOL = Gm::NCOL;
+    constexpr int KS = Gm::KS, DT = Gm::DT, TPC = Gm::TPC, NCT = Gm::NCT, CPW = Gm::CPW, PS = Gm::PS;
+    constexpr int NCOL = Gm::NCOL;
     constexpr int LDW = Gm::LDW, TW = Gm::TW, KW = Gm::KW, CH = Gm::CH, NPT = Gm::NPT;
     extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
     bf16* s_q = reinterpret_cast<bf16*>(s_raw + Gm::OFF_Q);
@@ -187,11 +199,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
     __syncthreads();  // entries in LDS
 
-    // global -> registers for one iteration: q and dO pieces (column, 8 d), and per column its metadata
-    bf16x8 rq[NPT], rdo[NPT];
-    float m_lse2 = INFINITY, m_dsum = 0.f;
-    int m_vis = 0, m_row = -1;
-    auto load_it = [&](int it) {
+    // global -> registers for one iteration: q and dO pieces (column, 8 d), and per column its
+    // metadata; two sets, so that an iteration's loads are issued two iterations before use
+    struct Regs {
+        bf16x8 q[NPT], o[NPT];
+        float lse2, dsum;
+        int vis, row;
+    };
+    auto load_it = [&](int it, Regs& R) {
 #pragma unroll
         for (int j = 0; j < NPT; ++j) {
             const int p = tid + 256 * j;
@@ -200,9 +215,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             const int ent = s_ent[el < n ? el : n - 1];
             const int64_t r = (uint32_t)ent >> 6;
             const int64_t off = (((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head) * D + 8 * dc;
-            rq[j] = load8h(Qg + off);
-            rdo[j] = load8h(dOg + off);
+            R.q[j] = load8h(Qg + off);
+            R.o[j] = load8h(dOg + off);
         }
+        R.lse2 = INFINITY;  // padding column: p = 2^-inf = 0
+        R.dsum = 0.f;
+        R.vis = 0;
+        R.row = -1;
         if (tid < NCOL) {
             const int col = tid;
             const int el = it * epi + col / G, head = col % G;
@@ -210,48 +229,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 const int ent = s_ent[el];
                 const int64_t r = (uint32_t)ent >> 6;
                 const int64_t li = ((int64_t)b * a.H_q + (int64_t)h * G + head) * a.N_q + r;
-                m_lse2 = A.lse[li] * kLog2e;
-                m_dsum = A.dsum[li];
+                R.lse2 = A.lse[li] * kLog2e;
+                R.dsum = A.dsum[li];
                 int64_t kend = k0 + C < nb ? k0 + C : nb;
                 const int64_t pos = nb - a.N_q + r;
                 if (a.causal && kend > pos + 1) kend = pos + 1;
-                m_vis = (int)(kend - k0);
-                m_row = (int)(((bh * a.N_q + r) * a.K_top + (ent & 63)) * G + head);
-            } else {
-                m_lse2 = INFINITY;  // padding column: p = 2^-inf = 0
-                m_dsum = 0.f;
-                m_vis = 0;
-                m_row = -1;
+                R.vis = (int)(kend - k0);
+                R.row = (int)(((bh * a.N_q + r) * a.K_top + (ent & 63)) * G + head);
             }
         }
     };
-    auto store_it = [&]() {
+    auto store_it = [&](const Regs& R) {
 #pragma unroll
         for (int j = 0; j < NPT; ++j) {
             const int p = tid + 256 * j;
             if (p < NCOL * CH) {
                 const int col = p / CH, dc = p % CH;
-                *reinterpret_cast<bf16x8*>(s_q + col * LDW + 8 * dc) = rq[j];
-                *reinterpret_cast<bf16x8*>(s_do + col * LDW + 8 * dc) = rdo[j];
+                *reinterpret_cast<bf16x8*>(s_q + col * LDW + 8 * dc) = R.q[j];
+                *reinterpret_cast<bf16x8*>(s_do + col * LDW + 8 * dc) = R.o[j];
+                const int tc = tcol(8 * dc, col);  // the same for the eight d of the piece
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    s_qt[(8 * dc + k) * TW + col] = rq[j][k];
-                    s_dot[(8 * dc + k) * TW + col] = rdo[j][k];
+                    s_qt[(8 * dc + k) * TW + tc] = R.q[j][k];
+                    s_dot[(8 * dc + k) * TW + tc] = R.o[j][k];
                 }
             }
         }
         if (tid < NCOL) {
-            s_lse2[tid] = m_lse2;
-            s_dsum[tid] = m_dsum;
-            s_vis[tid] = m_vis;
-            s_dqrow[tid] = m_row;
+            s_lse2[tid] = R.lse2;
+            s_dsum[tid] = R.dsum;
+            s_vis[tid] = R.vis;
+            s_dqrow[tid] = R.row;
         }
     };
 
     const float sc2 = kLog2e * rsqrtf((float)D);  // logits in base 2
     const float inv_sqrt_d = rsqrtf((float)D);
     const int key = kt * 16 + (lane & 15);
-    const int cb = 16 * ct;  // this wave's column tile within the iteration
     f32x4 accV[DT], accK[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -259,50 +273,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         accK[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    load_it(0);
-    store_it();
-    __syncthreads();
-    for (int it = 0; it < n_it; ++it) {
-        if (it + 1 < n_it) load_it(it + 1);  // in flight during this iteration's products
-        // S and dP for (this wave's 16 columns) x (its 16 keys): lane = key, columns cb + 4 lg + i
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one iteration over the columns in LDS: this wave's CPW column tiles against its key tile
+    auto compute = [&]() {
+#pragma unroll 1
+        for (int j = 0; j < CPW; ++j) {
+            const int cb = 16 * (ct + NCT * j);
+            // S and dP for 16 columns x this wave's 16 keys: lane = key, columns cb + 4 lg + i
+            f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 aq = *reinterpret_cast<const bf16x8*>(s_q + (cb + (lane & 15)) * LDW + 32 * s + 8 * lg);
-            const bf16x8 ad = *reinterpret_cast<const bf16x8*>(s_do + (cb + (lane & 15)) * LDW + 32 * s + 8 * lg);
-            sacc = mfma(aq, bK[s], sacc);
-            pacc = mfma(ad, bV[s], pacc);
-        }
-        bf16x4 ph, pl, dh, dl;
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(s_q + (cb + (lane & 15)) * LDW + 32 * s + 8 * lg);
+                const bf16x8 ad = *reinterpret_cast<const bf16x8*>(s_do + (cb + (lane & 15)) * LDW + 32 * s + 8 * lg);
+                sacc = mfma(aq, bK[s], sacc);
+                pacc = mfma(ad, bV[s], pacc);
+            }
+            bf16x4 ph, pl, dh, dl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = cb + 4 * lg + i;
-            const float p = key < s_vis[c] ? __builtin_amdgcn_exp2f(sacc[i] * sc2 - s_lse2[c]) : 0.f;
-            const float ds = p * (pacc[i] - s_dsum[c]);
-            ph[i] = to_bf16(p);
-            pl[i] = to_bf16(p - from_bf16(ph[i]));
-            dh[i] = to_bf16(ds);
-            dl[i] = to_bf16(ds - from_bf16(dh[i]));
-        }
-        // dV += P^T dO and dK += dS^T Q over this tile's 16 columns (lane = d, keys 4 lg + i)
+            for (int i = 0; i < 4; ++i) {
+                const int c = cb + 4 * lg + i;
+                const float p = key < s_vis[c] ? __builtin_amdgcn_exp2f(sacc[i] * sc2 - s_lse2[c]) : 0.f;
+                const float ds = p * (pacc[i] - s_dsum[c]);
+                ph[i] = to_bf16(p);
+                pl[i] = to_bf16(p - from_bf16(ph[i]));
+                dh[i] = to_bf16(ds);
+                dl[i] = to_bf16(ds - from_bf16(dh[i]));
+            }
+            // dV += P^T dO and dK += dS^T Q over these 16 columns (lane = d, keys 4 lg + i)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const bf16x4 bdo = *reinterpret_cast<const bf16x4*>(s_dot + (dt * 16 + (lane & 15)) * TW + cb + 4 * lg);
-            const bf16x4 bq = *reinterpret_cast<const bf16x4*>(s_qt + (dt * 16 + (lane & 15)) * TW + cb + 4 * lg);
-            accV[dt] = mfma16(ph, bdo, accV[dt]);
-            accV[dt] = mfma16(pl, bdo, accV[dt]);
-            accK[dt] = mfma16(dh, bq, accK[dt]);
-            accK[dt] = mfma16(dl, bq, accK[dt]);
-        }
-        // dS to LDS as [column][key] for dQ = dS K
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = dt * 16 + (lane & 15);
+                const bf16x4 bdo = *reinterpret_cast<const bf16x4*>(s_dot + d * TW + tcol(d, cb + 4 * lg));
+                const bf16x4 bq = *reinterpret_cast<const bf16x4*>(s_qt + d * TW + tcol(d, cb + 4 * lg));
+                accV[dt] = mfma16(ph, bdo, accV[dt]);
+                accV[dt] = mfma16(pl, bdo, accV[dt]);
+                accK[dt] = mfma16(dh, bq, accK[dt]);
+                accK[dt] = mfma16(dl, bq, accK[dt]);
+            }
+            // dS to LDS as [column][key] for dQ = dS K
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s_dsh[(cb + 4 * lg + i) * KW + key] = dh[i];
-            s_dsl[(cb + 4 * lg + i) * KW + key] = dl[i];
+            for (int i = 0; i < 4; ++i) {
+                s_dsh[(cb + 4 * lg + i) * KW + key] = dh[i];
+                s_dsl[(cb + 4 * lg + i) * KW + key] = dl[i];
+            }
         }
         __syncthreads();
         // dQ^T tiles (16 d x 16 columns) = K^T dS^T over the block's keys; lane = column, d 4 lg + i
-#pragma unroll
+#pragma unroll 1
         for (int k = 0; k < Gm::DQT; ++k) {
             const int ti = wave + 4 * k;
             const int ctq = ti / DT, dt = ti % DT;
@@ -320,10 +336,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 *reinterpret_cast<f32x4*>(A.part_dq + (int64_t)row * D + dt * 16 + 4 * lg) = q * inv_sqrt_d;
         }
         __syncthreads();  // every wave is done with this iteration's LDS
-        if (it + 1 < n_it) {
-            store_it();
-            __syncthreads();
+    };
+
+    Regs RA, RB;
+    load_it(0, RA);
+    store_it(RA);
+    __syncthreads();
+    if constexpr (!Gm::PD2) {  // one iteration ahead: the next iteration's loads fly during this one
+        for (int it = 0; it < n_it; ++it) {
+            if (it + 1 < n_it) load_it(it + 1, RA);
+            compute();
+            if (it + 1 < n_it) {
+                store_it(RA);
+                __syncthreads();
+            }
         }
+    } else {
+    if (n_it > 1) load_it(1, RB);
+    for (int it = 0; it < n_it; it += 2) {
+        if (it + 2 < n_it) load_it(it + 2, RA);  // RA's data is in LDS already
+        compute();
+        if (it + 1 >= n_it) break;
+        store_it(RB);
+        __syncthreads();
+        if (it + 3 < n_it) load_it(it + 3, RB);
+        compute();
+        if (it + 2 >= n_it) break;
+        store_it(RA);
+        __syncthreads();
+    }
     }
     // this chunk's part of dK and dV for the wave's keys: lane = d (lane & 15) + 16 dt, keys 4 lg + i
 #pragma unroll
@@ -373,9 +414,19 @@ __global__ __launch_bounds__(256) void dq_combine_kernel(AttnBwdArgs A)
         for (int pc = lane; pc < G * CH4; pc += 64) {
             const int head = pc / CH4, dc = pc % CH4;
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (uint64_t m = valid; m; m &= m - 1) {
-                const int slot = __builtin_ctzll(m);
-                acc += *reinterpret_cast<const f32x4*>(A.part_dq + ((prow + slot) * G + head) * D + 4 * dc);
+            for (int s0 = 0; s0 < K_top; s0 += 8) {  // eight slots' loads in flight together, added in slot order
+                const uint32_t grp = (uint32_t)(valid >> s0) & 0xffu;
+                if (!grp) continue;
+                const int sfirst = s0 + __builtin_ctz(grp);
+                f32x4 x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int slot = (grp >> j) & 1 ? s0 + j : sfirst;
+                    x[j] = *reinterpret_cast<const f32x4*>(A.part_dq + ((prow + slot) * G + head) * D + 4 * dc);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if ((grp >> j) & 1) acc += x[j];
             }
             *reinterpret_cast<f32x4*>(A.dQ + (((int64_t)b * a.N_q + r) * a.H_q + (int64_t)h * G + head) * D + 4 * dc) =
                 acc;
