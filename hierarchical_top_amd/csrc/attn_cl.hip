@@ -147,6 +147,15 @@ __device__ __forceinline__ int vt_pos(int key)
     return (key & ~31) + 8 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
 }
 
+// Row d of the transposed values holds its NK key positions with groups of eight XOR-swizzled by
+// d / 8, so that the 16-bit stores of the eight d of one 16-byte value piece fall in different
+// banks, while the eight positions an MFMA operand reads stay one 16-byte load.
+template <int NK>
+__device__ __forceinline__ int vt_swz(int d, int pos)
+{
+    return pos ^ ((((d >> 3) & (NK / 8 - 1))) << 3);
+}
+
 template <int D, int C, int NB, bool FW>
 __global__ __launch_bounds__(FW ? 320 : 256) __attribute__((amdgpu_waves_per_eu(3))) void attn_cl_kernel(AttnClArgs a)
 {
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(FW ? 320 : 256) __attribute__((amdgpu_waves_per_eu(
                 const int key = p / CH, dc = p % CH;
                 const int vp = vt_pos(key);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) s_vt[(8 * dc + j) * VLD + vp] = vreg[i][j];
+                for (int j = 0; j < 8; ++j) s_vt[(8 * dc + j) * VLD + vt_swz<PS * 32>(8 * dc, vp)] = vreg[i][j];
             }
         }
     }
@@ -360,7 +369,8 @@ __global__ __launch_bounds__(FW ? 320 : 256) __attribute__((amdgpu_waves_per_eu(
             for (int ps = 0; ps < PS; ++ps)
     #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(s_vt + (dt * 16 + (lane & 15)) * VLD + 32 * ps + 8 * lg);
+                    const int vd = dt * 16 + (lane & 15);
+                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(s_vt + vd * VLD + vt_swz<PS * 32>(vd, 32 * ps + 8 * lg));
                     o[dt] = mfma(va, pbh[ps], o[dt]);
                     o[dt] = mfma(va, pbl[ps], o[dt]);
                 }
