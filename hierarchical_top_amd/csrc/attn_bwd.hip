@@ -90,6 +90,11 @@ __global__ __launch_bounds__(256) void dsum_kernel(AttnBwdArgs a)
 // lane's four consecutive columns of one d stay one 8-byte read. Needs 32 | columns.
 __device__ __forceinline__ int tcol(int d, int col) { return col ^ (((d >> 3) & 7) << 2); }
 
+// Key position of a row of K^T or dS in LDS: groups of eight keys XOR-swizzled by a row tag f,
+// so that 16-bit stores to rows that share banks spread out, while the eight keys an MFMA
+// operand reads (positions 8 m .. 8 m + 7 of the natural order) stay one 16-byte load.
+__device__ __forceinline__ int swz8(int pos, int f) { return pos ^ (f << 3); }
+
 template <int D, int C>
 struct BwdGeom {
     static constexpr int KS = D / 32;          // k-steps of S = Q K^T and dP = dO V^T
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         const bool ok = key < kexist;
         const bf16x8 v = load8h(Kb + (ok ? (int64_t)key * kvstride : 0) + 8 * dc);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s_kt[(8 * dc + j) * KW + key] = ok ? v[j] : to_bf16(0.f);
+        for (int j = 0; j < 8; ++j) s_kt[(8 * dc + j) * KW + swz8(key, dc & (PS * 4 - 1))] = ok ? v[j] : to_bf16(0.f);
     }
     // this wave's keys as the B operand of S = Q K^T and dP = dO V^T: lane (key, 8 d)
     bf16x8 bK[KS], bV[KS];
@@ -311,9 +316,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             }
             // dS to LDS as [column][key] for dQ = dS K
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s_dsh[(cb + 4 * lg + i) * KW + key] = dh[i];
-                s_dsl[(cb + 4 * lg + i) * KW + key] = dl[i];
+            for (int i = 0; i < 4; ++i) {  // row cb + 4 lg + i: tag ((row / 4) & 3) = lg
+                s_dsh[(cb + 4 * lg + i) * KW + swz8(key, lg)] = dh[i];
+                s_dsl[(cb + 4 * lg + i) * KW + swz8(key, lg)] = dl[i];
             }
         }
         __syncthreads();
@@ -325,9 +330,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ps = 0; ps < PS; ++ps) {
-                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(s_kt + (dt * 16 + (lane & 15)) * KW + 32 * ps + 8 * lg);
-                const bf16x8 bh_ = *reinterpret_cast<const bf16x8*>(s_dsh + (16 * ctq + (lane & 15)) * KW + 32 * ps + 8 * lg);
-                const bf16x8 bl_ = *reinterpret_cast<const bf16x8*>(s_dsl + (16 * ctq + (lane & 15)) * KW + 32 * ps + 8 * lg);
+                const int dk = dt * 16 + (lane & 15), ka = swz8(32 * ps + 8 * lg, (dk >> 3) & (PS * 4 - 1));
+                const int kb = swz8(32 * ps + 8 * lg, ((lane & 15) >> 2) & 3);
+                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(s_kt + dk * KW + ka);
+                const bf16x8 bh_ = *reinterpret_cast<const bf16x8*>(s_dsh + (16 * ctq + (lane & 15)) * KW + kb);
+                const bf16x8 bl_ = *reinterpret_cast<const bf16x8*>(s_dsl + (16 * ctq + (lane & 15)) * KW + kb);
                 q = mfma(ak, bh_, q);
                 q = mfma(ak, bl_, q);
             }
