@@ -342,8 +342,8 @@ pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, cons
 {
     if (score_kind != PISA_SCORE_LSE && score_kind != PISA_SCORE_MEAN && score_kind != PISA_SCORE_MEAN_VAR)
         return fail(PISA_EINVAL, "score_kind=%d", score_kind);
-    if (score_kind != PISA_SCORE_LSE && mode != PISA_ROUTE_LEVELS)
-        return fail(PISA_EUNSUPPORTED, "PISA-1 / PISA-2 scores need mode PISA_ROUTE_LEVELS");
+    if (score_kind != PISA_SCORE_LSE && mode == PISA_ROUTE_TWO_STAGE)
+        return fail(PISA_EUNSUPPORTED, "PISA-1 / PISA-2 scores need mode PISA_ROUTE_LEVELS or PISA_ROUTE_FUSED");
     pisa_status s = check_pyramid(p);
     if (s != PISA_OK) return s;
     if (N < 1) return fail(PISA_EINVAL, "N=%lld < 1", (long long)N);
@@ -451,6 +451,15 @@ pisa_status pisa_route_decode(const pisa_pyramid* p, const void* q, const void* 
                               const int64_t* seqlen, int32_t H_q, int32_t K_top, int32_t gqa_group, int32_t* idx,
                               float* score, void* stream)
 {
+    return pisa_route_decode_scored(p, q, K, dt, seqlen, H_q, K_top, gqa_group, PISA_SCORE_LSE, idx, score, stream);
+}
+
+pisa_status pisa_route_decode_scored(const pisa_pyramid* p, const void* q, const void* K, pisa_dtype dt,
+                                     const int64_t* seqlen, int32_t H_q, int32_t K_top, int32_t gqa_group,
+                                     int32_t score_kind, int32_t* idx, float* score, void* stream)
+{
+    if (score_kind != PISA_SCORE_LSE && score_kind != PISA_SCORE_MEAN && score_kind != PISA_SCORE_MEAN_VAR)
+        return fail(PISA_EINVAL, "score_kind=%d", score_kind);
     pisa_status s = check_pyramid(p);
     if (s != PISA_OK) return s;
     s = check_route(p, dt, H_q, K_top, gqa_group, 1, nodes_at(p->N_cap, p->C, p->g, 1));
@@ -462,6 +471,7 @@ pisa_status pisa_route_decode(const pisa_pyramid* p, const void* q, const void* 
     r.p = pyr_args(p);
     r.Q = q; r.K = K; r.N = 0; r.seqlen = seqlen;
     r.H_q = H_q; r.G = gqa_group; r.K_top = K_top; r.causal = 1;
+    r.score_kind = score_kind;
     r.idx = idx; r.score = score;
     stage_mark(PISA_STAGE_ROUTE_DECODE, false, (hipStream_t)stream);
     hipError_t e = launch_route_query(r, dt == PISA_F32 ? 0 : 1, p->d, MODE_DECODE, (hipStream_t)stream);

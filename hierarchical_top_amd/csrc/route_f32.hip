@@ -3,18 +3,31 @@
 
 namespace pisa {
 
+template <int D, int G, int SK>
+static hipError_t route_query_sk(const RouteArgs& a, int mode, hipStream_t s)
+{
+    if (mode == MODE_DECODE)
+        hipLaunchKernelGGL((route_decode_kernel<D, float, G, SK>), dim3((unsigned)(a.p.B * a.p.H)), dim3(64 * kDecodeWaves), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL((route_query_kernel<D, float, G, MODE_FUSED, SK>), dim3((unsigned)((int64_t)a.p.B * a.p.H * a.N)),
+                           dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int D, int G>
 static hipError_t route_query_dg(const RouteArgs& a, int mode, hipStream_t s)
 {
-    if (mode == MODE_DECODE)
-        hipLaunchKernelGGL((route_decode_kernel<D, float, G>), dim3((unsigned)(a.p.B * a.p.H)), dim3(64 * kDecodeWaves), 0, s, a);
-    else if (mode == MODE_STAGE1)
+    if (mode == MODE_STAGE1) {
         hipLaunchKernelGGL((route_query_kernel<D, float, G, MODE_STAGE1>), dim3((unsigned)((int64_t)a.p.B * a.p.H * a.N)),
                            dim3(64), 0, s, a);
-    else
-        hipLaunchKernelGGL((route_query_kernel<D, float, G, MODE_FUSED>), dim3((unsigned)((int64_t)a.p.B * a.p.H * a.N)),
-                           dim3(64), 0, s, a);
-    return hipGetLastError();
+        return hipGetLastError();
+    }
+    switch (a.score_kind) {  // block score: LSE, PISA-1 mean, PISA-2 mean + var / 2
+    case 1: return route_query_sk<D, G, 1>(a, mode, s);
+    case 2: return route_query_sk<D, G, 2>(a, mode, s);
+    default: return route_query_sk<D, G, 0>(a, mode, s);
+    }
 }
 
 template <int D, int G>

@@ -46,7 +46,38 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t total)
     return i;
 }
 
-template <int D, typename T, int G, int WAVES>
+// Block score (base 2; the callers scale by ln 2) of one candidate and query head from the
+// values its group of `width` adjacent lanes hold, n per lane with validity flags: SK 1 is
+// the mean of the valid values (PISA-1, section 4.4 eq 33), SK 2 the mean plus half their
+// population variance, the variance taken about the mean in a second pass and scaled by ln 2
+// to natural units (PISA-2, eq 34). No valid value: -inf.
+template <int SK, int N>
+__device__ __forceinline__ float group_moment_score(const float* y, const bool* ok, int width)
+{
+    float s = 0.f, c = 0.f;
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+        s += ok[t] ? y[t] : 0.f;
+        c += ok[t] ? 1.f : 0.f;
+    }
+    s = group_sum(s, width);
+    c = group_sum(c, width);
+    const float mu = c > 0.f ? s / c : 0.f;
+    if constexpr (SK == 1) {
+        return c > 0.f ? mu : -INFINITY;
+    } else {
+        float q = 0.f;
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+            const float dy = y[t] - mu;
+            q += ok[t] ? dy * dy : 0.f;
+        }
+        q = group_sum(q, width);
+        return c > 0.f ? mu + (0.5f * kLn2) * (q / c) : -INFINITY;
+    }
+}
+
+template <int D, typename T, int G, int WAVES, int SK = 0>
 struct RouteQuery {
     static constexpr int TA = Src<T>::TERMS;  // query terms per head
     static constexpr int R = G * TA;          // MFMA rows in use
@@ -103,10 +134,14 @@ struct RouteQuery {
                 float y = s_z[hd * 65 + lane];
                 if constexpr (TA == 2) y += s_z[(G + hd) * 65 + lane];
                 y = ok ? y * scale : -INFINITY;
-                const float m = group_max(y, nch);
-                const float e = ok ? __builtin_amdgcn_exp2f(y - m) : 0.f;
-                const float ssum = group_sum(e, nch);
-                u += m + __builtin_amdgcn_logf(ssum);
+                if constexpr (SK != 0) {
+                    u += group_moment_score<SK, 1>(&y, &ok, nch);
+                } else {
+                    const float m = group_max(y, nch);
+                    const float e = ok ? __builtin_amdgcn_exp2f(y - m) : 0.f;
+                    const float ssum = group_sum(e, nch);
+                    u += m + __builtin_amdgcn_logf(ssum);
+                }
             }
             if ((lane & (nch - 1)) == 0 && j < ns) s_u[j] = u * kLn2;
             wave_lds_sync();
@@ -152,10 +187,16 @@ struct RouteQuery {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float y = ok ? c[i] * scale : -INFINITY;
-                    const float m = group_max(y, nch);
-                    const float e = ok ? __builtin_amdgcn_exp2f(y - m) : 0.f;
-                    const float sum = group_sum(e, nch);
-                    if (4 * lg + i < G) u += m + __builtin_amdgcn_logf(sum);
+                    float sc;
+                    if constexpr (SK != 0) {
+                        sc = group_moment_score<SK, 1>(&y, &ok, nch);
+                    } else {
+                        const float m = group_max(y, nch);
+                        const float e = ok ? __builtin_amdgcn_exp2f(y - m) : 0.f;
+                        const float sum = group_sum(e, nch);
+                        sc = m + __builtin_amdgcn_logf(sum);
+                    }
+                    if (4 * lg + i < G) u += sc;
                 }
                 u += shfl_xor(u, 16);
                 u += shfl_xor(u, 32);
@@ -188,15 +229,24 @@ struct RouteQuery {
                 float u = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float m = -INFINITY;
+                    float sc;
+                    if constexpr (SK != 0) {
+                        float y[4];
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) m = fmaxf(m, ok[tt] ? c[tt][i] * scale : -INFINITY);
-                    m = group_max(m, 16);
-                    float sum = 0.f;
+                        for (int tt = 0; tt < 4; ++tt) y[tt] = c[tt][i] * scale;
+                        sc = group_moment_score<SK, 4>(y, ok, 16);
+                    } else {
+                        float m = -INFINITY;
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) sum += ok[tt] ? __builtin_amdgcn_exp2f(c[tt][i] * scale - m) : 0.f;
-                    sum = group_sum(sum, 16);
-                    if (4 * lg + i < G) u += m + __builtin_amdgcn_logf(sum);
+                        for (int tt = 0; tt < 4; ++tt) m = fmaxf(m, ok[tt] ? c[tt][i] * scale : -INFINITY);
+                        m = group_max(m, 16);
+                        float sum = 0.f;
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) sum += ok[tt] ? __builtin_amdgcn_exp2f(c[tt][i] * scale - m) : 0.f;
+                        sum = group_sum(sum, 16);
+                        sc = m + __builtin_amdgcn_logf(sum);
+                    }
+                    if (4 * lg + i < G) u += sc;
                 }
                 u += shfl_xor(u, 16);
                 u += shfl_xor(u, 32);
@@ -353,10 +403,10 @@ struct RouteQuery {
     }
 };
 
-template <int D, typename T, int G, int MODE>
+template <int D, typename T, int G, int MODE, int SK = 0>
 __global__ __launch_bounds__(64) void route_query_kernel(RouteArgs a)
 {
-    RouteQuery<D, T, G, 1>::template run<MODE>(a);
+    RouteQuery<D, T, G, 1, SK>::template run<MODE>(a);
 }
 
 // Decode: one workgroup per (sequence, KV head); kDecodeWaves waves share the
@@ -364,10 +414,10 @@ __global__ __launch_bounds__(64) void route_query_kernel(RouteArgs a)
 // candidate block), so their loads are in flight together.
 constexpr int kDecodeWaves = 8;
 
-template <int D, typename T, int G>
+template <int D, typename T, int G, int SK = 0>
 __global__ __launch_bounds__(64 * kDecodeWaves) void route_decode_kernel(RouteArgs a)
 {
-    RouteQuery<D, T, G, kDecodeWaves>::template run<MODE_DECODE>(a);
+    RouteQuery<D, T, G, kDecodeWaves, SK>::template run<MODE_DECODE>(a);
 }
 
 // ---------------------------------------------------------------------------

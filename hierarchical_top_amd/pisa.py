@@ -63,6 +63,7 @@ def lib():
             "pisa_route_prefill_scored": [P, c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_p,
                                           c_p, c_p, c_size, c_p],
             "pisa_route_decode": [P, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p],
+            "pisa_route_decode_scored": [P, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_sparse_attn": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p,
                                  c_i32, c_i32, c_p, c_p, c_p, c_p],
             "pisa_sparse_attn_workspace": [c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -95,7 +96,8 @@ def lib():
 
 
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
-           "pisa_route_prefill", "pisa_route_prefill_scored", "pisa_route_decode", "pisa_sparse_attn", "pisa_sparse_attn_workspace",
+           "pisa_route_prefill", "pisa_route_prefill_scored", "pisa_route_decode",
+           "pisa_route_decode_scored", "pisa_sparse_attn", "pisa_sparse_attn_workspace",
            "pisa_sparse_attn_clustered", "pisa_sparse_attn_bwd_workspace", "pisa_sparse_attn_bwd",
            "pisa_selection_quality_workspace", "pisa_selection_quality", "pisa_bsa_select", "pisa_time_stage",
            "pisa_time_stage_pending",
@@ -181,7 +183,7 @@ def route_prefill(pyr: Pyramid, Q: torch.Tensor, K: torch.Tensor, N: int, K_top:
     """Route every position of Q [B][N][H_q][d]; returns idx [B][H_kv][N][K_top] (and scores).
 
     score_kind: "lse" (PISA), "mean" (PISA-1) or "mean_var" (PISA-2); the last two
-    run on the level-synchronous router only."""
+    run on the level-synchronous and fused routers."""
     _dev(Q, K)
     B, Nq, H_q, d = Q.shape
     assert Nq == N and K.dtype == Q.dtype
@@ -201,8 +203,10 @@ def route_prefill(pyr: Pyramid, Q: torch.Tensor, K: torch.Tensor, N: int, K_top:
 
 
 def route_decode(pyr: Pyramid, q: torch.Tensor, K: torch.Tensor, seqlen: torch.Tensor, K_top: int,
-                 with_score: bool = False, out: torch.Tensor | None = None, score_out: torch.Tensor | None = None):
-    """Route the newest token of each sequence: q [B][H_q][d]; returns idx [B][H_kv][K_top]."""
+                 with_score: bool = False, out: torch.Tensor | None = None, score_out: torch.Tensor | None = None,
+                 score_kind: str = "lse"):
+    """Route the newest token of each sequence: q [B][H_q][d]; returns idx [B][H_kv][K_top].
+    score_kind: "lse" (PISA), "mean" (PISA-1) or "mean_var" (PISA-2)."""
     _dev(q, K, seqlen)
     B, H_q, d = q.shape
     idx = out if out is not None else torch.empty(B, pyr.H_kv, K_top, dtype=torch.int32, device=q.device)
@@ -210,8 +214,9 @@ def route_decode(pyr: Pyramid, q: torch.Tensor, K: torch.Tensor, seqlen: torch.T
     if with_score:
         score = score_out if score_out is not None else torch.empty(B, pyr.H_kv, K_top, dtype=torch.float32,
                                                                     device=q.device)
-    _check(lib().pisa_route_decode(ctypes.byref(pyr.desc), _ptr(q), _ptr(K), _dt(q), _ptr(seqlen), H_q, K_top,
-                                   H_q // pyr.H_kv, _ptr(idx), _ptr(score), _stream()))
+    _check(lib().pisa_route_decode_scored(ctypes.byref(pyr.desc), _ptr(q), _ptr(K), _dt(q), _ptr(seqlen), H_q, K_top,
+                                          H_q // pyr.H_kv, SCORE_KINDS[score_kind], _ptr(idx), _ptr(score),
+                                          _stream()))
     return (idx, score) if with_score else idx
 
 

@@ -170,9 +170,9 @@ typedef enum pisa_score_kind {
 /* pisa_route_prefill with the block score chosen by score_kind (a
  * pisa_score_kind); pisa_route_prefill is this call with PISA_SCORE_LSE.
  * Score outputs hold the chosen score. PISA_SCORE_MEAN and
- * PISA_SCORE_MEAN_VAR need mode PISA_ROUTE_LEVELS (PISA_EUNSUPPORTED
- * otherwise); an unknown score_kind is PISA_EINVAL. Everything else as in
- * pisa_route_prefill. */
+ * PISA_SCORE_MEAN_VAR need mode PISA_ROUTE_LEVELS or PISA_ROUTE_FUSED
+ * (PISA_EUNSUPPORTED for PISA_ROUTE_TWO_STAGE); an unknown score_kind is
+ * PISA_EINVAL. Everything else as in pisa_route_prefill. */
 pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, const void* K,
                                       pisa_dtype dt, int64_t N, int32_t H_q, int32_t K_top,
                                       int32_t causal, int32_t gqa_group, int32_t mode,
@@ -190,6 +190,14 @@ pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, cons
 pisa_status pisa_route_decode(const pisa_pyramid* p, const void* q, const void* K,
                               pisa_dtype dt, const int64_t* seqlen, int32_t H_q, int32_t K_top,
                               int32_t gqa_group, int32_t* idx, float* score, void* stream);
+
+/* pisa_route_decode with the block score chosen by score_kind (a
+ * pisa_score_kind, section 4.4); pisa_route_decode is this call with
+ * PISA_SCORE_LSE. An unknown score_kind is PISA_EINVAL. */
+pisa_status pisa_route_decode_scored(const pisa_pyramid* p, const void* q, const void* K,
+                                     pisa_dtype dt, const int64_t* seqlen, int32_t H_q,
+                                     int32_t K_top, int32_t gqa_group, int32_t score_kind,
+                                     int32_t* idx, float* score, void* stream);
 
 /*
  * Block-sparse attention forward (section 3.1 eq 6). Query row r of sequence

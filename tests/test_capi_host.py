@@ -130,9 +130,12 @@ def test_route_prefill_scored_validation(lib):
 
     assert scored(3) == EINVAL
     assert scored(-1) == EINVAL
-    # PISA-1 / PISA-2 scores run on the level-synchronous router only
+    # PISA-1 / PISA-2 scores run on the level-synchronous and fused routers, not the two-stage one
     assert scored(pisa.SCORE_KINDS["mean"], mode=pisa.TWO_STAGE) == EUNSUPPORTED
-    assert scored(pisa.SCORE_KINDS["mean_var"], mode=pisa.FUSED) == EUNSUPPORTED
+    assert scored(pisa.SCORE_KINDS["mean_var"], mode=pisa.TWO_STAGE) == EUNSUPPORTED
+    dec = lib.pisa_route_decode_scored
+    assert dec(ctypes.byref(desc), FAKE, FAKE, pisa.BF16, FAKE, 16, 8, 4, 3, FAKE, None, None) == EINVAL
+    assert dec(ctypes.byref(desc), FAKE, FAKE, pisa.BF16, None, 16, 8, 4, 1, FAKE, None, None) == EINVAL
     # past the score checks, the usual validation applies: no workspace was given
     for kind in (0, 1, 2):
         assert scored(kind) == ENOSPACE

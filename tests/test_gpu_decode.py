@@ -31,9 +31,9 @@ def _rebuild_equal(pyr, K, b, n):
     return None
 
 
-def _check_route(K, q, b, n, C, g, K_top, idx, score):
+def _check_route(K, q, b, n, C, g, K_top, idx, score, score_kind="lse"):
     opyr = oracle.Pyramid(K[b:b + 1, :n].float().cpu().numpy(), n, C, g)
-    orc = oracle.route(opyr, q[b:b + 1].float().cpu().numpy(), [0], [n - 1], K_top)
+    orc = oracle.route(opyr, q[b:b + 1].float().cpu().numpy(), [0], [n - 1], K_top, score_kind=score_kind)
     st = compare(idx[b:b + 1].cpu().numpy(), score[b:b + 1].cpu().numpy(), orc, np.array([n - 1]), C, K_top,
                  max_near_tie_frac=1.0)
     return st, orc["idx"]
@@ -69,6 +69,35 @@ def test_decode_small_ragged_lengths():
             _check_route(Kc, q, b, lens[b], C, g, K_top, idx, score)
             checked += 1
     assert lens[0] == N0 + steps and checked == steps * B
+
+
+@pytest.mark.parametrize("kind", ["mean", "mean_var"])
+def test_decode_pisa1_pisa2_scores(kind):
+    """The decode router with the PISA-1 / PISA-2 block scores (section 4.4) against the
+    oracle routing the newest token with the same score, over growing ragged lengths and
+    d = 128, C = 64, g = 4 (leaf candidates of 64 keys, four score tiles per candidate)."""
+    B, H_q, H, d, C, g, K_top = 4, 8, 2, 128, 64, 4, 8
+    N0, steps = 9000, 24
+    cap = N0 + steps
+    gen = torch.Generator().manual_seed(43)
+    K_all = torch.randn(B, cap, H, d, generator=gen).to(torch.bfloat16)
+    q_all = torch.randn(steps, B, H_q, d, generator=gen).to(torch.bfloat16)
+    Kc = K_all.clone().cuda()
+    pyr = pisa.Pyramid(B, H, d, C, g, cap)
+    lens = [N0 - 1000 * b for b in range(B)]
+    pyr.build(Kc, N0)
+    for s in range(steps):
+        for b in range(B):
+            lens[b] += 1
+        seqlen = torch.tensor(lens, dtype=torch.int64, device="cuda")
+        # one build over the longest prefix: a shorter sequence's summaries then include keys
+        # past its length, but only on its current path, whose nodes are forced and never scored
+        pyr.build(Kc, max(lens))
+        q = q_all[s].cuda()
+        idx, score = pisa.route_decode(pyr, q, Kc, seqlen, K_top, with_score=True, score_kind=kind)
+        torch.cuda.synchronize()
+        for b in range(B):
+            _check_route(Kc, q, b, lens[b], C, g, K_top, idx, score, score_kind=kind)
 
 
 def test_decode_first_level_growth_and_short_sequences():

@@ -129,6 +129,7 @@ def test_route_matches_oracle(mode, case, K_top, causal, sample):
         print(case, mode, b, stats)
 
 
+@pytest.mark.parametrize("mode", ["levels", "fused"])
 @pytest.mark.parametrize("kind", ["mean", "mean_var"])
 @pytest.mark.parametrize("case,K_top,causal,sample", [
     ("tiny", 4, True, None),          # fp32: LDS-staged and register-row scoring, dense top levels
@@ -141,15 +142,15 @@ def test_route_matches_oracle(mode, case, K_top, causal, sample):
     ("sparse64k", 8, True, 600),      # sparse upper levels
     ("ragged_big", 8, True, 600),     # tail nodes missing grandchildren at sparse levels
 ])
-def test_route_pisa1_pisa2_match_oracle(kind, case, K_top, causal, sample):
+def test_route_pisa1_pisa2_match_oracle(kind, case, K_top, causal, sample, mode):
     """PISA-1 (mean logit) and PISA-2 (mean + half the variance) block scores of section 4.4,
-    on the level-synchronous router: same protocol as the LSE score."""
+    on the level-synchronous and the fused per-query routers: same protocol as the LSE score."""
     w = CASES[case]
-    print("case", case, "score", kind, "K_top", K_top, "causal", causal, flush=True)
+    print("case", case, "score", kind, "mode", mode, "K_top", K_top, "causal", causal, flush=True)
     Q, K = _inputs(w)
     t = _positions(w, sample)
     _, orc = _oracle_route(w, Q, K, K_top, causal, t, score_kind=kind)
-    _, idx, score = _gpu_route(w, Q, K, K_top, causal, pisa.LEVELS, score_kind=kind)
+    _, idx, score = _gpu_route(w, Q, K, K_top, causal, MODES[mode], score_kind=kind)
     M1 = -(-w.N // w.C)
     # PISA-1's upper-level scores are logits of mean keys, whose spread shrinks with the span of
     # the node, so more items than under LSE have a ranked level inside the 1e-3 band (26 % on
