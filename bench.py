@@ -411,6 +411,22 @@ def selection_quality_table(P):
     return res
 
 
+def attn_bwd_alone(reps: int = 10):
+    """The 64K attention backward alone (random causal selection of the routing shape)."""
+    w = synth.workload("p64k")
+    Q, K, V, _ = synth.make_prefill(w)
+    Q, K, V = Q.cuda(), K.cuda(), V.cuda()
+    idx = torch.from_numpy(synth.random_selection(8, w.B, w.H_kv, w.N, w.K_top, w.C, [w.N], causal=True)).cuda()
+    O, lse = pisa.sparse_attn_clustered(Q, K, V, idx, w.C, w.N, with_lse=True)
+    dO = synth.make_grad_out(Q.shape, 303).cuda()
+    ws = torch.empty(pisa.sparse_attn_bwd_workspace_bytes(w.B, w.N, w.N, w.H_q, w.H_kv, w.d, w.C, w.K_top),
+                     dtype=torch.uint8, device="cuda")
+    g = tuple(torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in (Q, K, V))
+    ms = time_fn(lambda: pisa.sparse_attn_bwd(Q, K, V, O, dO, lse, idx, w.C, w.N, workspace=ws, out=g), reps)
+    bw = workcount.attn_bwd_work(w.B, w.N, w.H_q, w.d, w.C, w.K_top)
+    return dict(attn_bwd_ms=ms, attn_bwd_tflops=2 * bw["mac"] / (ms * 1e-3) / 1e12)
+
+
 PAPER_SWEEP_N = (4096, 8192, 16384, 32768, 65536, 131072, 262144)
 
 
@@ -464,6 +480,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle routing to time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a 1 GiB device copy (counter calibration for --traffic)")
+    ap.add_argument("--only", choices=["attn_bwd", "decode"],
+                    help="time one part alone (for kernel traces): the 64K attention backward, or 32 decode steps")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
     args = ap.parse_args()
@@ -479,6 +497,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pisa.lib()  # fail loudly when the library is missing
+    if args.only:
+        print(json.dumps({"only": args.only, **(attn_bwd_alone() if args.only == "attn_bwd" else decode_bench(32))}),
+              flush=True)
+        return
 
     w = synth.workload("p256k")
     log("generating", w)
