@@ -205,7 +205,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     __syncthreads();  // entries in LDS
 
     // global -> registers for one iteration: q and dO pieces (column, 8 d), and per column its
-    // metadata; two sets, so that an iteration's loads are issued two iterations before use
+    // metadata; at d = 64 two sets, so that an iteration's loads are issued two iterations
+    // before use (one iteration before at d = 128)
     struct Regs {
         bf16x8 q[NPT], o[NPT];
         float lse2, dsum;
