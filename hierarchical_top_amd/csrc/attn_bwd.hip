@@ -401,7 +401,12 @@ __global__ __launch_bounds__(256) void dq_combine_kernel(AttnBwdArgs A)
     const int64_t total = (int64_t)a.B * a.H_kv * a.N_q;
     const int64_t stride = (int64_t)gridDim.x * 4;
     const int G = a.G, K_top = a.K_top;
-    for (int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); item < total; item += stride) {
+    int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    int blk_next = (item < total && lane < K_top) ? a.idx[item * K_top + lane] : -1;
+    for (; item < total; item += stride) {
+        const int blk = blk_next;  // this item's slot ids; the next item's are read during the merge
+        const int64_t next = item + stride;
+        blk_next = (next < total && lane < K_top) ? a.idx[next * K_top + lane] : -1;
         const int64_t r = item % a.N_q;
         const int64_t bh = item / a.N_q;
         const int h = (int)(bh % a.H_kv);
@@ -411,7 +416,6 @@ __global__ __launch_bounds__(256) void dq_combine_kernel(AttnBwdArgs A)
         const int64_t pos = nb - a.N_q + r;
         bool vis = false;
         if (lane < K_top) {
-            const int blk = a.idx[item * K_top + lane];
             const int64_t k0 = (int64_t)blk * a.C;
             int64_t kend = k0 + a.C < nb ? k0 + a.C : nb;
             if (a.causal && kend > pos + 1) kend = pos + 1;
