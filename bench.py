@@ -48,6 +48,8 @@ STAGES_FUSED = ["build", "route_fused"]
 ARMED = {"build": 1, "route_fused": 1, "leaf": 1, "upper": 8, "cluster": 8, "final": 8}
 # kernel (name fragment in a rocprofv3 trace) of each single-kernel stage
 STAGE_KERNEL = {"leaf": "leaf_kernel", "build": "build_l12_kernel", "route_fused": "route_query_kernel"}
+# kernels of the 64K attention workload whose HBM traffic the counters measure (bench.py --only attn_bwd)
+ATTN_KERNEL = {"attn_fwd": "attn_cl_kernel", "attn_bwd": "attn_bwd_kernel", "dq_combine": "dq_combine_kernel"}
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read and 1 GiB written
 
 
@@ -140,6 +142,9 @@ STAGE_SOURCES = {
     "build": ("pyramid.hip",),
     "leaf": ("levels.hip", "levels_impl.hpp", "levels_bf16.hip", "stream.hpp"),
     "route_fused": ("route.hip", "route_impl.hpp", "route_bf16.hip"),
+    "attn_fwd": ("attn_cl.hip", "attn_bwd.hpp", "stream.hpp"),
+    "attn_bwd": ("attn_bwd.hip", "attn_bwd.hpp", "attn_cl.hip"),
+    "dq_combine": ("attn_bwd.hip", "attn_bwd.hpp"),
 }
 
 
@@ -214,7 +219,7 @@ def _counter_rows(d):
     return list(per.values())
 
 
-def traffic_from_counters(fetch_dir, write_dir, workload="p256k"):
+def traffic_from_counters(fetch_dir, write_dir, workload="p256k", kernels=None):
     """HBM bytes per launch of the stage kernels from two rocprofv3 --pmc runs of
     `bench.py --quick --no-cpu --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, in
     KiB per dispatch), each scaled so that the calibration copy reads / writes
@@ -232,7 +237,7 @@ def traffic_from_counters(fetch_dir, write_dir, workload="p256k"):
     kf, kw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     out_file = ROOT / "profiles" / "traffic.json"
     recs = json.loads(out_file.read_text()) if out_file.exists() else {}
-    for stage, frag in STAGE_KERNEL.items():
+    for stage, frag in (kernels or STAGE_KERNEL).items():
         fb, nf = avg(fetch, frag, "FETCH_SIZE")
         wb, nw = avg(write, frag, "WRITE_SIZE")
         if fb is None or wb is None:
@@ -380,6 +385,10 @@ def prefill_extra(name, reps, with_attn=False):
         ms_b = time_fn(lambda: pisa.sparse_attn_bwd(P.Q, P.K, P.V, O, dO, lse, P.idx, w.C, w.N, workspace=bws,
                                                     out=grads), reps)
         out["attn_bwd_ms"] = ms_b
+        for st, ms_st in (("attn_fwd", None), ("attn_bwd", None)):
+            tr = load_traffic(st, "p64k")
+            if tr is not None:
+                out[st + "_traffic_bytes"] = tr
         out["attn_bwd_tflops"] = 2 * bw["mac"] / (ms_b * 1e-3) / 1e12
         out["attn_bwd_mfma_frac"] = out["attn_bwd_tflops"] / PEAK_BF16_TFLOPS
         del O, lse, dO, bws, grads
@@ -482,11 +491,15 @@ def main():
                     help="end with a 1 GiB device copy (counter calibration for --traffic)")
     ap.add_argument("--only", choices=["attn_bwd", "decode"],
                     help="time one part alone (for kernel traces): the 64K attention backward, or 32 decode steps")
+    ap.add_argument("--traffic-workload", choices=["p256k", "p64k"], default="p256k",
+                    help="with --traffic: the counter runs were of the headline (p256k) or of --only attn_bwd (p64k)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
     args = ap.parse_args()
     if args.traffic:
-        print(json.dumps(traffic_from_counters(*args.traffic), indent=1, sort_keys=True))
+        kern = ATTN_KERNEL if args.traffic_workload == "p64k" else STAGE_KERNEL
+        print(json.dumps(traffic_from_counters(*args.traffic, workload=args.traffic_workload, kernels=kern), indent=1,
+                         sort_keys=True))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -500,6 +513,8 @@ def main():
     if args.only:
         print(json.dumps({"only": args.only, **(attn_bwd_alone() if args.only == "attn_bwd" else decode_bench(32))}),
               flush=True)
+        if args.copy_calibration:
+            copy_calibration()
         return
 
     w = synth.workload("p256k")
