@@ -3,7 +3,8 @@ heads, d=128, C=64, g=4, K_top=8, causal, bf16 with planted blocks -- in the con
 the benchmark times (pyramid build, then the level-synchronous router over every
 position), checked on sampled outputs the oracle computes one by one: every level's
 summaries on sampled nodes, the selections and scores of sampled positions for the three
-block scores (LSE, PISA-1, PISA-2), and the exhaustive selector on sampled positions."""
+block scores (LSE, PISA-1, PISA-2), the exhaustive selector on sampled positions, and the
+level router across a leaf-level clustering window (two sequences of 2^18 + 3001 tokens)."""
 import numpy as np
 import pytest
 import torch
@@ -74,3 +75,27 @@ def test_p256k_exhaustive_selector_sampled(p256k):
     stats = compare(idx[0][:, ts].cpu().numpy().transpose(1, 0, 2), score[0][:, ts].cpu().numpy().transpose(1, 0, 2),
                     orc, ts, w.C, w.K_top, band=band, score_tol=1e-7, score_rtol=1e-4)
     print("bsa", stats)
+
+
+def test_level_router_across_leaf_windows():
+    """Two sequences of 2^18 + 3001 tokens (4 / 2 heads, d=64, C=64, g=4, planted blocks):
+    the level router's leaf clusters are keyed by windows of 2^18 positions, so positions on
+    both sides of the first window boundary, and the ragged tail, land in different
+    clusters of the same nodes. Sampled positions (dense around the boundary) against the
+    oracle."""
+    w = synth.Workload("win2", 2, (1 << 18) + 3001, 4, 2, 64, 64, 4, 8, "bf16", 16, 91, False)
+    Q, K, _, _ = synth.make_prefill(w)
+    edge = 1 << 18
+    t = np.unique(np.concatenate([np.linspace(0, w.N - 1, 300).astype(np.int64), np.arange(edge - 70, edge + 70),
+                                  np.arange(w.N - w.C, w.N), np.arange(2 * w.C)]))
+    print("positions", len(t), flush=True)
+    pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
+    pyr.build(K.cuda(), w.N)
+    idx, score = pisa.route_prefill(pyr, Q.cuda(), K.cuda(), w.N, w.K_top, mode=pisa.LEVELS, with_score=True)
+    torch.cuda.synchronize()
+    opyr = oracle.Pyramid(K.float().numpy(), w.N, w.C, w.g)
+    for b in range(w.B):
+        orc = oracle.route(opyr, Q[b, t].float().numpy(), [b] * len(t), t, w.K_top)
+        gi = idx[b][:, t].cpu().numpy().transpose(1, 0, 2)
+        gs = score[b][:, t].cpu().numpy().transpose(1, 0, 2)
+        print("b", b, compare(gi, gs, orc, t, w.C, w.K_top, max_near_tie_frac=0.6))
