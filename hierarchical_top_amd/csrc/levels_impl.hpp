@@ -746,7 +746,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB >= 3 ? 3
         }
         if (lim > 0) {
             const unsigned char* cur = reinterpret_cast<const unsigned char*>(L.q + (sb % NB) * kSubRows * D);
-            for (int tl = part; tl < kSubRows / 16; tl += wpc) {
+            for (int tl = part; tl < kSubRows / 16 && tl * QT < nsub; tl += wpc) {
                 const int el = tl * QT + qi;  // entry of this lane's column within the sub-chunk
                 const unsigned char* tb = cur + tl * (16 * D * 2);
                 bf16x8 B[KS];
