@@ -200,7 +200,7 @@ constexpr int kRegWaves = 4;
 constexpr int kLeafQC = 256;
 constexpr int kSubRows = 64;
 constexpr int kLeafNB = 2;
-constexpr int kUpperNB = 4;
+constexpr int kUpperNB = 2;
 // LDS bytes of one such workgroup: the ring, the chunk's entries and its scores
 inline size_t stream_lds_bytes(int d, int nb) { return (size_t)nb * kSubRows * d * 2 + (size_t)kLeafQC * (4 + 16); }
 
