@@ -282,18 +282,31 @@ def cpu_baseline(P: Prefill, budget_s: float):
     t_route_full = dt * scale
     qps = w.B * w.N / (t_build + t_route_full)
     # parity of the GPU selection on the sampled positions
-    gi = gpu_idx[0][:, t].transpose(1, 0, 2)
-    same = (gi == orc["idx"]).all(-1)
-    outside = orc["gap"] >= 1e-3
-    parity = dict(sampled_positions=int(len(t)), items=int(same.size), identical=int(same.sum()),
-                  near_tie_items=int((~outside).sum()),
-                  mismatches_outside_band=int((~same & outside).sum()), band=1e-3)
+    parity = selection_parity(opyr, Qs, t, gpu_idx[0][:, t].transpose(1, 0, 2), orc, w.K_top, threads)
     res = dict(value=qps, unit="queries/s", cores=threads, kind="oracle",
                sample="full fp64 pyramid build (%.2f s) + routing of %d evenly spaced positions x %d KV heads "
                       "(%.2f s), extrapolated to all %d positions by the scored work (x%.1f)"
                       % (t_build, len(t), w.H_kv, dt, w.N, scale),
                build_s=t_build, route_sample_s=dt)
     return res, parity
+
+
+def selection_parity(opyr, Qs, t, gi, orc, K_top, threads, band=1e-3, strict=1e-5):
+    """Parity of GPU selections gi [n][H][K_top] with the oracle's on positions t: exact
+    wherever every ranked level's margin is at least `strict`; elsewhere a differing selection
+    must be a tie resolution of the oracle's route within `band` (the oracle's search)."""
+    import oracle  # test infrastructure: parity of the timed selection
+    same = (gi == orc["idx"]).all(-1)
+    mism = np.argwhere(~same)
+    eps = np.zeros(0)
+    if len(mism):
+        eps = oracle.route_reach(opyr, Qs[mism[:, 0]], [0] * len(mism), np.asarray(t)[mism[:, 0]], mism[:, 1],
+                                 gi[mism[:, 0], mism[:, 1]], K_top, cap=band, threads=threads)
+    return dict(sampled_positions=int(len(t)), items=int(same.size), identical=int(same.sum()),
+                near_tie_items=int((orc["gap"] < band).sum()), band=band, strict_band=strict,
+                mismatches_outside_strict=int((~same & (orc["gap"] >= strict)).sum()),
+                invalid_tie_resolutions=int((~(eps <= band)).sum()),
+                max_tie_resolution_cost=float(eps.max()) if len(eps) else 0.0)
 
 
 def decode_bench(reps_steps: int):
@@ -468,10 +481,8 @@ def paper_sweep(check: bool, sizes=PAPER_SWEEP_N):
             orc = oracle.route(opyr, P.Q_cpu[0, t].float().numpy(), [0] * len(t), t, w.K_top, causal=True,
                                threads=max(1, min(len(os.sched_getaffinity(0)), 16)))
             gi = P.idx.cpu().numpy()[0][:, t].transpose(1, 0, 2)
-            same = (gi == orc["idx"]).all(-1)
-            outside = orc["gap"] >= 1e-3
-            r["parity"] = dict(sampled_positions=int(len(t)), items=int(same.size), identical=int(same.sum()),
-                               mismatches_outside_band=int((~same & outside).sum()), band=1e-3)
+            r["parity"] = selection_parity(opyr, P.Q_cpu[0, t].float().numpy(), t, gi, orc, w.K_top,
+                                           max(1, min(len(os.sched_getaffinity(0)), 16)))
         out[str(N)] = r
         del P
         torch.cuda.empty_cache()

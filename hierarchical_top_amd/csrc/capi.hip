@@ -319,8 +319,13 @@ pisa_status pisa_route_prefill_workspace(const pisa_pyramid* p, int64_t N, int32
                                          size_t* bytes)
 {
     (void)H_q;
-    if (!p || !bytes) return fail(PISA_EINVAL, "NULL argument");
+    if (!bytes) return fail(PISA_EINVAL, "NULL argument");
+    pisa_status s = check_pyramid(p);  /* the layouts divide by C and g and walk the levels */
+    if (s != PISA_OK) return s;
     if (N < 1 || K_top < 1 || K_top > 64) return fail(PISA_EINVAL, "N or K_top out of range");
+    if (N > p->N_cap) return fail(PISA_ENOSPACE, "N=%lld exceeds N_cap=%lld", (long long)N, (long long)p->N_cap);
+    if (mode != PISA_ROUTE_FUSED && mode != PISA_ROUTE_TWO_STAGE && mode != PISA_ROUTE_LEVELS)
+        return fail(PISA_EINVAL, "mode=%d", mode);
     if (mode == PISA_ROUTE_FUSED) *bytes = 0;
     else if (mode == PISA_ROUTE_LEVELS) *bytes = levels_layout(p, N, K_top).total;
     else *bytes = two_stage_layout(p, N, K_top).total;

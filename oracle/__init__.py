@@ -70,6 +70,12 @@ def _load():
         lib.orc_bsa.argtypes = [P, P, P, i64, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
                                 i32, P, P, P, i32]
         lib.orc_bsa.restype = i32
+        lib.orc_route_reach.argtypes = [P, P, P, P, i64, P, P, P, i32, i64, i64, i32, i32, i32, i32,
+                                        i32, i32, i32, i32, P, dbl, i64, P, i32]
+        lib.orc_route_reach.restype = i32
+        lib.orc_bsa_scores.argtypes = [P, P, P, i64, P, P, i32, i64, i32, i32, i32, i32, i32, i32,
+                                       i32, P]
+        lib.orc_bsa_scores.restype = i32
         lib.orc_sparse_attn.argtypes = [P, P, P, i64, P, P, i32, i64, i64, i32, i32, i32, i32,
                                         P, i32, i32, P, P, i32]
         lib.orc_sparse_attn.restype = i32
@@ -162,6 +168,48 @@ def route(pyr: Pyramid, Qi, item_b, item_t, K_top: int, causal: bool = True,
     if rc != 0:
         raise ValueError("oracle route rejected its arguments")
     return dict(idx=idx, score=score, gap=gap, trace=tr)
+
+
+def route_reach(pyr: Pyramid, Qi, item_b, item_t, item_h, target, K_top: int, causal: bool = True,
+                score_kind: str = "lse", cap: float = 1e-3, budget: int = 200000,
+                threads: int | None = None):
+    """Smallest tie-resolution cost at which the route of each item can end in a given
+    selection: item k is query Qi[k] [H_q][d] at position item_t[k] of sequence item_b[k],
+    routed for KV head item_h[k]; target [n][K_top] is the selection to explain (-1 padded).
+
+    At every ranked level a kept set may drop a candidate that scores up to `cost` above a
+    kept one (Select_K resolved the other way within that margin); a path costs its largest
+    such margin. Returns eps [n]: 0 when target is the oracle's own selection, the smallest
+    path cost <= cap that reaches target, +inf when none does, NaN when the search hit its
+    budget before finding a path."""
+    Qi = _f32(Qi)
+    n, H_q, d = Qi.shape
+    b, t = _items(item_b, item_t)
+    hh = np.ascontiguousarray(item_h, dtype=np.int32)
+    tg = np.ascontiguousarray(target, dtype=np.int32).reshape(n, int(K_top))
+    eps = np.empty(n, dtype=np.float64)
+    rc = _load().orc_route_reach(_ptr(Qi), _ptr(b), _ptr(t), _ptr(hh), n, _ptr(pyr.K), _ptr(pyr.buf),
+                                 _ptr(pyr.off), pyr.B, pyr.N_alloc, pyr.N, pyr.H, H_q, d, pyr.C, pyr.g,
+                                 int(K_top), int(bool(causal)), SCORE_KINDS[score_kind], _ptr(tg),
+                                 float(cap), int(budget), _ptr(eps), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle reachability check rejected its arguments")
+    return eps
+
+
+def bsa_scores(pyr: Pyramid, Qi, item_b, item_t, K_top: int, causal: bool = True):
+    """Every leaf's BSA score u [n][H][M_1] for queries Qi [n][H_q][d]: the per-head softmax
+    over the scored leaves summed over the group for a scored leaf, +inf for a leaf kept
+    without a score, -inf for a leaf after the query."""
+    Qi = _f32(Qi)
+    n, H_q, d = Qi.shape
+    b, t = _items(item_b, item_t)
+    u = np.empty((n, pyr.H, pyr.M[1]), dtype=np.float64)
+    rc = _load().orc_bsa_scores(_ptr(Qi), _ptr(b), _ptr(t), n, _ptr(pyr.buf), _ptr(pyr.off), pyr.B,
+                                pyr.N, pyr.H, H_q, d, pyr.C, pyr.g, int(K_top), int(bool(causal)), _ptr(u))
+    if rc != 0:
+        raise ValueError("oracle bsa scores rejected its arguments")
+    return u
 
 
 def bsa(pyr: Pyramid, Qi, item_b, item_t, K_top: int, causal: bool = True,

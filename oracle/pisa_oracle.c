@@ -137,6 +137,12 @@ typedef struct {
     int sel_k;
     double *out;            /* attention: [n_items][H_q][d] */
     double *lse;            /* attention: [n_items][H_q] (may be NULL) */
+    /* tie-resolution reachability (orc_route_reach) */
+    const int32_t *item_h;  /* KV head of each item */
+    const int32_t *target;  /* [n_items][K_top] selection to explain, -1 padded */
+    double reach_cap;
+    int64_t reach_budget;
+    double *reach_eps;      /* [n_items] */
     int nthreads;
 } orc_problem;
 
@@ -377,6 +383,174 @@ static void route_one(const orc_problem *P, int64_t item, int h)
 }
 
 /* ---------------------------------------------------------------------------
+ * Tie-resolution reachability of a given selection (checker for near ties).
+ *
+ * Select_K (section 3.2 eq 17) is exact only up to the precision of the
+ * scores: two implementations whose scores differ by rounding may resolve a
+ * near tie differently at some level and then descend into another subtree.
+ * This function decides whether a selection T of one (item, KV head) is the
+ * outcome of such a resolution. It walks the same levels as route_one, but at
+ * every level that ranks it tries each kept set S of the non-forced candidates
+ * R with |S| = K_top - |F| whose swap cost
+ *     cost(S) = max(0, max over R \ S of u - min over S of u)
+ * is at most cap (cost 0 is the ordinary Top-K; a positive cost means a
+ * candidate scoring up to that much above a kept one was dropped). A path's
+ * cost is the largest cost of its levels. The result is the smallest path
+ * cost among the paths whose kept leaf set equals T: 0 when T is the route's
+ * own output, +inf when no path within cap reaches T, NaN when the search
+ * exceeded budget visited kept sets before finding any path (undecided; a
+ * path found before that bounds the smallest cost from above).
+ * Only kept sets that contain the level-l ancestors of every leaf of T can
+ * lead to T (a leaf is reached only through its ancestors), which keeps the
+ * search small; and since |S| is fixed, an S of cost <= cap holds every
+ * candidate scoring above the (K_top - |F|)-th score plus cap and none below
+ * the next score minus cap, so only the candidates between those bounds are
+ * enumerated.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const orc_problem *P;
+    int64_t item, t;
+    int h;
+    int64_t tgt[4096];
+    int ntgt;
+    double cap, best;
+    int64_t budget, visits;
+    int overflow;
+} reach_ctx;
+
+static void reach_level(reach_ctx *R, int l, const int64_t *Ain, int64_t nAin, double cost);
+
+/* Continue from kept set I (nI ids) of level l with path cost `cost`. */
+static void reach_next(reach_ctx *R, int l, int64_t *I, int64_t nI, double cost)
+{
+    const orc_problem *P = R->P;
+    if (l == 1) {
+        qsort(I, (size_t)nI, sizeof(int64_t), cmp_i64);
+        if (nI != R->ntgt) return;
+        for (int64_t k = 0; k < nI; k++) if (I[k] != R->tgt[k]) return;
+        if (cost < R->best) R->best = cost;
+        return;
+    }
+    int64_t *A = malloc(sizeof(int64_t) * (size_t)(nI * P->g > 0 ? nI * P->g : 1));
+    int64_t nA = 0;
+    for (int64_t k = 0; k < nI; k++) {
+        int64_t lo = I[k] * P->g, hi = lo + P->g < P->M[l - 1] ? lo + P->g : P->M[l - 1];
+        for (int64_t r = lo; r < hi; r++) A[nA++] = r;
+    }
+    qsort(A, (size_t)nA, sizeof(int64_t), cmp_i64);
+    reach_level(R, l - 1, A, nA, cost);
+    free(A);
+}
+
+static void reach_level(reach_ctx *R, int l, const int64_t *Ain, int64_t nAin, double cost)
+{
+    const orc_problem *P = R->P;
+    if (R->overflow || cost >= R->best) return;
+    int64_t span = span_of(l, P->C, P->g), den = span / P->C;
+    int64_t *A = malloc(sizeof(int64_t) * (size_t)(nAin > 0 ? nAin : 1));
+    int64_t *I = malloc(sizeof(int64_t) * (size_t)(nAin + 3));
+    scored_t *S = malloc(sizeof(scored_t) * (size_t)(nAin > 0 ? nAin : 1));
+    char *st = malloc((size_t)(nAin > 0 ? nAin : 1));      /* 0 out, 1 sure in, 2 pool, 3 required */
+    int64_t *pool = malloc(sizeof(int64_t) * (size_t)(nAin > 0 ? nAin : 1));
+    int64_t *cmb = malloc(sizeof(int64_t) * (size_t)(nAin > 0 ? nAin : 1));
+    int64_t nA = 0;
+    for (int64_t k = 0; k < nAin; k++)
+        if (!P->causal || Ain[k] * span <= R->t) A[nA++] = Ain[k];
+    /* every leaf of T must still be reachable through a candidate of this level */
+    for (int j = 0; j < R->ntgt; j++)
+        if (!contains(A, (int)nA, R->tgt[j] / den)) goto done;
+    if (nA <= P->K_top) {
+        memcpy(I, A, sizeof(int64_t) * (size_t)nA);
+        reach_next(R, l, I, nA, cost);
+        goto done;
+    }
+    {
+        int64_t F[3];
+        int nF = P->causal ? forced_set(P, R->t, l, F) : 0;
+        int64_t ns = 0;
+        for (int64_t k = 0; k < nA; k++) {
+            if (contains(F, nF, A[k])) continue;
+            S[ns].i = A[k];
+            S[ns].u = group_score(P, R->item, R->h, l, A[k]);
+            ns++;
+        }
+        qsort(S, (size_t)ns, sizeof(scored_t), cmp_scored);
+        int64_t keep = P->K_top - nF;
+        double hi = keep >= 1 ? S[keep - 1].u : INFINITY;
+        double lo = keep < ns ? S[keep].u : -INFINITY;
+        int64_t nsure = 0, npool = 0, nreq = 0;
+        for (int64_t k = 0; k < ns; k++) {
+            int req = 0;
+            for (int j = 0; j < R->ntgt; j++) if (R->tgt[j] / den == S[k].i) req = 1;
+            if (S[k].u > hi + R->cap) st[k] = 1;
+            else if (S[k].u < lo - R->cap) st[k] = 0;
+            else st[k] = 2;
+            if (req && st[k] == 0) goto done;        /* a needed ancestor cannot be kept */
+            if (req && st[k] == 2) st[k] = 3;
+            if (st[k] == 1) nsure++;
+            if (st[k] == 3) nreq++;
+            if (st[k] == 2) pool[npool++] = k;
+        }
+        int64_t m = keep - nsure - nreq;              /* free picks from the pool */
+        if (m < 0 || m > npool) goto done;
+        for (int64_t k = 0; k < m; k++) cmb[k] = k;
+        for (;;) {
+            if (++R->visits > R->budget) { R->overflow = 1; break; }
+            /* kept set: sure + required + pool[cmb[0..m)] */
+            char *in = st;  /* reuse: mark chosen pool entries as 4 temporarily */
+            for (int64_t k = 0; k < m; k++) in[pool[cmb[k]]] = 4;
+            double mn = INFINITY, mx = -INFINITY;
+            int64_t nI = 0;
+            for (int k = 0; k < nF; k++) I[nI++] = F[k];
+            for (int64_t k = 0; k < ns; k++) {
+                if (in[k] == 1 || in[k] == 3 || in[k] == 4) {
+                    I[nI++] = S[k].i;
+                    if (S[k].u < mn) mn = S[k].u;
+                } else if (S[k].u > mx) {
+                    mx = S[k].u;
+                }
+            }
+            for (int64_t k = 0; k < m; k++) in[pool[cmb[k]]] = 2;
+            double cl = mx - mn > 0.0 ? mx - mn : 0.0;
+            double nc = cl > cost ? cl : cost;
+            if (cl <= R->cap && nc < R->best) reach_next(R, l, I, nI, nc);
+            if (R->overflow || R->best <= cost) break;  /* cannot improve further */
+            /* next combination of m out of npool (lexicographic) */
+            int64_t k = m - 1;
+            while (k >= 0 && cmb[k] == npool - m + k) k--;
+            if (k < 0) break;
+            cmb[k]++;
+            for (int64_t j = k + 1; j < m; j++) cmb[j] = cmb[j - 1] + 1;
+        }
+    }
+done:
+    free(A); free(I); free(S); free(st); free(pool); free(cmb);
+}
+
+static void reach_one(const orc_problem *P, int64_t item)
+{
+    reach_ctx *R = malloc(sizeof(reach_ctx));
+    R->P = P;
+    R->item = item;
+    R->t = P->item_t[item];
+    R->h = P->item_h[item];
+    R->ntgt = 0;
+    const int32_t *T = P->target + item * (int64_t)P->K_top;
+    for (int k = 0; k < P->K_top; k++) if (T[k] >= 0) R->tgt[R->ntgt++] = T[k];
+    qsort(R->tgt, (size_t)R->ntgt, sizeof(int64_t), cmp_i64);
+    R->cap = P->reach_cap;
+    R->best = INFINITY;
+    R->budget = P->reach_budget;
+    R->visits = 0;
+    R->overflow = 0;
+    int64_t root = 0;
+    reach_level(R, P->L, &root, 1, 0.0);
+    /* on overflow a path already found still bounds the smallest cost from above */
+    P->reach_eps[item] = (R->overflow && isinf(R->best)) ? NAN : R->best;
+    free(R);
+}
+
+/* ---------------------------------------------------------------------------
  * Exhaustive single-level selector in the style of BSA (section 3.1 eq 2-5),
  * with the grouped-query rule the page describes for its BSA baseline
  * (section 4.1 and appendix C: scores are normalised within each query head
@@ -387,48 +561,68 @@ static void route_one(const orc_problem *P, int64_t item, int h)
  * forced leaves are kept; if at most K_top leaves are eligible all are kept.
  * kbar_i is the level-1 summary of the pyramid (mean pooling, eq 2).
  * ------------------------------------------------------------------------- */
+/* u_i = sum over the group's heads of the per-head softmax of z_{h',i} over the
+ * scored leaves S[0..ns) (ids set by the caller; u written into S[k].u). */
+static void bsa_group_probs(const orc_problem *P, int64_t item, int h, scored_t *S, int64_t ns)
+{
+    int64_t b = P->item_b[item];
+    int G = P->H_q / P->H;
+    double *z = malloc(sizeof(double) * (size_t)(ns > 0 ? ns : 1));
+    const double *lev1 = P->pyr + P->off[1] + (b * P->H + h) * P->M[1] * P->d;
+    double scale = 1.0 / sqrt((double)P->d);
+    for (int64_t k = 0; k < ns; k++) S[k].u = 0.0;
+    for (int j = 0; j < G; j++) {
+        const float *q = P->Q + (item * P->H_q + (int64_t)h * G + j) * P->d;
+        for (int64_t k = 0; k < ns; k++) z[k] = dot_fd(q, lev1 + S[k].i * P->d, P->d) * scale;
+        double lz = logsumexp(z, ns);
+        for (int64_t k = 0; k < ns; k++) S[k].u += exp(z[k] - lz);
+    }
+    free(z);
+}
+
+/* The eligible leaf count of query t (all M_1 leaves when not causal) and the
+ * scored set: eligible minus forced; returns ns. */
+static int64_t bsa_scored_set(const orc_problem *P, int64_t t, scored_t *S, int64_t *E_out,
+                              int64_t *F, int *nF_out)
+{
+    int64_t E = P->causal ? t / P->C + 1 : P->M[1];
+    if (E > P->M[1]) E = P->M[1];
+    int nF = P->causal ? forced_set(P, t, 1, F) : 0;
+    int64_t ns = 0;
+    for (int64_t i = 0; i < E; i++) {
+        if (contains(F, nF, i)) continue;
+        S[ns].i = i;
+        S[ns].u = 0.0;
+        ns++;
+    }
+    *E_out = E;
+    *nF_out = nF;
+    return ns;
+}
+
 static void bsa_one(const orc_problem *P, int64_t item, int h)
 {
     int64_t t = P->item_t[item];
-    int64_t b = P->item_b[item];
     int Kt = P->K_top;
-    int G = P->H_q / P->H;
-    int64_t E = P->causal ? t / P->C + 1 : P->M[1];
-    if (E > P->M[1]) E = P->M[1];
     int64_t I[4096];
     double Iu[4096];
     int nI = 0;
     double gap = INFINITY;
+    int64_t E, F[3];
+    int nF;
+    scored_t *S = malloc(sizeof(scored_t) * (size_t)P->M[1]);
+    int64_t ns = bsa_scored_set(P, t, S, &E, F, &nF);
     if (E <= Kt) {
         for (int64_t i = 0; i < E; i++) { I[nI] = i; Iu[nI] = INFINITY; nI++; }
     } else {
-        int64_t F[3];
-        int nF = P->causal ? forced_set(P, t, 1, F) : 0;
-        scored_t *S = malloc(sizeof(scored_t) * (size_t)E);
-        double *z = malloc(sizeof(double) * (size_t)E);
-        int64_t ns = 0;
-        for (int64_t i = 0; i < E; i++) {
-            if (contains(F, nF, i)) continue;
-            S[ns].i = i;
-            S[ns].u = 0.0;
-            ns++;
-        }
-        const double *lev1 = P->pyr + P->off[1] + (b * P->H + h) * P->M[1] * P->d;
-        double scale = 1.0 / sqrt((double)P->d);
-        for (int j = 0; j < G; j++) {
-            const float *q = P->Q + (item * P->H_q + (int64_t)h * G + j) * P->d;
-            for (int64_t k = 0; k < ns; k++) z[k] = dot_fd(q, lev1 + S[k].i * P->d, P->d) * scale;
-            double lz = logsumexp(z, ns);
-            for (int64_t k = 0; k < ns; k++) S[k].u += exp(z[k] - lz);
-        }
+        bsa_group_probs(P, item, h, S, ns);
         qsort(S, (size_t)ns, sizeof(scored_t), cmp_scored);
         int keep = Kt - nF;
         for (int k = 0; k < nF; k++) { I[nI] = F[k]; Iu[nI] = INFINITY; nI++; }
         for (int k = 0; k < keep; k++) { I[nI] = S[k].i; Iu[nI] = S[k].u; nI++; }
         if (keep >= 1 && keep < ns) gap = S[keep - 1].u - S[keep].u;
-        free(S);
-        free(z);
     }
+    free(S);
     emit(P, item, h, I, Iu, nI);
     if (P->gap) P->gap[item * P->H + h] = gap;
 }
@@ -566,7 +760,7 @@ static void attn_bwd_group(const orc_problem *P, int64_t b, int h)
  * ------------------------------------------------------------------------- */
 typedef struct {
     const orc_problem *P;
-    int which;   /* 0 route, 1 bsa, 2 attention, 3 attention backward */
+    int which;   /* 0 route, 1 bsa, 2 attention, 3 attention backward, 4 reachability */
     int tid;
 } worker_arg;
 
@@ -577,6 +771,10 @@ static void *worker(void *p)
     if (w->which == 3) {  /* attention backward: one task per (sequence, KV head) */
         for (int64_t k = w->tid; k < (int64_t)P->B * P->H; k += P->nthreads)
             attn_bwd_group(P, k / P->H, (int)(k % P->H));
+        return NULL;
+    }
+    if (w->which == 4) {  /* reachability: one task per item (its KV head is item_h) */
+        for (int64_t k = w->tid; k < P->n_items; k += P->nthreads) reach_one(P, k);
         return NULL;
     }
     int per = w->which == 2 ? P->H_q : P->H;
@@ -657,6 +855,29 @@ int orc_route(const float *Q, const int64_t *item_b, const int64_t *item_t, int6
                             g, K_top, causal, 0, idx, score, gap, trace, nthreads);
 }
 
+/* Smallest tie-resolution cost (see reach_one) at which the route of item k
+ * for KV head item_h[k] can end in the selection target [n_items][K_top]
+ * (ascending or not, -1 padded), searching kept sets of cost <= cap and at
+ * most budget of them per item. eps [n_items]. Returns 0 or -1. */
+int orc_route_reach(const float *Q, const int64_t *item_b, const int64_t *item_t,
+                    const int32_t *item_h, int64_t n_items, const float *K, const double *pyr,
+                    const int64_t *off, int B, int64_t N_alloc, int64_t N, int H, int H_q, int d,
+                    int C, int g, int K_top, int causal, int score_kind, const int32_t *target,
+                    double cap, int64_t budget, double *eps, int nthreads)
+{
+    orc_problem P;
+    if (score_kind < 0 || score_kind > 2 || !(cap >= 0.0) || budget < 1) return -1;
+    if (setup(&P, Q, item_b, item_t, n_items, K, pyr, off, B, N_alloc, N, H, H_q, d, C, g,
+              K_top, causal, nthreads)) return -1;
+    for (int64_t k = 0; k < n_items; k++)
+        if (item_h[k] < 0 || item_h[k] >= H) return -1;
+    P.score_kind = score_kind;
+    P.item_h = item_h; P.target = target; P.reach_cap = cap; P.reach_budget = budget;
+    P.reach_eps = eps;
+    run_pool(&P, 4);
+    return 0;
+}
+
 /* Exhaustive BSA-style selection for n_items queries. Returns 0 or -1. */
 int orc_bsa(const float *Q, const int64_t *item_b, const int64_t *item_t, int64_t n_items,
             const double *pyr, const int64_t *off, int B, int64_t N, int H, int H_q, int d,
@@ -668,6 +889,35 @@ int orc_bsa(const float *Q, const int64_t *item_b, const int64_t *item_t, int64_
               K_top, causal, nthreads)) return -1;
     P.idx = idx; P.score = score; P.gap = gap;
     run_pool(&P, 1);
+    return 0;
+}
+
+/* Every leaf's BSA score for n_items queries and every KV head:
+ * u [n_items][H][M_1] holds u_i of eq 3-5 (per-head softmax, summed over the
+ * group) for a scored leaf, +inf for a leaf kept without a score (forced, or
+ * every eligible leaf when at most K_top are eligible) and -inf for a leaf
+ * after the query. Exposed so tests can check the normalisation itself.
+ * Returns 0 or -1. */
+int orc_bsa_scores(const float *Q, const int64_t *item_b, const int64_t *item_t, int64_t n_items,
+                   const double *pyr, const int64_t *off, int B, int64_t N, int H, int H_q, int d,
+                   int C, int g, int K_top, int causal, double *u)
+{
+    orc_problem P;
+    if (setup(&P, Q, item_b, item_t, n_items, NULL, pyr, off, B, N, N, H, H_q, d, C, g,
+              K_top, causal, 1)) return -1;
+    scored_t *S = malloc(sizeof(scored_t) * (size_t)P.M[1]);
+    for (int64_t item = 0; item < n_items; item++)
+        for (int h = 0; h < H; h++) {
+            double *o = u + (item * H + h) * P.M[1];
+            int64_t E, F[3];
+            int nF;
+            int64_t ns = bsa_scored_set(&P, item_t[item], S, &E, F, &nF);
+            for (int64_t i = 0; i < P.M[1]; i++) o[i] = i < E ? INFINITY : -INFINITY;
+            if (E <= K_top) continue;
+            bsa_group_probs(&P, item, h, S, ns);
+            for (int64_t k = 0; k < ns; k++) o[S[k].i] = S[k].u;
+        }
+    free(S);
     return 0;
 }
 

@@ -142,6 +142,23 @@ def test_route_prefill_scored_validation(lib):
         assert scored(kind, K_top=2) == EINVAL
 
 
+def test_workspace_query_validates_descriptor(lib):
+    """The workspace query walks the pyramid geometry, so it must reject a zeroed or
+    hand-edited descriptor (C = 0 or g = 1 would divide by zero or never terminate)."""
+    n = ctypes.c_size_t(7)
+    zero = pisa._PyramidDesc()
+    for mode in (pisa.LEVELS, pisa.TWO_STAGE, pisa.FUSED):
+        assert lib.pisa_route_prefill_workspace(ctypes.byref(zero), 4096, 16, 8, mode, ctypes.byref(n)) == EINVAL
+    bad = fake_pyramid(lib)
+    bad.g = 1
+    assert lib.pisa_route_prefill_workspace(ctypes.byref(bad), 4096, 16, 8, pisa.LEVELS, ctypes.byref(n)) == EUNSUPPORTED
+    desc = fake_pyramid(lib)
+    assert lib.pisa_route_prefill_workspace(ctypes.byref(desc), 4096, 16, 8, 9, ctypes.byref(n)) == EINVAL
+    assert lib.pisa_route_prefill_workspace(ctypes.byref(desc), 4097, 16, 8, pisa.LEVELS, ctypes.byref(n)) == ENOSPACE
+    assert lib.pisa_route_prefill_workspace(None, 4096, 16, 8, pisa.LEVELS, ctypes.byref(n)) == EINVAL
+    assert n.value == 7  # untouched on error
+
+
 def test_descriptor_must_come_from_plan(lib):
     desc = fake_pyramid(lib)
     desc.off[2] += 64

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from hierarchical_top_amd import pisa, synth
-from tests.parity import compare
+from tests.parity import bsa_reach, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -137,8 +137,10 @@ def _bsa_compare(w, t, causal, K_top):
         fin = np.where(np.isfinite(s), s, np.nan)
         ukth = np.nan_to_num(np.nanmin(fin, axis=-1), nan=1.0)
         band = 1e-4 * np.abs(ukth) + 1e-9
+        # strict band a tenth of that: fp32 scores of summed probabilities are within ~1e-7 relative
         stats = compare(idx[b][:, t].transpose(1, 0, 2), score[b][:, t].transpose(1, 0, 2), orc, t, w.C, K_top,
-                        causal=causal, band=band, score_tol=1e-7, score_rtol=1e-4, M1=-(-w.N // w.C))
+                        causal=causal, band=band, strict=band / 10, score_tol=1e-7, score_rtol=1e-4,
+                        M1=-(-w.N // w.C), reach=bsa_reach(opyr, Q[b, t].float().numpy(), b, t, K_top, causal))
         print(w.name, b, stats)
 
 

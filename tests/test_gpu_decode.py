@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from hierarchical_top_amd import pisa, synth
-from tests.parity import compare
+from tests.parity import compare, route_reach
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,8 @@ def _check_route(K, q, b, n, C, g, K_top, idx, score, score_kind="lse"):
     opyr = oracle.Pyramid(K[b:b + 1, :n].float().cpu().numpy(), n, C, g)
     orc = oracle.route(opyr, q[b:b + 1].float().cpu().numpy(), [0], [n - 1], K_top, score_kind=score_kind)
     st = compare(idx[b:b + 1].cpu().numpy(), score[b:b + 1].cpu().numpy(), orc, np.array([n - 1]), C, K_top,
-                 max_near_tie_frac=1.0)
+                 max_near_tie_frac=1.0,
+                 reach=route_reach(opyr, q[b:b + 1].float().cpu().numpy(), 0, [n - 1], K_top, score_kind=score_kind))
     return st, orc["idx"]
 
 

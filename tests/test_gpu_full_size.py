@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from hierarchical_top_amd import pisa, synth
-from tests.parity import compare
+from tests.parity import bsa_reach, compare, route_reach
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,8 @@ def test_p256k_level_router_sampled(p256k, kind):
     orc = oracle.route(opyr, Q[0, t].float().numpy(), [0] * len(t), t, w.K_top, score_kind=kind)
     # four ranked levels at this length, each a chance for a sub-1e-3 margin: about a third of
     # the items have one somewhere (33 % measured); the cap only guards against a vacuous test
-    stats = compare(gi, gs, orc, t, w.C, w.K_top, max_near_tie_frac=0.6)
+    stats = compare(gi, gs, orc, t, w.C, w.K_top, max_near_tie_frac=0.6,
+                    reach=route_reach(opyr, Q[0, t].float().numpy(), 0, t, w.K_top, score_kind=kind))
     print(kind, stats)
 
 
@@ -73,7 +74,8 @@ def test_p256k_exhaustive_selector_sampled(p256k):
     ukth = np.nan_to_num(np.nanmin(fin, axis=-1), nan=1.0)
     band = 1e-4 * np.abs(ukth) + 1e-9
     stats = compare(idx[0][:, ts].cpu().numpy().transpose(1, 0, 2), score[0][:, ts].cpu().numpy().transpose(1, 0, 2),
-                    orc, ts, w.C, w.K_top, band=band, score_tol=1e-7, score_rtol=1e-4)
+                    orc, ts, w.C, w.K_top, band=band, strict=band / 10, score_tol=1e-7, score_rtol=1e-4,
+                    reach=bsa_reach(opyr, Q[0, ts].float().numpy(), 0, ts, w.K_top))
     print("bsa", stats)
 
 
@@ -98,4 +100,5 @@ def test_level_router_across_leaf_windows():
         orc = oracle.route(opyr, Q[b, t].float().numpy(), [b] * len(t), t, w.K_top)
         gi = idx[b][:, t].cpu().numpy().transpose(1, 0, 2)
         gs = score[b][:, t].cpu().numpy().transpose(1, 0, 2)
-        print("b", b, compare(gi, gs, orc, t, w.C, w.K_top, max_near_tie_frac=0.6))
+        print("b", b, compare(gi, gs, orc, t, w.C, w.K_top, max_near_tie_frac=0.6,
+                              reach=route_reach(opyr, Q[b, t].float().numpy(), b, t, w.K_top)))

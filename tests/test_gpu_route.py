@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from hierarchical_top_amd import pisa, synth
-from tests.parity import compare
+from tests.parity import compare, route_reach
 
 pytestmark = pytest.mark.gpu
 
@@ -119,13 +119,14 @@ def test_route_matches_oracle(mode, case, K_top, causal, sample):
     print("case", case, "mode", mode, "K_top", K_top, "causal", causal, flush=True)
     Q, K = _inputs(w)
     t = _positions(w, sample)
-    _, orc = _oracle_route(w, Q, K, K_top, causal, t)
+    opyr, orc = _oracle_route(w, Q, K, K_top, causal, t)
     _, idx, score = _gpu_route(w, Q, K, K_top, causal, MODES[mode])
     M1 = -(-w.N // w.C)
     for b in range(w.B):
         gi = idx[b][:, t].transpose(1, 0, 2)
         gs = score[b][:, t].transpose(1, 0, 2)
-        stats = compare(gi, gs, orc[b], t, w.C, K_top, causal=causal, M1=M1)
+        stats = compare(gi, gs, orc[b], t, w.C, K_top, causal=causal, M1=M1,
+                        reach=route_reach(opyr, Q[b, t].float().numpy(), b, t, K_top, causal))
         print(case, mode, b, stats)
 
 
@@ -149,7 +150,7 @@ def test_route_pisa1_pisa2_match_oracle(kind, case, K_top, causal, sample, mode)
     print("case", case, "score", kind, "mode", mode, "K_top", K_top, "causal", causal, flush=True)
     Q, K = _inputs(w)
     t = _positions(w, sample)
-    _, orc = _oracle_route(w, Q, K, K_top, causal, t, score_kind=kind)
+    opyr, orc = _oracle_route(w, Q, K, K_top, causal, t, score_kind=kind)
     _, idx, score = _gpu_route(w, Q, K, K_top, causal, MODES[mode], score_kind=kind)
     M1 = -(-w.N // w.C)
     # PISA-1's upper-level scores are logits of mean keys, whose spread shrinks with the span of
@@ -159,7 +160,8 @@ def test_route_pisa1_pisa2_match_oracle(kind, case, K_top, causal, sample, mode)
     for b in range(w.B):
         gi = idx[b][:, t].transpose(1, 0, 2)
         gs = score[b][:, t].transpose(1, 0, 2)
-        stats = compare(gi, gs, orc[b], t, w.C, K_top, causal=causal, M1=M1, max_near_tie_frac=cap)
+        stats = compare(gi, gs, orc[b], t, w.C, K_top, causal=causal, M1=M1, max_near_tie_frac=cap,
+                        reach=route_reach(opyr, Q[b, t].float().numpy(), b, t, K_top, causal, score_kind=kind))
         print(case, kind, b, stats)
 
 

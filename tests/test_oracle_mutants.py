@@ -49,6 +49,13 @@ MUTANTS = [
      "P->recall[o] = (double)hit / (double)(Kt + 1);"),
     ("quality_future_key", "if (hi > i + 1) hi = i + 1;", "if (hi > i + 2) hi = i + 2;"),
     ("bwd_mask_self", "if (P->causal && t < j) continue;", "if (P->causal && t <= j) continue;"),
+    ("bsa_exp_unnormalised", "S[k].u += exp(z[k] - lz);", "S[k].u += exp(z[k]);"),
+    ("bsa_forced_in_softmax", "        if (contains(F, nF, i)) continue;\n        S[ns].i = i;",
+     "        S[ns].i = i;"),
+    ("reach_no_cost", "double cl = mx - mn > 0.0 ? mx - mn : 0.0;", "double cl = 0.0;"),
+    ("reach_last_level_cost", "double nc = cl > cost ? cl : cost;", "double nc = cl;"),
+    ("reach_sure_in_without_band", "if (S[k].u > hi + R->cap) st[k] = 1;", "if (S[k].u > hi) st[k] = 1;"),
+    ("reach_pool_too_narrow", "else if (S[k].u < lo - R->cap) st[k] = 0;", "else if (S[k].u < lo) st[k] = 0;"),
     ("ascending_scores", "if (x->u > y->u) return -1;\n    if (x->u < y->u) return 1;",
      "if (x->u < y->u) return -1;\n    if (x->u > y->u) return 1;"),
 ]

@@ -8,6 +8,7 @@ Each test checks the oracle (oracle/pisa_oracle.c) against one of:
     appendix B, the Jensen sandwich of appendix A.1, causality).
 All citations refer to "Block Sparse Attention with Log-Linear Complexity".
 """
+import itertools
 import json
 import math
 import os
@@ -408,6 +409,164 @@ def test_bsa_matches_library_softmax():
                                            np.sort(r["score"][n, h][np.isfinite(r["score"][n, h])])[::-1],
                                            atol=1e-12)
             assert [int(x) for x in r["idx"][n, h] if x >= 0] == want
+
+
+def test_bsa_two_heads_per_head_normalisation():
+    """Two query heads whose unnormalised scores favour leaf 1 while the per-head softmax,
+    summed, favours leaf 0 (closed form in tests/golden): the normalisation is per head."""
+    w = GOLD["bsa_two_heads"]
+    K = np.array(w["keys"], np.float32).reshape(1, w["N"], 1, w["d"])
+    pyr = oracle.Pyramid(K, w["N"], w["C"], w["g"])
+    q = np.array(w["q"], np.float32).reshape(1, 2, w["d"])
+    u = oracle.bsa_scores(pyr, q, [0], [w["N"] - 1], 1, causal=False)[0, 0]
+    np.testing.assert_allclose(u, [ev(x) for x in w["u"]], rtol=0, atol=1e-14)
+    for pick in w["picks"]:
+        r = oracle.bsa(pyr, q, [0], [w["N"] - 1], pick["K_top"], causal=False)
+        assert [int(x) for x in r["idx"][0, 0] if x >= 0] == pick["idx"]
+        kept = r["score"][0, 0][:len(pick["idx"])]
+        np.testing.assert_allclose(kept, [ev(w["u"][i]) for i in pick["idx"]], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bsa_probabilities_sum_to_group_size(causal):
+    """Each head's softmax over the scored leaves sums to one, so the grouped scores of one
+    (query, KV head) sum to G_Q over the scored set; forced leaves carry +inf, future -inf."""
+    rng = np.random.default_rng(16)
+    N, C, g, d, H, Hq, Kt = 700, 16, 4, 16, 2, 6, 5
+    K = rng.standard_normal((1, N, H, d)).astype(np.float32)
+    Q = (2.0 * rng.standard_normal((30, Hq, d))).astype(np.float32)
+    t = np.linspace(0, N - 1, 30).astype(np.int64)
+    pyr = oracle.Pyramid(K, N, C, g)
+    u = oracle.bsa_scores(pyr, Q, [0] * 30, t, Kt, causal=causal)
+    M1 = pyr.M[1]
+    for n in range(30):
+        c = t[n] // C if causal else M1 - 1
+        E = c + 1
+        for h in range(H):
+            row = u[n, h]
+            assert np.isneginf(row[E:]).all()
+            if E <= Kt:
+                assert np.isposinf(row[:E]).all()
+                continue
+            F = sorted({0, c, c - 1}) if causal else []
+            assert np.isposinf(row[F]).all() and np.isfinite(np.delete(row[:E], F)).all()
+            assert np.delete(row[:E], F).sum() == pytest.approx(Hq // H, abs=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Tie-resolution reachability (the checker behind the near-tie parity protocol)
+# --------------------------------------------------------------------------
+
+def test_w1_tie_resolution_costs():
+    w = GOLD["w1_tie_resolutions"]
+    pyr, q = _w1_pyr()
+    qi = q.reshape(1, 1, 1)
+    for tgt in w["targets"]:
+        eps = oracle.route_reach(pyr, qi, [0], [w["t"]], [0], np.array([tgt["idx"]]), w["K_top"],
+                                 causal=False, cap=10.0)
+        assert eps[0] == pytest.approx(ev(tgt["cost"]), abs=1e-13), tgt["note"]
+        cost = ev(tgt["cost"])
+        if cost > 0:  # a cap below the cost rules the resolution out
+            eps = oracle.route_reach(pyr, qi, [0], [w["t"]], [0], np.array([tgt["idx"]]), w["K_top"],
+                                     causal=False, cap=cost * 0.99)
+            assert np.isposinf(eps[0])
+    for bad in w["unreachable"]:
+        eps = oracle.route_reach(pyr, qi, [0], [w["t"]], [0], np.array([bad]), w["K_top"], causal=False,
+                                 cap=10.0)
+        assert np.isposinf(eps[0]), w["unreachable_note"]
+
+
+def _brute_force_paths(pyr, q_heads, h, t, Kt, causal):
+    """Every kept leaf set reachable by keeping ANY K_top - |F| of the non-forced candidates
+    at each ranked level (no pruning), with the smallest path cost: the largest, over the
+    ranked levels, of max(0, best dropped score - worst kept score)."""
+    C, g, M = pyr.C, pyr.g, pyr.M
+    c = t // C
+    memo = {}
+
+    def u(l, i):
+        if (l, i) not in memo:
+            memo[(l, i)] = sum(oracle.score(pyr, q, 0, h, l, i) for q in q_heads)
+        return memo[(l, i)]
+
+    out = {}
+
+    def rec(l, A, cost):
+        span = C * g ** (l - 1)
+        if causal:
+            A = [i for i in A if i * span <= t]
+        if len(A) <= Kt:
+            choices = [(list(A), 0.0)]
+        else:
+            den = span // C
+            F = sorted({0, c // den} | ({(c - 1) // den} if c >= 1 else set())) if causal else []
+            R = [i for i in A if i not in F]
+            choices = []
+            for S in itertools.combinations(R, Kt - len(F)):
+                dropped = [u(l, i) for i in R if i not in S]
+                cl = max(0.0, max(dropped) - min(u(l, i) for i in S)) if S else 0.0
+                choices.append((F + list(S), cl))
+        for I, cl in choices:
+            nc = max(cost, cl)
+            if l == 1:
+                key = tuple(sorted(I))
+                out[key] = min(out.get(key, math.inf), nc)
+            else:
+                rec(l - 1, sorted(r for i in I for r in range(i * g, min(i * g + g, M[l - 1]))), nc)
+
+    rec(pyr.L, [0], 0.0)
+    return out
+
+
+@pytest.mark.parametrize("N,C,g,Kt,causal", [(64, 8, 2, 2, False), (128, 8, 2, 4, True), (100, 4, 3, 4, True)])
+def test_reach_matches_brute_force(N, C, g, Kt, causal):
+    """On trees small enough to enumerate every path, the checker's smallest cost for each
+    reachable leaf set equals the brute-force minimum, a cap just below it rules the set
+    out, and sets that no path reaches get +inf."""
+    rng = np.random.default_rng(17 + N)
+    d, H, Hq = 8, 1, 2
+    K = (0.5 * rng.standard_normal((1, N, H, d))).astype(np.float32)
+    pyr = oracle.Pyramid(K, N, C, g)
+    M1 = pyr.M[1]
+    checked = 0
+    for t in ([N - 1, N // 2, 3 * C + 1] if causal else [N - 1]):
+        q = rng.standard_normal((1, Hq, d)).astype(np.float32)
+        paths = _brute_force_paths(pyr, list(q[0]), 0, t, Kt, causal)
+        sets = list(paths)
+        tg = np.full((len(sets), Kt), -1, np.int32)
+        for k, s in enumerate(sets):
+            tg[k, :len(s)] = s
+        eps = oracle.route_reach(pyr, np.repeat(q, len(sets), 0), [0] * len(sets), [t] * len(sets),
+                                 [0] * len(sets), tg, Kt, causal=causal, cap=1e9)
+        np.testing.assert_allclose(eps, [paths[s] for s in sets], rtol=0, atol=1e-12)
+        r = oracle.route(pyr, q, [0], [t], Kt, causal=causal)
+        assert paths[tuple(int(x) for x in r["idx"][0, 0] if x >= 0)] == 0.0
+        pos = [k for k, s in enumerate(sets) if paths[s] > 0]
+        if pos:
+            sub = tg[pos]
+            eps2 = oracle.route_reach(pyr, np.repeat(q, len(pos), 0), [0] * len(pos), [t] * len(pos),
+                                      [0] * len(pos), sub, Kt, causal=causal,
+                                      cap=0.999 * min(paths[sets[k]] for k in pos))
+            assert np.isposinf(eps2).all()
+        # leaf sets of the right size that no path reaches
+        E = min(M1, t // C + 1) if causal else M1
+        extra = [s for s in itertools.combinations(range(E), min(Kt, E)) if s not in paths][:40]
+        if extra:
+            tg3 = np.array([list(s) + [-1] * (Kt - len(s)) for s in extra], np.int32)
+            eps3 = oracle.route_reach(pyr, np.repeat(q, len(extra), 0), [0] * len(extra), [t] * len(extra),
+                                      [0] * len(extra), tg3, Kt, causal=causal, cap=1e9)
+            assert np.isposinf(eps3).all()
+        checked += len(sets)
+    assert checked > 10
+
+
+def test_reach_reports_undecided_on_budget():
+    """With a budget of one kept set per item the search cannot reach a set that needs a
+    resolution below the top level: NaN (undecided), never a false +inf or a false cost."""
+    pyr, q = _w1_pyr()
+    eps = oracle.route_reach(pyr, q.reshape(1, 1, 1), [0], [7], [0], np.array([[3]]), 1, causal=False,
+                             cap=10.0, budget=1)
+    assert np.isnan(eps[0])
 
 
 @pytest.mark.parametrize("causal", [True, False])
