@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "attn_bwd.hpp"
 #include "quality.hpp"
 #include "pisa_internal.hpp"
@@ -14,6 +16,15 @@ using namespace pisa;
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Library-owned workspace of pisa_route_prefill_noalloc, one copy per device,
+// held until the process ends. In host code `scratch` only names the symbol:
+// its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)PISA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 // Armed stage events of this host thread (pisa_time_stage): a queue of up to
 // kStageSlots (start, stop) pairs per stage, consumed one per stage occurrence.
@@ -330,6 +341,39 @@ pisa_status pisa_route_prefill_workspace(const pisa_pyramid* p, int64_t N, int32
     else if (mode == PISA_ROUTE_LEVELS) *bytes = levels_layout(p, N, K_top).total;
     else *bytes = two_stage_layout(p, N, K_top).total;
     return ok();
+}
+
+pisa_status pisa_route_prefill_noalloc(const pisa_pyramid* p, const void* Q, const void* K, pisa_dtype dt,
+                                       int64_t N, int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group,
+                                       int32_t* idx, float* score, void* stream)
+{
+    pisa_status s = check_pyramid(p);
+    if (s != PISA_OK) return s;
+    if (N < 1 || K_top < 1 || K_top > 64) return fail(PISA_EINVAL, "N or K_top out of range");
+    if (N > p->N_cap) return fail(PISA_ENOSPACE, "N=%lld exceeds N_cap=%lld", (long long)N, (long long)p->N_cap);
+    const size_t need = levels_layout(p, N, K_top).total;
+    if (need > kScratchBytes)
+        return fail(PISA_ENOSPACE, "pisa_route_prefill_noalloc: %zu bytes of workspace needed, the library's "
+                    "scratch holds %zu (use pisa_route_prefill with a workspace)", need, kScratchBytes);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "pisa_route_prefill_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(PISA_EUNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+    void* ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            // the current device's copy of the array (each device holds its own)
+            e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+            if (e != hipSuccess) {
+                g_scratch_ptr[dev] = nullptr;
+                return hip_fail(e, "pisa_route_prefill_noalloc: hipGetSymbolAddress");
+            }
+        }
+        ws = g_scratch_ptr[dev];
+    }
+    return pisa_route_prefill_scored(p, Q, K, dt, N, H_q, K_top, causal, gqa_group, PISA_ROUTE_LEVELS,
+                                     PISA_SCORE_LSE, idx, score, ws, kScratchBytes, stream);
 }
 
 pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void* K, pisa_dtype dt, int64_t N,

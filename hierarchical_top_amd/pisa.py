@@ -19,6 +19,8 @@ LIB_PATH = Path(__file__).resolve().parent / "libpisa.so"
 MAX_LEVELS = 32
 F32, BF16 = 0, 1
 TWO_STAGE, FUSED, LEVELS = 0, 1, 2
+# size of the library-owned workspace of pisa_route_prefill_noalloc (PISA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 # block scores (pisa_score_kind): PISA's LSE, PISA-1 (mean), PISA-2 (mean + var / 2)
 SCORE_KINDS = {"lse": 0, "mean": 1, "mean_var": 2}
 
@@ -62,6 +64,7 @@ def lib():
                                    c_size, c_p],
             "pisa_route_prefill_scored": [P, c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_p,
                                           c_p, c_p, c_size, c_p],
+            "pisa_route_prefill_noalloc": [P, c_p, c_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_route_decode": [P, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_route_decode_scored": [P, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p],
             "pisa_sparse_attn": [c_p, c_p, c_p, c_i32, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_p,
@@ -96,7 +99,7 @@ def lib():
 
 
 EXPORTS = ["pisa_pyramid_plan", "pisa_build_pyramid", "pisa_pyramid_append", "pisa_route_prefill_workspace",
-           "pisa_route_prefill", "pisa_route_prefill_scored", "pisa_route_decode",
+           "pisa_route_prefill", "pisa_route_prefill_scored", "pisa_route_prefill_noalloc", "pisa_route_decode",
            "pisa_route_decode_scored", "pisa_sparse_attn", "pisa_sparse_attn_workspace",
            "pisa_sparse_attn_clustered", "pisa_sparse_attn_bwd_workspace", "pisa_sparse_attn_bwd",
            "pisa_selection_quality_workspace", "pisa_selection_quality", "pisa_bsa_select", "pisa_time_stage",
@@ -200,6 +203,22 @@ def route_prefill(pyr: Pyramid, Q: torch.Tensor, K: torch.Tensor, N: int, K_top:
                                            1 if causal else 0, H_q // pyr.H_kv, mode, SCORE_KINDS[score_kind],
                                            _ptr(idx), _ptr(score), _ptr(ws) if need else None, need, _stream()))
     return (idx, score) if with_score else idx
+
+
+def route_prefill_noalloc(pyr: Pyramid, Q: torch.Tensor, K: torch.Tensor, N: int, K_top: int, causal: bool = True,
+                          out: torch.Tensor | None = None, score_out: torch.Tensor | None = None):
+    """route_prefill with the level-synchronous router and the library's own scratch array as
+    its workspace (pisa_route_prefill_noalloc): returns (idx, score) [B][H_kv][N][K_top]. Only
+    the outputs are allocated here, and not at all when out / score_out are given."""
+    _dev(Q, K)
+    B, Nq, H_q, d = Q.shape
+    assert Nq == N and K.dtype == Q.dtype
+    idx = out if out is not None else torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.int32, device=Q.device)
+    score = score_out if score_out is not None else torch.empty(B, pyr.H_kv, N, K_top, dtype=torch.float32,
+                                                                device=Q.device)
+    _check(lib().pisa_route_prefill_noalloc(ctypes.byref(pyr.desc), _ptr(Q), _ptr(K), _dt(Q), N, H_q, K_top,
+                                            1 if causal else 0, H_q // pyr.H_kv, _ptr(idx), _ptr(score), _stream()))
+    return idx, score
 
 
 def route_decode(pyr: Pyramid, q: torch.Tensor, K: torch.Tensor, seqlen: torch.Tensor, K_top: int,

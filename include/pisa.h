@@ -150,6 +150,27 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
                                float* score, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Allocation-free prefill routing, for callers that cannot allocate device
+ * memory (code under stream capture, serving loops, harnesses that forbid
+ * allocation). Same semantics, outputs and errors as pisa_route_prefill with
+ * mode PISA_ROUTE_LEVELS and no caller workspace: the workspace is a
+ * library-owned device array of PISA_NOALLOC_SCRATCH_BYTES per device (held
+ * until the process ends), so the call accepts only shapes whose level-router
+ * workspace (pisa_route_prefill_workspace with PISA_ROUTE_LEVELS) fits in it,
+ * and returns PISA_ENOSPACE otherwise (e.g. B * H_kv * N up to about 2^18
+ * (query, KV head) items at K_top = 8, g = 4). It calls no allocator. Every
+ * call on one device shares that array: calls that overlap on one device
+ * (concurrent streams or host threads) race and must be serialised by the
+ * caller; consecutive calls on one stream are safe (the array needs no
+ * clearing between calls).
+ */
+#define PISA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pisa_status pisa_route_prefill_noalloc(const pisa_pyramid* p, const void* Q, const void* K,
+                                       pisa_dtype dt, int64_t N, int32_t H_q, int32_t K_top,
+                                       int32_t causal, int32_t gqa_group, int32_t* idx,
+                                       float* score, void* stream);
+
+/*
  * Block scores (section 4.4 eq 33-34, appendix A.2). PISA scores a candidate
  * by the log-sum-exp of its m valid child logits z_1..z_m (eq 21). Expanding
  * that LSE about the mean zbar gives log m + zbar + Var(z) / 2 + ...;
