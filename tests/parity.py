@@ -85,13 +85,16 @@ def bsa_reach(opyr, Qi, b, t, K_top, causal=True):
 
 
 def compare(gpu_idx, gpu_score, orc, t, C, K_top, causal=True, band=1e-3, score_tol=1e-3, strict=1e-5,
-            M1=None, max_near_tie_frac=0.25, score_rtol=0.0, reach=None):
+            M1=None, max_near_tie_frac=0.25, score_rtol=0.0, reach=None, tie_tol=5e-5):
     """gpu_idx/gpu_score [n][H][K] numpy, orc = oracle.route(...) dict, t [n] positions.
 
     band and strict may be arrays broadcastable to [n][H] (per-item bands); scores must
     satisfy |gpu - oracle| <= score_tol + score_rtol * |oracle|. reach(k, h, target) -> eps
     gives, for items (t[k], head h) and GPU selections target [m][K], the smallest
-    tie-resolution cost that reproduces each one (required when any selection differs)."""
+    tie-resolution cost that reproduces each one (required when any selection differs).
+    Besides the band, that cost must stay within tie_tol (when given): scores that are
+    each within d of the oracle's can only swap candidates less than 2 d apart, and the
+    fp32 scores here are within 1e-5 of the fp64 ones."""
     n, H, _ = gpu_idx.shape
     oi, os_, gap = orc["idx"], orc["score"], orc["gap"]
     band = np.broadcast_to(band, (n, H))
@@ -117,6 +120,8 @@ def compare(gpu_idx, gpu_score, orc, t, C, K_top, causal=True, band=1e-3, score_
                                  "gpu %s oracle %s cost %s (nan: undecided)" % (
                                      t[k], h, band[k, h], gpu_idx[k, h], oi[k, h], eps[j]))
         max_eps = float(eps.max())
+        if tie_tol is not None:
+            assert max_eps <= tie_tol, "a tie resolution needs a swap of %g, more than fp32 rounding explains" % max_eps
     if gpu_score is not None:
         s_g = gpu_score[same]
         s_o = os_[same]
