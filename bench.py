@@ -42,12 +42,15 @@ from hierarchical_top_amd import pisa, synth, workcount  # noqa: E402
 METRIC = "routed queries/sec at 64K and 256K tokens (GQA prefill); decode route µs/step"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# v_exp_f32 lane results per second from the unit counts: 256 CUs x 4 SIMDs x 16 lanes per
+# clock at 2.4 GHz, issued at half rate (the rate the in-run exp loop measures on gfx950)
+PEAK_EXP_GPS = 256 * 4 * 16 * 2.4 / 2
 MODES = {"levels": pisa.LEVELS, "two_stage": pisa.TWO_STAGE, "fused": pisa.FUSED}
 STAGES_TWO = ["build", "upper", "cluster", "leaf", "final"]
 STAGES_FUSED = ["build", "route_fused"]
 ARMED = {"build": 1, "route_fused": 1, "leaf": 1, "upper": 8, "cluster": 8, "final": 8}
 # kernel (name fragment in a rocprofv3 trace) of each single-kernel stage
-STAGE_KERNEL = {"leaf": "leaf_kernel", "build": "build_l12_kernel", "route_fused": "route_query_kernel"}
+STAGE_KERNEL = {"leaf": "leaf_kernel", "build": "build_block_kernel", "route_fused": "route_query_kernel"}
 # kernels of the 64K attention workload whose HBM traffic the counters measure (bench.py --only attn_bwd)
 ATTN_KERNEL = {"attn_fwd": "attn_cl_kernel", "attn_bwd": "attn_bwd_kernel", "dq_combine": "dq_combine_kernel"}
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read and 1 GiB written
@@ -194,6 +197,74 @@ def roofline(stage, ms, w, traffic):
                 frac=ach / PEAK_BF16_TFLOPS, traffic=traffic, algorithmic=flops, ms_per_launch=ms)
 
 
+def leaf_roofs(roof, w, peaks):
+    """The leaf scoring against the roofs measured in the same run: its MFMA work against the
+    MFMA loop and against the MFMA rate of the 1:1 MFMA + exp mix (the leaf's own mix: per 16 x 64
+    logit tile 16 MFMAs and 16 wave-wide exponentials), and its exponentials (one per raw-key
+    logit of a scored leaf and head, section 3.2 eq 21) against the exp loop. The binding roof is
+    the slowest of the three floors."""
+    G = w.H_q // w.H_kv
+    rw = workcount.route_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.g, w.K_top)
+    s = roof["ms_per_launch"] * 1e-3
+    flops, exps = 2 * rw["leaf_mac"], rw["leaf_exp"]
+    floors = {"mfma": flops / (peaks["mfma_bf16_tflops"] * 1e12),
+              "exp": exps / (peaks["exp_gps"] * 1e9),
+              "mfma+exp": flops / (peaks["mix_mfma_tflops"] * 1e12)}
+    bind = max(floors, key=floors.get)
+    return dict(algorithmic_exp=exps, achieved_exp_gps=exps / s / 1e9,
+                exp_frac_of_derived_peak=exps / s / 1e9 / PEAK_EXP_GPS, derived_exp_peak_gps=PEAK_EXP_GPS,
+                measured_mfma_tflops=peaks["mfma_bf16_tflops"], frac_of_measured_mfma=roof["achieved"] / peaks["mfma_bf16_tflops"],
+                measured_mix_mfma_tflops=peaks["mix_mfma_tflops"],
+                frac_of_measured_mix=roof["achieved"] / peaks["mix_mfma_tflops"],
+                measured_exp_gps=peaks["exp_gps"], frac_of_measured_exp=exps / s / 1e9 / peaks["exp_gps"],
+                floors_ms={k: v * 1e3 for k, v in floors.items()}, binding_roof=bind,
+                time_over_binding_floor=s / floors[bind])
+
+
+PEAKS_LIB = ROOT / "hierarchical_top_amd" / "libpisa_peaks.so"
+
+
+def unit_peaks(reps: int = 5):
+    """The units the selection kernels are bound by, timed in this run (include/pisa_peaks.h):
+    v_exp_f32 throughput, bf16 MFMA 16x16x32 throughput, the two issued 1:1 from the same waves
+    (the mix of the leaf scoring: per 16 x 64 logit tile, 16 MFMAs and 16 wave-wide exponentials
+    per wave), and an HBM copy."""
+    import ctypes
+    L = ctypes.CDLL(str(PEAKS_LIB))
+    for f in ("pisa_peak_exp", "pisa_peak_mfma", "pisa_peak_mix"):
+        getattr(L, f).argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.pisa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    blocks, iters = 2048, 4096                      # 8 waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def run(f):
+        rc = f()
+        if rc != 0:
+            raise RuntimeError("peak kernel launch failed (%d)" % rc)
+
+    ms_exp = time_fn(lambda: run(lambda: L.pisa_peak_exp(out.data_ptr(), blocks, iters, st)), reps)
+    ms_mfma = time_fn(lambda: run(lambda: L.pisa_peak_mfma(out.data_ptr(), blocks, iters, st)), reps)
+    ms_mix = time_fn(lambda: run(lambda: L.pisa_peak_mix(out.data_ptr(), blocks, iters, st)), reps)
+    exps = blocks * 256 * iters * 8
+    mfmas = blocks * 4 * iters * 8
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ms_copy = time_fn(lambda: run(lambda: L.pisa_peak_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, st)), reps)
+    ok = bool(torch.equal(src, dst))
+    del src, dst, out
+    torch.cuda.empty_cache()
+    return dict(exp_gps=exps / (ms_exp * 1e-3) / 1e9,
+                mfma_bf16_tflops=mfmas * 16384 / (ms_mfma * 1e-3) / 1e12,
+                mix_mfma_tflops=mfmas * 16384 / (ms_mix * 1e-3) / 1e12,
+                mix_exp_gps=mfmas * 64 / (ms_mix * 1e-3) / 1e9,
+                mix_over_mfma_time=ms_mix / ms_mfma,
+                copy_gbs=2 * COPY_BYTES / (ms_copy * 1e-3) / 1e9, copy_verified=ok,
+                how="exp: 8 independent chains x <- 2^-x per thread; mfma: 8 independent accumulators per wave; "
+                    "mix: the two interleaved 1:1 in every wave; copy: 1 GiB read + 1 GiB written, 16-byte "
+                    "accesses; %d workgroups of 256 threads" % blocks)
+
+
 def copy_calibration():
     """A plain 1 GiB device-to-device copy, so that a counter run over this program
     also holds the counters of a transfer of known size."""
@@ -283,7 +354,9 @@ def cpu_baseline(P: Prefill, budget_s: float):
     qps = w.B * w.N / (t_build + t_route_full)
     # parity of the GPU selection on the sampled positions
     parity = selection_parity(opyr, Qs, t, gpu_idx[0][:, t].transpose(1, 0, 2), orc, w.K_top, threads)
-    res = dict(value=qps, unit="queries/s", cores=threads, kind="oracle",
+    # cores: the threads the oracle ran on; the host's own core count is stated beside it
+    res = dict(value=qps, unit="queries/s", cores=threads, threads=threads, host_cores=os.cpu_count(),
+               host_cores_available=len(os.sched_getaffinity(0)), kind="oracle",
                sample="full fp64 pyramid build (%.2f s) + routing of %d evenly spaced positions x %d KV heads "
                       "(%.2f s), extrapolated to all %d positions by the scored work (x%.1f)"
                       % (t_build, len(t), w.H_kv, dt, w.N, scale),
@@ -566,8 +639,13 @@ def main():
     roof_all = {s: {k: roofline(s, stages_ms[s], w, load_traffic(s, w.name))[k]
                     for k in ("bound", "achieved", "unit", "frac")} for s in stage_names}
 
+    # the units the leaf kernel is bound by, measured on this GPU in this run
+    peaks = unit_peaks()
+    log("unit peaks", peaks)
+    if dom == "leaf":
+        roof["measured_roofs"] = leaf_roofs(roof, w, peaks)
     extra = dict(headline_mode=mname, premeasure_ms=pre, stage_ms=stages_ms, stage_launches=launches,
-                 stage_roofline=roof_all)
+                 stage_roofline=roof_all, unit_peaks=peaks)
     for m, v in MODES.items():
         extra["route_ms_" + m] = time_fn(lambda: P.route_only(v), 5)
     extra["bsa_ms"] = time_fn(P.bsa, 3)

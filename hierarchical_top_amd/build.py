@@ -18,6 +18,9 @@ CSRC = PKG / "csrc"
 ROOT = PKG.parent
 OBJ = ROOT / "_build" / "pisa"
 LIB = PKG / "libpisa.so"
+# unit-throughput loops timed beside the selection kernels (include/pisa_peaks.h)
+PEAKS_SRC = PKG / "peaks" / "peaks.hip"
+PEAKS_LIB = PKG / "libpisa_peaks.so"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -44,7 +47,8 @@ def _compile(src: Path) -> Path:
 
 
 def build(jobs: int | None = None) -> Path:
-    """Compile every csrc/*.hip for gfx950 and link libpisa.so (always rebuilds)."""
+    """Compile every csrc/*.hip for gfx950 and link libpisa.so, then libpisa_peaks.so
+    (always rebuilds)."""
     OBJ.mkdir(parents=True, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -56,6 +60,12 @@ def build(jobs: int | None = None) -> Path:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link of libpisa.so failed")
     os.replace(tmp, LIB)
+    tmp = PEAKS_LIB.with_suffix(".so.tmp%d" % os.getpid())
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", str(PEAKS_SRC), "-o", str(tmp)], capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build of libpisa_peaks.so failed")
+    os.replace(tmp, PEAKS_LIB)
     return LIB
 
 
