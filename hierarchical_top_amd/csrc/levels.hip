@@ -631,7 +631,9 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         const bool reg_keys = leaf && dtype == 1 && (p.g == 2 || p.g == 4) && r.G <= 8;
         const bool reg_upper = !leaf && dtype == 1 && (p.g == 2 || p.g == 4) && r.G <= 8;
         const bool reg_rows = !leaf && !reg_upper && p.g * p.g <= 16;
-        const int qc = reg_rows ? kRegChunk : ((reg_keys || reg_upper) ? kLeafQC : 256);
+        // one wave per chunk when a sequence's query elements index in 31 bits (offsets are 32-bit)
+        const bool wave_upper = reg_upper && N * r.H_q * d < ((int64_t)1 << 31);
+        const int qc = reg_rows ? kRegChunk : (reg_keys ? kLeafQC : (wave_upper ? kWaveQC : (reg_upper ? kLeafQC : 256)));
         int32_t* counts = a.counts + a.cnt_off[l];
         int32_t* cursor = a.cursor + a.cnt_off[l];
 
@@ -685,7 +687,7 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         int64_t grid = ((int64_t)BH * N * r.K_top + qc - 1) / qc + n_clusters;  // bound on the chunks
         if (reg_rows) grid = (grid + kRegWaves - 1) / kRegWaves;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, false, s);
-        const int kind = reg_keys ? 3 : (reg_upper ? 4 : (leaf ? 1 : (reg_rows ? 2 : 0)));
+        const int kind = reg_keys ? 3 : (wave_upper ? 6 : (reg_upper ? 4 : (leaf ? 1 : (reg_rows ? 2 : 0))));
         if ((err = launch_score(sc2, dtype, d, kind, grid, s)) != hipSuccess) return err;
         stage_mark(leaf ? PISA_STAGE_LEAF : PISA_STAGE_UPPER, true, s);
 

@@ -27,6 +27,19 @@ template <int D, int SK>
 static hipError_t score_d(const ScoreArgs& a, int kind, int64_t grid, hipStream_t s)
 {
     if (kind == 2) return a.rc == 2 ? score_reg_launch<D, 2, SK>(a, grid, s) : score_reg_launch<D, 4, SK>(a, grid, s);
+    if (kind == 6) {  // upper levels, one wave per chunk with its own LDS ring: four chunks per workgroup
+        const size_t lds = 4 * wave_ring_bytes<D, kUpperWaveNB>();
+        const void* k = a.rc == 2 ? (const void*)upper_ring_kernel<D, 2, kUpperWaveNB, SK>
+                                  : (const void*)upper_ring_kernel<D, 4, kUpperWaveNB, SK>;
+        if (lds > 65536) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        ScoreArgs arg = a;
+        void* args[] = {&arg};
+        hipError_t e = hipLaunchKernel(k, dim3((unsigned)((grid + 3) / 4)), dim3(256), args, lds, s);
+        return e != hipSuccess ? e : hipGetLastError();
+    }
     if (kind == 3 || kind == 4) {  // queries streamed through LDS: leaf (keys) or upper (grandchildren)
         const size_t lds = stream_lds_bytes(D, kind == 3 ? kLeafNB : kUpperNB);
         const void* k;

@@ -891,4 +891,172 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void u
     stream_write_scores(L, a.u + bh * a.N * ucols, n, ucols, RC, ncand);
 }
 
+// Upper levels with g in {2, 4}, bf16 queries: one wave per chunk of at most kWaveQC
+// entries, so a small cluster costs one wave's start-up, which the other waves of the CU
+// overlap (clusters are small when the windows are L2-sized: a window's query rows then
+// stay in the XCD's L2 across the clusters that re-read them). The per-tile arithmetic is
+// upper_kernel's: P's g * g grandchild summaries as one 16-row A tile of two bf16 terms in
+// registers; a tile of 16 query columns (16 / G entries x G heads) on the MFMA; each lane
+// reduces whole candidates; heads summed with DPP. Query rows stream through a ring of NBW
+// tiles in the wave's own LDS (global_load_lds, 16-byte pieces XOR-swizzled by row as in
+// the shared ring), with exact vmcnt waits and no workgroup barrier. Lane j collects the
+// scores of entry j with permutes and writes them after the chunk (no LDS beyond the ring, so
+// five workgroups fit a CU).
+template <int D>
+struct WaveRing {
+    static constexpr int CH = D / 8;       // 16-byte pieces per row
+    static constexpr int RPI = 64 / CH;    // rows per fetch instruction
+    static constexpr int NIT = 16 / RPI;   // fetch instructions per 16-row tile
+};
+template <int D, int NBW>
+constexpr size_t wave_ring_bytes() { return (size_t)NBW * 16 * D * 2; }
+
+template <int D, int NB, int K = NB - 2>
+__device__ __forceinline__ void wave_ring_wait(int later)
+{
+    constexpr int NIT = WaveRing<D>::NIT;
+    static_assert(NB >= 2 && (NB - 2) * NIT < 64, "ring depth within the vmcnt range");
+    if constexpr (K <= 0) {
+        wait_vm<0>();
+    } else {
+        if (later >= K) {
+            wait_vm<K * NIT>();
+            return;
+        }
+        wave_ring_wait<D, NB, K - 1>(later);
+    }
+}
+
+template <int D, int RC, int NBW, int SK>
+__global__ __launch_bounds__(256) void upper_ring_kernel(ScoreArgs a)
+{
+    static_assert(RC == 2 || RC == 4, "g in {2, 4}");
+    static_assert(kWaveQC == 64, "one entry per lane");
+    using W = WaveRing<D>;
+    constexpr int KS = D / 32;
+    constexpr int CPL = 4 / RC;  // candidates per lane
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
+
+    const int64_t total = a.chunk_off[a.n_clusters];
+    const int64_t nblk = (total + 3) >> 2;
+    if ((int64_t)blockIdx.x >= nblk) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t chunk = (a.xcd ? xcd_chunk(blockIdx.x, nblk) : (int64_t)blockIdx.x) * 4 + wave;
+    if (chunk >= total) return;  // whole wave; nothing below synchronises across waves
+    bf16* ring = reinterpret_cast<bf16*>(s_raw + (size_t)wave * wave_ring_bytes<D, NBW>());
+    const int64_t cl = a.chunk_cl[chunk];
+    const int e0 = a.offsets[cl] + (int)(chunk - a.chunk_off[cl]) * a.qc;
+    const int n = min(a.offsets[cl + 1], e0 + a.qc) - e0;  // 1 <= n <= kWaveQC
+    const int64_t P = cl % a.M_bins;
+    const int64_t bh = (cl / a.M_bins) % a.BH;
+    const int h = (int)(bh % a.H);
+    const int b = (int)(bh / a.H);
+    const int lane = threadIdx.x & 63, lg = lane >> 4;
+    const int G = a.G, QT = 16 / G;
+    const int glog = __builtin_ctz(G);  // G is a power of two
+    const int ucols = a.K_top * RC;
+    const int ent = a.entries[e0 + min(lane, n - 1)];  // lane j: entry j (the last one past n)
+
+    // A operand: row (lane & 15) of P's grandchildren, k-chunk 8 * lg + 32 * s, as hi / lo bf16 terms
+    constexpr int nrows = RC * RC;
+    const int64_t row0 = P * nrows;
+    const int64_t rem = a.rows_limit - row0;
+    const int lim_rows = rem < nrows ? (int)rem : nrows;  // >= 1: P's first grandchild exists
+    bf16x8 ah[KS], al[KS];
+    {
+        const int r = lane & 15;
+        const bool ok = r < lim_rows;
+        const float* rp = reinterpret_cast<const float*>(a.rows) + (int64_t)b * a.rows_b_stride +
+                          (int64_t)h * a.rows_h_stride + (row0 + (ok ? r : 0)) * a.row_stride + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) Src<float>::load(rp + 32 * s, ok, ah[s], al[s]);
+    }
+    // the A rows are in flight ahead of the ring's first fetches: a wait for a tile (exact count
+    // of the fetches issued after it) also covers every older load
+
+    const bf16* Qb = reinterpret_cast<const bf16*>(a.Q) + (int64_t)b * a.N * a.H_q * D + (int64_t)h * G * D;
+    // element offset of this lane's entry's query row (below 2^31: N * H_q * D < 2^31 on this path)
+    const uint32_t qoff = ((uint32_t)ent >> 6) * (uint32_t)(a.H_q * D);
+    // this lane's part of fetch instruction i of a tile: tile row r = i * RPI + lane / CH holds
+    // entry r / G, head r % G; the lane stores piece (lane % CH) of that row's LDS copy, which
+    // holds piece (lane % CH) ^ (r % CH) of the global row. Per lane and instruction, the entry's
+    // place in the tile and the offset within its G rows are fixed: only the tile changes.
+    int rel[W::NIT], within[W::NIT];
+#pragma unroll
+    for (int i = 0; i < W::NIT; ++i) {
+        const int r = i * W::RPI + lane / W::CH;
+        rel[i] = r >> glog;
+        within[i] = (r & (G - 1)) * D + 8 * ((lane % W::CH) ^ (r & (W::CH - 1)));
+    }
+    auto fetch = [&](int t, int slot) {
+#pragma unroll
+        for (int i = 0; i < W::NIT; ++i) {
+            const int idx = min(t * QT + rel[i], n - 1);
+            const uint32_t off = (uint32_t)shfl((int)qoff, idx) + (uint32_t)within[i];
+            __builtin_amdgcn_global_load_lds(
+                Qb + off, (__attribute__((address_space(3))) void*)(ring + (slot * 16 + i * W::RPI) * D), 16, 0, 0);
+        }
+    };
+    const int ntiles = (n + QT - 1) / QT;
+#pragma unroll
+    for (int k = 0; k < NBW - 1; ++k)
+        if (k < ntiles) fetch(k, k);
+
+    const float scale = kLog2e * rsqrtf((float)D);
+    const int col = lane & 15;
+    const int qi = col / G, head = col % G;
+    int boff[KS];  // byte offset of this lane's B piece within a tile (swizzled as fetched)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) boff[s] = (col * D + 8 * ((4 * s + lg) ^ (col & (W::CH - 1)))) * 2;
+    const int ncand = (lim_rows + RC - 1) / RC;  // children of P that exist
+    float us[4] = {0.f, 0.f, 0.f, 0.f};          // scores of this lane's entry (lane j: entry j)
+
+    for (int t = 0; t < ntiles; ++t) {
+        wave_ring_wait<D, NBW>(min(NBW - 2, ntiles - 1 - t));
+        if (t + NBW - 1 < ntiles) {
+            // the slot of tile t - 1, whose reads have completed (their values fed its products)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            fetch(t + NBW - 1, (t + NBW - 1) % NBW);
+        }
+        const unsigned char* tb = reinterpret_cast<const unsigned char*>(ring + (t % NBW) * 16 * D);
+        bf16x8 B[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) B[s] = *reinterpret_cast<const bf16x8*>(tb + boff[s]);
+        f32x4 acc_h = f32x4{0.f, 0.f, 0.f, 0.f}, acc_l = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            acc_h = mfma(ah[s], B[s], acc_h);
+            acc_l = mfma(al[s], B[s], acc_l);
+        }
+        float z[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] = (acc_h[r] + acc_l[r]) * scale;
+        if (lim_rows < 16) {  // padding rows (g = 2), or a tail node with missing grandchildren
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * lg + r >= lim_rows) z[r] = -INFINITY;
+        }
+        float l2c[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int rfirst = 4 * lg + c * RC;
+            float l2 = block_score2<SK, RC, 0>(z + c * RC, rfirst < lim_rows);
+            l2c[c] = sum_adjacent(l2, G) * kLn2;
+        }
+        // candidate q of entry j = t * QT + i sits in lane (i * G, lane group 4 q / RC), slot q % CPL
+        const int i = lane - t * QT;  // this lane's entry within the tile, when 0 <= i < QT
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float v = shfl(l2c[q % CPL], (i & (QT - 1)) * G + 16 * ((q * RC) >> 2));
+            if (i >= 0 && i < QT) us[q] = v;
+        }
+    }
+    if (lane < n) {
+        float* up = a.u + bh * a.N * ucols + (uint64_t)((uint32_t)ent >> 6) * (uint32_t)ucols + (ent & 63) * RC;
+        if (RC == 4 && ncand == 4) *reinterpret_cast<f32x4*>(up) = f32x4{us[0], us[1], us[2], us[3]};
+        else
+            for (int q = 0; q < ncand; ++q) up[q] = us[q];
+    }
+}
+
 }  // namespace pisa

@@ -140,7 +140,7 @@ struct BsaArgs {
 // ring, and small windows leave many clusters far below 256 entries. Measured at 256K
 // (16 / 4 heads, d=128): leaf windows of 2^18 and level-2 windows of 2^14 beat 2^15 and
 // 2^13 by about 4 % each, with identical selections.
-inline int cluster_win_log2(int level) { return level == 1 ? 18 : (level == 2 ? 14 : 13); }
+inline int cluster_win_log2(int level) { return level == 1 ? 18 : 12; }
 
 // Level-synchronous routing: clustered scoring of one level.
 struct ScoreArgs {
@@ -201,6 +201,10 @@ constexpr int kLeafQC = 256;
 constexpr int kSubRows = 64;
 constexpr int kLeafNB = 2;
 constexpr int kUpperNB = 2;
+// Upper levels, one wave per chunk (upper_ring_kernel): chunks of kWaveQC entries, a ring of
+// kUpperWaveNB 16-row tiles per wave.
+constexpr int kWaveQC = 64;
+constexpr int kUpperWaveNB = 2;
 // LDS bytes of one such workgroup: the ring, the chunk's entries and its scores
 inline size_t stream_lds_bytes(int d, int nb) { return (size_t)nb * kSubRows * d * 2 + (size_t)kLeafQC * (4 + 16); }
 
