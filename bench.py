@@ -522,12 +522,12 @@ def attn_bwd_alone(reps: int = 10):
     return dict(attn_bwd_ms=ms, attn_bwd_tflops=2 * bw["mac"] / (ms * 1e-3) / 1e12)
 
 
-PAPER_SWEEP_N = (4096, 8192, 16384, 32768, 65536, 131072, 262144)
+PAPER_SWEEP_N = (4096, 8192, 16384, 32768, 65536, 131072, 262144, 1048576)
 
 
 def paper_sweep(check: bool, sizes=PAPER_SWEEP_N):
     """Build + route at the appendix's selection-benchmark shape (32 query / 2 KV heads,
-    d=64, C=64, g=2, K_top=8, random bf16 Q and K) for N = 4K .. 256K: every router, the
+    d=64, C=64, g=2, K_top=8, random bf16 Q and K) for N = 4K .. 256K and 1M: every router, the
     exhaustive BSA-style selector and the build alone, in ms. With check, the longest
     sequence's level-router selection is compared with the oracle on sampled positions."""
     out = {}
@@ -537,9 +537,10 @@ def paper_sweep(check: bool, sizes=PAPER_SWEEP_N):
         P = Prefill(w)
         r = {}
         for mname, mode in MODES.items():
-            r["build_route_ms_" + mname] = time_fn(lambda: P.step(mode), 10 if mname == "levels" else 3)
+            r["build_route_ms_" + mname] = time_fn(lambda: P.step(mode), 10 if mname == "levels" else 3,
+                                                   warm=2 if N < (1 << 20) else 1)
         r["build_ms"] = time_fn(lambda: P.pyr.build(P.K, N), 10)
-        r["bsa_ms"] = time_fn(P.bsa, 3)
+        r["bsa_ms"] = time_fn(P.bsa, 3, warm=2 if N < (1 << 20) else 1)
         best = min(r["build_route_ms_" + m] for m in MODES)
         r["routed_queries_per_s"] = N / (best * 1e-3)
         r["speedup_vs_bsa"] = (r["bsa_ms"] + r["build_ms"]) / best

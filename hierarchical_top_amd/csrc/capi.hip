@@ -106,8 +106,8 @@ pisa_status plan(pisa_pyramid* p, int32_t B, int32_t H, int32_t d, int32_t C, in
     return PISA_OK;
 }
 
-// Checks a caller-supplied descriptor against a fresh plan of its geometry.
-pisa_status check_pyramid(const pisa_pyramid* p)
+// Checks a caller-supplied descriptor's geometry against a fresh plan of it.
+pisa_status check_geometry(const pisa_pyramid* p)
 {
     if (!p) return fail(PISA_EINVAL, "pyramid descriptor is NULL");
     pisa_pyramid q;
@@ -116,6 +116,14 @@ pisa_status check_pyramid(const pisa_pyramid* p)
     if (q.L_cap != p->L_cap || q.floats != p->floats ||
         memcmp(q.M_cap, p->M_cap, sizeof(q.M_cap)) || memcmp(q.off, p->off, sizeof(q.off)))
         return fail(PISA_EINVAL, "pyramid descriptor was not produced by pisa_pyramid_plan");
+    return PISA_OK;
+}
+
+// ... and that it carries its summary buffer (every call that queues work).
+pisa_status check_pyramid(const pisa_pyramid* p)
+{
+    pisa_status s = check_geometry(p);
+    if (s != PISA_OK) return s;
     if (!p->buf || !aligned16(p->buf)) return fail(PISA_EINVAL, "pyramid buf is NULL or not 16-byte aligned");
     return PISA_OK;
 }
@@ -135,10 +143,10 @@ PyrArgs pyr_args(const pisa_pyramid* p)
     return a;
 }
 
-bool dtype_ok(pisa_dtype dt) { return dt == PISA_F32 || dt == PISA_BF16; }
+bool dtype_ok(int32_t dt) { return dt == PISA_F32 || dt == PISA_BF16; }
 
 // Routing arguments shared by prefill and decode.
-pisa_status check_route(const pisa_pyramid* p, pisa_dtype dt, int32_t H_q, int32_t K_top, int32_t gqa, int causal,
+pisa_status check_route(const pisa_pyramid* p, int32_t dt, int32_t H_q, int32_t K_top, int32_t gqa, int causal,
                         int64_t M1)
 {
     if (!dtype_ok(dt)) return fail(PISA_EINVAL, "dtype %d is not PISA_F32 or PISA_BF16", (int)dt);
@@ -298,7 +306,7 @@ pisa_status pisa_pyramid_plan(pisa_pyramid* p, int32_t B, int32_t H_kv, int32_t 
     return s == PISA_OK ? ok() : s;
 }
 
-pisa_status pisa_build_pyramid(const pisa_pyramid* p, const void* K, pisa_dtype dt, int64_t N, void* stream)
+pisa_status pisa_build_pyramid(const pisa_pyramid* p, const void* K, int32_t dt, int64_t N, void* stream)
 {
     pisa_status s = check_pyramid(p);
     if (s != PISA_OK) return s;
@@ -312,7 +320,7 @@ pisa_status pisa_build_pyramid(const pisa_pyramid* p, const void* K, pisa_dtype 
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_build_pyramid");
 }
 
-pisa_status pisa_pyramid_append(const pisa_pyramid* p, const void* K, pisa_dtype dt, const int64_t* seqlen,
+pisa_status pisa_pyramid_append(const pisa_pyramid* p, const void* K, int32_t dt, const int64_t* seqlen,
                                 void* stream)
 {
     pisa_status s = check_pyramid(p);
@@ -331,7 +339,7 @@ pisa_status pisa_route_prefill_workspace(const pisa_pyramid* p, int64_t N, int32
 {
     (void)H_q;
     if (!bytes) return fail(PISA_EINVAL, "NULL argument");
-    pisa_status s = check_pyramid(p);  /* the layouts divide by C and g and walk the levels */
+    pisa_status s = check_geometry(p);  /* the layouts divide by C and g and walk the levels */
     if (s != PISA_OK) return s;
     if (N < 1 || K_top < 1 || K_top > 64) return fail(PISA_EINVAL, "N or K_top out of range");
     if (N > p->N_cap) return fail(PISA_ENOSPACE, "N=%lld exceeds N_cap=%lld", (long long)N, (long long)p->N_cap);
@@ -343,7 +351,7 @@ pisa_status pisa_route_prefill_workspace(const pisa_pyramid* p, int64_t N, int32
     return ok();
 }
 
-pisa_status pisa_route_prefill_noalloc(const pisa_pyramid* p, const void* Q, const void* K, pisa_dtype dt,
+pisa_status pisa_route_prefill_noalloc(const pisa_pyramid* p, const void* Q, const void* K, int32_t dt,
                                        int64_t N, int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group,
                                        int32_t* idx, float* score, void* stream)
 {
@@ -376,7 +384,7 @@ pisa_status pisa_route_prefill_noalloc(const pisa_pyramid* p, const void* Q, con
                                      PISA_SCORE_LSE, idx, score, ws, kScratchBytes, stream);
 }
 
-pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void* K, pisa_dtype dt, int64_t N,
+pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void* K, int32_t dt, int64_t N,
                                int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group, int32_t mode,
                                int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream)
 {
@@ -384,7 +392,7 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
                                      ws, ws_bytes, stream);
 }
 
-pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, const void* K, pisa_dtype dt, int64_t N,
+pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, const void* K, int32_t dt, int64_t N,
                                       int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group, int32_t mode,
                                       int32_t score_kind, int32_t* idx, float* score, void* ws, size_t ws_bytes,
                                       void* stream)
@@ -496,14 +504,14 @@ pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, cons
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_route_prefill (two-stage)");
 }
 
-pisa_status pisa_route_decode(const pisa_pyramid* p, const void* q, const void* K, pisa_dtype dt,
+pisa_status pisa_route_decode(const pisa_pyramid* p, const void* q, const void* K, int32_t dt,
                               const int64_t* seqlen, int32_t H_q, int32_t K_top, int32_t gqa_group, int32_t* idx,
                               float* score, void* stream)
 {
     return pisa_route_decode_scored(p, q, K, dt, seqlen, H_q, K_top, gqa_group, PISA_SCORE_LSE, idx, score, stream);
 }
 
-pisa_status pisa_route_decode_scored(const pisa_pyramid* p, const void* q, const void* K, pisa_dtype dt,
+pisa_status pisa_route_decode_scored(const pisa_pyramid* p, const void* q, const void* K, int32_t dt,
                                      const int64_t* seqlen, int32_t H_q, int32_t K_top, int32_t gqa_group,
                                      int32_t score_kind, int32_t* idx, float* score, void* stream)
 {
@@ -528,7 +536,7 @@ pisa_status pisa_route_decode_scored(const pisa_pyramid* p, const void* q, const
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_route_decode");
 }
 
-pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_dtype dt, int32_t B, int64_t N_q,
+pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, int32_t dt, int32_t B, int64_t N_q,
                              int64_t N_kv, int64_t N_alloc, int32_t H_q, int32_t H_kv, int32_t d, int32_t C,
                              const int32_t* block_idx, int32_t K_top, int32_t causal, const int64_t* kv_len, void* O,
                              float* lse, void* stream)
@@ -581,7 +589,7 @@ pisa_status pisa_sparse_attn_workspace(int32_t B, int64_t N_q, int64_t N_alloc, 
     return ok();
 }
 
-pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void* V, pisa_dtype dt, int32_t B,
+pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void* V, int32_t dt, int32_t B,
                                        int64_t N_q, int64_t N_kv, int64_t N_alloc, int32_t H_q, int32_t H_kv,
                                        int32_t d, int32_t C, const int32_t* block_idx, int32_t K_top, int32_t causal,
                                        const int64_t* kv_len, void* O, float* lse, void* ws, size_t ws_bytes,
@@ -622,7 +630,7 @@ pisa_status pisa_sparse_attn_bwd_workspace(int32_t B, int64_t N_q, int64_t N_all
 }
 
 pisa_status pisa_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                                 const float* lse, pisa_dtype dt, int32_t B, int64_t N_q, int64_t N_kv,
+                                 const float* lse, int32_t dt, int32_t B, int64_t N_q, int64_t N_kv,
                                  int64_t N_alloc, int32_t H_q, int32_t H_kv, int32_t d, int32_t C,
                                  const int32_t* block_idx, int32_t K_top, int32_t causal, const int64_t* kv_len,
                                  float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes, void* stream)
@@ -671,7 +679,7 @@ pisa_status pisa_selection_quality_workspace(int32_t B, int64_t N, int32_t H_q, 
     return ok();
 }
 
-pisa_status pisa_selection_quality(const void* Q, const void* K, pisa_dtype dt, int32_t B, int64_t N, int32_t H_q,
+pisa_status pisa_selection_quality(const void* Q, const void* K, int32_t dt, int32_t B, int64_t N, int32_t H_q,
                                    int32_t H_kv, int32_t d, int32_t C, const int32_t* sel, int32_t K_top, float* mass,
                                    int32_t* ref, float* recall, float* captured, float* ratio, void* ws,
                                    size_t ws_bytes, void* stream)
@@ -701,7 +709,7 @@ pisa_status pisa_selection_quality(const void* Q, const void* K, pisa_dtype dt, 
     return e == hipSuccess ? ok() : hip_fail(e, "pisa_selection_quality");
 }
 
-pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt, int64_t N, int32_t H_q,
+pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, int32_t dt, int64_t N, int32_t H_q,
                             int32_t K_top, int32_t causal, int32_t gqa_group, int32_t* idx, float* score,
                             void* stream)
 {

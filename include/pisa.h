@@ -52,6 +52,8 @@ typedef enum pisa_status {
     PISA_EHIP = -4           /* the HIP runtime reported an error while queueing */
 } pisa_status;
 
+/* Element types. Calls take a dtype as int32_t holding one of these values (any other
+ * value is rejected with PISA_EINVAL), so that no caller can pass an out-of-range enum. */
 typedef enum pisa_dtype { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
 
 typedef enum pisa_route_mode {
@@ -101,7 +103,7 @@ pisa_status pisa_pyramid_plan(pisa_pyramid* p, int32_t B, int32_t H_kv, int32_t 
  * 1..L(N) of p->buf. Summaries are fp32 sums in token (or child) order
  * divided by the count. Errors: PISA_EINVAL (null pointers, N < 1),
  * PISA_ENOSPACE (N > N_cap). */
-pisa_status pisa_build_pyramid(const pisa_pyramid* p, const void* K, pisa_dtype dt, int64_t N,
+pisa_status pisa_build_pyramid(const pisa_pyramid* p, const void* K, int32_t dt, int64_t N,
                                void* stream);
 
 /* Decode cache update (section 3.3, "Decoding": only the current leaf mean and
@@ -113,7 +115,7 @@ pisa_status pisa_build_pyramid(const pisa_pyramid* p, const void* K, pisa_dtype 
  * ancestors up to level L(seqlen[b]) in the same order as
  * pisa_build_pyramid, so the result is bit-identical to a rebuild.
  * The previous lengths must have been built or appended one token at a time. */
-pisa_status pisa_pyramid_append(const pisa_pyramid* p, const void* K, pisa_dtype dt,
+pisa_status pisa_pyramid_append(const pisa_pyramid* p, const void* K, int32_t dt,
                                 const int64_t* seqlen, void* stream);
 
 /* Workspace bytes pisa_route_prefill needs for these arguments (0 for
@@ -145,7 +147,7 @@ pisa_status pisa_route_prefill_workspace(const pisa_pyramid* p, int64_t N, int32
  * workspace is too small), PISA_EHIP.
  */
 pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void* K,
-                               pisa_dtype dt, int64_t N, int32_t H_q, int32_t K_top,
+                               int32_t dt, int64_t N, int32_t H_q, int32_t K_top,
                                int32_t causal, int32_t gqa_group, int32_t mode, int32_t* idx,
                                float* score, void* ws, size_t ws_bytes, void* stream);
 
@@ -166,7 +168,7 @@ pisa_status pisa_route_prefill(const pisa_pyramid* p, const void* Q, const void*
  */
 #define PISA_NOALLOC_SCRATCH_BYTES (64u << 20)
 pisa_status pisa_route_prefill_noalloc(const pisa_pyramid* p, const void* Q, const void* K,
-                                       pisa_dtype dt, int64_t N, int32_t H_q, int32_t K_top,
+                                       int32_t dt, int64_t N, int32_t H_q, int32_t K_top,
                                        int32_t causal, int32_t gqa_group, int32_t* idx,
                                        float* score, void* stream);
 
@@ -195,7 +197,7 @@ typedef enum pisa_score_kind {
  * (PISA_EUNSUPPORTED for PISA_ROUTE_TWO_STAGE); an unknown score_kind is
  * PISA_EINVAL. Everything else as in pisa_route_prefill. */
 pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, const void* K,
-                                      pisa_dtype dt, int64_t N, int32_t H_q, int32_t K_top,
+                                      int32_t dt, int64_t N, int32_t H_q, int32_t K_top,
                                       int32_t causal, int32_t gqa_group, int32_t mode,
                                       int32_t score_kind, int32_t* idx, float* score, void* ws,
                                       size_t ws_bytes, void* stream);
@@ -209,14 +211,14 @@ pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, cons
  * idx: device int32 [B][H_kv][K_top]; score: device float32 [B][H_kv][K_top] or NULL.
  */
 pisa_status pisa_route_decode(const pisa_pyramid* p, const void* q, const void* K,
-                              pisa_dtype dt, const int64_t* seqlen, int32_t H_q, int32_t K_top,
+                              int32_t dt, const int64_t* seqlen, int32_t H_q, int32_t K_top,
                               int32_t gqa_group, int32_t* idx, float* score, void* stream);
 
 /* pisa_route_decode with the block score chosen by score_kind (a
  * pisa_score_kind, section 4.4); pisa_route_decode is this call with
  * PISA_SCORE_LSE. An unknown score_kind is PISA_EINVAL. */
 pisa_status pisa_route_decode_scored(const pisa_pyramid* p, const void* q, const void* K,
-                                     pisa_dtype dt, const int64_t* seqlen, int32_t H_q,
+                                     int32_t dt, const int64_t* seqlen, int32_t H_q,
                                      int32_t K_top, int32_t gqa_group, int32_t score_kind,
                                      int32_t* idx, float* score, void* stream);
 
@@ -233,7 +235,7 @@ pisa_status pisa_route_decode_scored(const pisa_pyramid* p, const void* q, const
  * A row with no visible key gets O = 0 and lse = -inf.
  * fp32 softmax statistics and accumulation.
  */
-pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_dtype dt,
+pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, int32_t dt,
                              int32_t B, int64_t N_q, int64_t N_kv, int64_t N_alloc, int32_t H_q,
                              int32_t H_kv, int32_t d, int32_t C, const int32_t* block_idx,
                              int32_t K_top, int32_t causal, const int64_t* kv_len, void* O,
@@ -257,7 +259,7 @@ pisa_status pisa_sparse_attn(const void* Q, const void* K, const void* V, pisa_d
  */
 pisa_status pisa_sparse_attn_workspace(int32_t B, int64_t N_q, int64_t N_alloc, int32_t H_q, int32_t H_kv,
                                        int32_t d, int32_t C, int32_t K_top, size_t* bytes);
-pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void* V, pisa_dtype dt,
+pisa_status pisa_sparse_attn_clustered(const void* Q, const void* K, const void* V, int32_t dt,
                                        int32_t B, int64_t N_q, int64_t N_kv, int64_t N_alloc, int32_t H_q,
                                        int32_t H_kv, int32_t d, int32_t C, const int32_t* block_idx,
                                        int32_t K_top, int32_t causal, const int64_t* kv_len, void* O,
@@ -291,7 +293,7 @@ pisa_status pisa_sparse_attn_bwd_workspace(int32_t B, int64_t N_q, int64_t N_all
                                            int32_t H_kv, int32_t d, int32_t C, int32_t K_top,
                                            size_t* bytes);
 pisa_status pisa_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
-                                 const void* dO, const float* lse, pisa_dtype dt, int32_t B,
+                                 const void* dO, const float* lse, int32_t dt, int32_t B,
                                  int64_t N_q, int64_t N_kv, int64_t N_alloc, int32_t H_q,
                                  int32_t H_kv, int32_t d, int32_t C, const int32_t* block_idx,
                                  int32_t K_top, int32_t causal, const int64_t* kv_len, float* dQ,
@@ -310,7 +312,7 @@ pisa_status pisa_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
  * kept without a score). The pyramid must hold a build over N.
  * Supported: K_top <= 8. Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE.
  */
-pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt, int64_t N,
+pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, int32_t dt, int64_t N,
                             int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group,
                             int32_t* idx, float* score, void* stream);
 
@@ -340,7 +342,7 @@ pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, pisa_dtype dt,
  */
 pisa_status pisa_selection_quality_workspace(int32_t B, int64_t N, int32_t H_q, int32_t C,
                                              size_t* bytes);
-pisa_status pisa_selection_quality(const void* Q, const void* K, pisa_dtype dt, int32_t B,
+pisa_status pisa_selection_quality(const void* Q, const void* K, int32_t dt, int32_t B,
                                    int64_t N, int32_t H_q, int32_t H_kv, int32_t d, int32_t C,
                                    const int32_t* sel, int32_t K_top, float* mass, int32_t* ref,
                                    float* recall, float* captured, float* ratio, void* ws,

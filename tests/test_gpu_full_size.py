@@ -4,7 +4,8 @@ the benchmark times (pyramid build, then the level-synchronous router over every
 position), checked on sampled outputs the oracle computes one by one: every level's
 summaries on sampled nodes, the selections and scores of sampled positions for the three
 block scores (LSE, PISA-1, PISA-2), the exhaustive selector on sampled positions, and the
-level router across a leaf-level clustering window (two sequences of 2^18 + 3001 tokens)."""
+level router across a leaf-level clustering window (two sequences of 2^18 + 3001 tokens), and
+the page's benchmark shape at 2^20 tokens (level router and exhaustive selector, sampled)."""
 import numpy as np
 import pytest
 import torch
@@ -102,3 +103,37 @@ def test_level_router_across_leaf_windows():
         gs = score[b][:, t].cpu().numpy().transpose(1, 0, 2)
         print("b", b, compare(gi, gs, orc, t, w.C, w.K_top, max_near_tie_frac=0.6,
                               reach=route_reach(opyr, Q[b, t].float().numpy(), b, t, w.K_top)))
+
+
+def test_paper_shape_1m_sampled():
+    """The page's selection-benchmark shape (32 query / 2 KV heads, d=64, C=64, g=2, K_top=8,
+    random bf16 Q and K) at 1,048,576 tokens, in the benchmark's launch configuration: the
+    level router and the exhaustive selector on sampled positions against the oracle."""
+    w = synth.paper_shape(1 << 20)
+    Q, K, _, _ = synth.make_prefill(w)
+    t = np.unique(np.concatenate([np.linspace(0, w.N - 1, 240).astype(np.int64), np.arange(2 * w.C),
+                                  np.arange(w.N - w.C, w.N)]))
+    print("positions", len(t), flush=True)
+    Qd, Kd = Q.cuda(), K.cuda()
+    pyr = pisa.Pyramid(w.B, w.H_kv, w.d, w.C, w.g, w.N)
+    pyr.build(Kd, w.N)
+    idx, score = pisa.route_prefill(pyr, Qd, Kd, w.N, w.K_top, mode=pisa.LEVELS, with_score=True)
+    bidx, bscore = pisa.bsa_select(pyr, Qd, w.N, w.K_top, with_score=True)
+    torch.cuda.synchronize()
+    opyr = oracle.Pyramid(K.float().numpy(), w.N, w.C, w.g)
+    Qs = Q[0, t].float().numpy()
+    orc = oracle.route(opyr, Qs, [0] * len(t), t, w.K_top)
+    gi = idx[0][:, t].cpu().numpy().transpose(1, 0, 2)
+    gs = score[0][:, t].cpu().numpy().transpose(1, 0, 2)
+    print("levels", compare(gi, gs, orc, t, w.C, w.K_top, max_near_tie_frac=0.6,
+                            reach=route_reach(opyr, Qs, 0, t, w.K_top)))
+    ts = t[::3]
+    ob = oracle.bsa(opyr, Q[0, ts].float().numpy(), [0] * len(ts), ts, w.K_top)
+    s = ob["score"]
+    fin = np.where(np.isfinite(s), s, np.nan)
+    ukth = np.nan_to_num(np.nanmin(fin, axis=-1), nan=1.0)
+    band = 1e-4 * np.abs(ukth) + 1e-9
+    print("bsa", compare(bidx[0][:, ts].cpu().numpy().transpose(1, 0, 2),
+                         bscore[0][:, ts].cpu().numpy().transpose(1, 0, 2), ob, ts, w.C, w.K_top, band=band,
+                         strict=band / 10, score_tol=1e-7, score_rtol=1e-4,
+                         reach=bsa_reach(opyr, Q[0, ts].float().numpy(), 0, ts, w.K_top)))
