@@ -22,7 +22,6 @@ namespace pisa {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelItemsPerThread = 1;
-constexpr int kLdsBins = 8192;  // cluster bins aggregated in LDS (larger levels use global atomics)
 
 // Eligible existing children of node P of level lp at level lp - 1, for query t.
 __device__ __forceinline__ int64_t n_children(int64_t P, int g, int64_t M_child, int64_t elig_max_child)
@@ -323,21 +322,6 @@ struct ScatterLvArgs {
     int32_t* entries;
 };
 
-// Adds v to an LDS counter and returns the old value, with one atomic per wave
-// when every active lane targets the same counter.
-__device__ __forceinline__ int lds_add(int* p_mine, int P, int* base_arr)
-{
-    const uint64_t act = ballot(true);
-    const int P0 = __builtin_amdgcn_readfirstlane(P);
-    if (ballot(P == P0) == act) {
-        const int leader = __builtin_ctzll(act);
-        int old = 0;
-        if (lane_id() == leader) old = atomicAdd(&base_arr[P0], __popcll(act));
-        old = __shfl(old, leader, 64);
-        return old + rank_below(act);
-    }
-    return atomicAdd(p_mine, 1);
-}
 
 __global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a)
 {

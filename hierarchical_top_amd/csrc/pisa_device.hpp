@@ -166,6 +166,23 @@ __device__ __forceinline__ float max_xor32(float v)
     return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 // Sum over aligned groups of G adjacent lanes (G a power of two <= 16).
+// Adds one to the LDS counter p_mine (= base_arr + P) and returns its old value, with one
+// atomic per wave when every active lane targets the same counter (the lanes then take
+// consecutive values in lane order).
+__device__ __forceinline__ int lds_add(int* p_mine, int P, int* base_arr)
+{
+    const uint64_t act = ballot(true);
+    const int P0 = __builtin_amdgcn_readfirstlane(P);
+    if (ballot(P == P0) == act) {
+        const int leader = __builtin_ctzll(act);
+        int old = 0;
+        if (lane_id() == leader) old = atomicAdd(&base_arr[P0], __popcll(act));
+        old = __shfl(old, leader, 64);
+        return old + rank_below(act);
+    }
+    return atomicAdd(p_mine, 1);
+}
+
 __device__ __forceinline__ float sum_adjacent(float v, int G)
 {
     if (G >= 2) v += dpp_xor1(v);

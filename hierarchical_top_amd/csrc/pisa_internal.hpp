@@ -199,6 +199,8 @@ constexpr int kRegWaves = 4;
 // buffers kSubRows rows at a time, kLeafNB / kUpperNB buffers deep.
 constexpr int kLeafQC = 256;
 constexpr int kSubRows = 64;
+// cluster counters aggregated per workgroup in LDS up to this many bins (else global atomics)
+constexpr int kLdsBins = 8192;
 constexpr int kLeafNB = 2;
 constexpr int kUpperNB = 2;
 // Upper levels, one wave per chunk (upper_ring_kernel): chunks of kWaveQC entries, a ring of

@@ -59,20 +59,50 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 
 // Cluster membership: every (query, kept level-2 node) pair that has a leaf
 // to score is appended to its node's cluster as (t << 6) | slot. The order
-// inside a cluster does not affect any result.
+// inside a cluster does not affect any result. Block (tile of 256 positions,
+// sequence x KV head): the pairs are counted per node in LDS, each node's range
+// is reserved with one global atomic per block, and positions inside it are
+// handed out from LDS (nodes shared by every query -- the first block's and the
+// current path's ancestors -- would otherwise take one global atomic per query).
 __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)a.B * a.H * a.N) return;
-    const int64_t meta = a.meta[i];
-    if (!(meta & 1)) return;
-    const uint64_t mask = (uint64_t)meta >> 1;
-    const int64_t t = i % a.N, bh = i / a.N;
-    for (int k = 0; k < a.K_top; ++k) {
-        if (!((mask >> k) & 1)) continue;
-        const int64_t cl = bh * a.M2 + a.kept2[i * a.K_top + k];
-        const int pos = atomicAdd(&a.cursor[cl], 1);
-        a.entries[a.offsets[cl] + pos] = (int32_t)((t << 6) | k);
+    extern __shared__ int s_mem[];
+    const int64_t bh = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = t < a.N;
+    const int64_t i = bh * a.N + (live ? t : 0);
+    const int64_t meta = live ? a.meta[i] : 0;
+    const uint64_t mask = (meta & 1) ? (uint64_t)meta >> 1 : 0;
+    const int32_t* base_off = a.offsets + bh * a.M2;
+    int32_t* cur = a.cursor + bh * a.M2;
+    if (a.M2 <= kLdsBins) {
+        int* s_cnt = s_mem;
+        int* s_pos = s_mem + a.M2;
+        for (int64_t k = threadIdx.x; k < a.M2; k += 256) s_cnt[k] = 0;
+        __syncthreads();
+        for (int k = 0; k < a.K_top; ++k)
+            if ((mask >> k) & 1) {
+                const int P = a.kept2[i * a.K_top + k];
+                lds_add(&s_cnt[P], P, s_cnt);
+            }
+        __syncthreads();
+        for (int64_t k = threadIdx.x; k < a.M2; k += 256) {
+            const int v = s_cnt[k];
+            s_pos[k] = v ? base_off[k] + atomicAdd(&cur[k], v) : 0;
+        }
+        __syncthreads();
+        for (int k = 0; k < a.K_top; ++k)
+            if ((mask >> k) & 1) {
+                const int P = a.kept2[i * a.K_top + k];
+                const int pos = lds_add(&s_pos[P], P, s_pos);
+                a.entries[pos] = (int32_t)((t << 6) | k);
+            }
+    } else {
+        for (int k = 0; k < a.K_top; ++k) {
+            if (!((mask >> k) & 1)) continue;
+            const int P = a.kept2[i * a.K_top + k];
+            a.entries[base_off[P] + atomicAdd(&cur[P], 1)] = (int32_t)((t << 6) | k);
+        }
     }
 }
 
@@ -180,7 +210,11 @@ hipError_t launch_two_stage(const RouteArgs& r, const Stage2Args& s2, const Fina
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t items = (int64_t)f.B * f.H * f.N;
     const unsigned gi = (unsigned)((items + 255) / 256);
-    hipLaunchKernelGGL(scatter_kernel, dim3(gi), dim3(256), 0, s, sc);
+    {
+        const dim3 grid((unsigned)((f.N + 255) / 256), (unsigned)(f.B * f.H));
+        const size_t lds = sc.M2 <= kLdsBins ? (size_t)2 * sc.M2 * 4 : 0;
+        hipLaunchKernelGGL(scatter_kernel, grid, dim3(256), lds, s, sc);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     stage_mark(PISA_STAGE_CLUSTER, true, s);
     const int64_t max_chunks = (items * f.K_top + kChunkQ - 1) / kChunkQ + s2.n_clusters;
