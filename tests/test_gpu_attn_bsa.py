@@ -88,6 +88,28 @@ def test_sparse_attention_matches_oracle(case, causal, sample, dense, entry):
         np.testing.assert_allclose(gl, want["lse"], atol=1e-3 if w.dtype == "bf16" else 1e-4)
 
 
+def test_clustered_attention_every_row_64k():
+    """The 64K workload (32 query / 8 KV heads, d=128, C=64, K_top=8) with EVERY row selecting
+    blocks -- a structured random causal selection (first, previous and current block plus one
+    block from each of five strata of the older ones), drawn without scores -- so that every
+    block's cluster spans many chunks, as in the benchmark. Sampled rows against the oracle."""
+    w = W["p64k"]
+    Q, K, V, _ = synth.make_prefill(w)
+    sel_all = synth.random_selection(61, w.B, w.H_kv, w.N, w.K_top, w.C, [w.N], causal=True)
+    t = _positions(w, 900)
+    print("rows", w.N, "sampled", len(t), flush=True)
+    O, lse = pisa.sparse_attn_clustered(Q.cuda(), K.cuda(), V.cuda(), torch.from_numpy(sel_all).cuda(), w.C, w.N,
+                                        with_lse=True)
+    torch.cuda.synchronize()
+    sel = np.ascontiguousarray(sel_all[0][:, t].transpose(1, 0, 2))  # [n][H][K]
+    want = oracle.sparse_attn(Q[0, t].float().numpy(), [0] * len(t), t, K.float().numpy(), V.float().numpy(), w.N,
+                              w.C, sel)
+    err = np.abs(O[0, t].float().cpu().numpy() - want["out"]).max()
+    print("max |O - oracle|", err)
+    assert err <= ATOL["bf16"], err
+    np.testing.assert_allclose(lse[0][:, t].t().cpu().numpy(), want["lse"], atol=1e-3)
+
+
 @pytest.mark.parametrize("entry", ["rows", "clustered"])
 def test_attention_decode_rows_and_empty_rows(entry):
     """N_q = 1 with per-sequence lengths (decode shape); a row whose blocks are all
