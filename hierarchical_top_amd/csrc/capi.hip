@@ -183,7 +183,7 @@ int levels_top(int64_t N, int C, int g, int K_top)
 }
 
 struct LevelsLayout {
-    size_t kept0, kept1, flags, u, counts, offsets, chunk_off, chunk_cl, block_sums, entries, total;
+    size_t kept0, kept1, flags, u, u_pair, counts, offsets, chunk_off, chunk_cl, block_sums, entries, total;
     int64_t cnt_total, max_clusters;
     int64_t cnt_off[PISA_MAX_LEVELS + 2];
     int l_top;
@@ -212,6 +212,9 @@ LevelsLayout levels_layout(const pisa_pyramid* p, int64_t N, int K_top)
     w.kept1 = o; o = al(o + (size_t)items * K_top * 4);
     w.flags = o; o = al(o + (size_t)items * 8);
     w.u = o; o = al(o + (size_t)items * p->g * K_top * 4);
+    // by-node scores of the second level of a dense pair (pisa::dense_pair)
+    const int c_log2 = log2_exact(p->C), g_log2 = log2_exact(p->g);
+    w.u_pair = o; o = al(o + (size_t)items * pisa::dense_pair_max_cols(N, c_log2, g_log2, w.l_top) * 4);
     w.counts = o; o = al(o + (size_t)2 * c * 4);  // counts, then cursors (cleared together)
     w.offsets = o; o = al(o + (size_t)(w.max_clusters + 1) * 4);
     w.chunk_off = o; o = al(o + (size_t)(w.max_clusters + 1) * 4);
@@ -452,6 +455,7 @@ pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, cons
         la.kept[1] = (int32_t*)(base + w.kept1);
         la.flags = (int64_t*)(base + w.flags);
         la.u = (float*)(base + w.u);
+        la.u_pair = (float*)(base + w.u_pair);
         la.counts = (int32_t*)(base + w.counts);
         la.cursor = la.counts + w.cnt_total;
         la.cnt_total = w.cnt_total;

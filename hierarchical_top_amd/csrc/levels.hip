@@ -143,7 +143,20 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
         if constexpr (GB > 0) {
             // the whole score row in registers: K * g floats, 16-byte loads when aligned
             float ur[KMAX * GB];
-            if (((K * GB) & 3) == 0) {
+            if (a.u_cols) {  // scores by node id (second level of a dense pair): the children of kin[s]
+                const float* un = a.u + i * a.u_cols;
+#pragma unroll
+                for (int s = 0; s < KMAX; ++s) {
+                    const int x = kin[s] < 0 ? 0 : kin[s];  // unused when kin[s] < 0
+                    if constexpr (GB == 4) {
+                        const f32x4 x4 = *reinterpret_cast<const f32x4*>(un + 4 * x);
+                        ur[4 * s] = x4[0]; ur[4 * s + 1] = x4[1]; ur[4 * s + 2] = x4[2]; ur[4 * s + 3] = x4[3];
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < GB; ++j) ur[s * GB + j] = un[GB * x + j];
+                    }
+                }
+            } else if (((K * GB) & 3) == 0) {
 #pragma unroll
                 for (int v = 0; v < KMAX * GB / 4; ++v) {
                     if (4 * v < K * GB) {
@@ -565,11 +578,29 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
 
     const int64_t per_blk = (int64_t)kSelThreads * kSelItemsPerThread;
     // levels scored densely (see kDenseParents / kDenseRows)
-    auto dense_level = [&](int l) {
-        return l >= 2 && (p.g == 2 || p.g == 4) && nodes_n(N, p.c_log2, p.g_log2, l + 1) <= kDenseParents &&
-               nodes_n(N, p.c_log2, p.g_log2, l - 1) <= kDenseRows;
-    };
+    auto dense_level = [&](int l) { return pisa::dense_level(N, p.c_log2, p.g_log2, l); };
+    bool paired = false;  // this level's scores were written by the level above's dense pass
     for (int l = a.l_top; l >= 1; --l) {
+        if (paired) {
+            // second level of a dense pair: its scores are in u_pair by node id
+            paired = false;
+            stage_mark(PISA_STAGE_FINAL, false, s);
+            sa.level = l;
+            sa.init = 0;
+            sa.kept_in = a.kept[cur];
+            sa.u = a.u_pair;
+            sa.u_cols = dense_pair_cols(N, p.c_log2, p.g_log2, l + 1);
+            sa.kept_out = a.kept[cur ^ 1];
+            sa.flags_out = a.flags;
+            sa.M_bins = nodes_n(N, p.c_log2, p.g_log2, l);
+            sa.counts = (l > 1 && !dense_level(l - 1)) ? a.counts + a.cnt_off[l - 1] : nullptr;
+            sa.win_log2 = l > 1 ? cluster_win_log2(l - 1) : 0;
+            if ((err = launch_select(sa, r.K_top, s)) != hipSuccess) return err;
+            sa.u_cols = 0;
+            stage_mark(PISA_STAGE_FINAL, true, s);
+            cur ^= 1;
+            continue;
+        }
         if (dense_level(l)) {
             DenseArgs da;
             memset(&da, 0, sizeof(da));
@@ -584,6 +615,18 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
             da.kept = a.kept[cur];
             da.sk = r.score_kind;
             da.u = a.u;
+            if (dense_pair(N, p.c_log2, p.g_log2, l)) {
+                // level l - 1 rides along: rows of level l - 2, parents = level-l nodes
+                da.rows2 = p.buf + p.off[l - 2];
+                da.rows2_b_stride = (int64_t)p.H * p.M_cap[l - 2] * d;
+                da.rows2_h_stride = p.M_cap[l - 2] * d;
+                da.rows2_limit = nodes_n(N, p.c_log2, p.g_log2, l - 2);
+                da.par2_span_log2 = p.c_log2 + (l - 1) * p.g_log2;
+                da.M_par2 = nodes_n(N, p.c_log2, p.g_log2, l);
+                da.u2 = a.u_pair;
+                da.u2_cols = dense_pair_cols(N, p.c_log2, p.g_log2, l);
+                paired = true;
+            }
             stage_mark(PISA_STAGE_UPPER, false, s);
             if ((err = launch_dense(da, dtype, d, s)) != hipSuccess) return err;
             stage_mark(PISA_STAGE_UPPER, true, s);

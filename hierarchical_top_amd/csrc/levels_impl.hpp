@@ -504,7 +504,10 @@ __global__ __launch_bounds__(64 * kRegWaves) void score_reg_kernel(ScoreArgs a)
 // nodes) stream through LDS in batches of 4 row tiles as two bf16 terms; a row
 // tile holds 16 / g^2 parents whose g children are the candidates. A per-query
 // table maps each parent to its slot in the query's kept list (0xFF = not
-// kept); only kept parents' candidates are written to u.
+// kept); only kept parents' candidates are written to u. With rows2 set, the
+// workgroup then scores level l - 1 from the query tiles it already holds: the
+// children of every eligible level-l node, written to u2 by node id (the kept
+// level-l nodes are chosen after this kernel).
 constexpr int kDenseBatch = 4;
 constexpr int kDenseQW = 64;  // queries per workgroup (at most)
 
@@ -567,61 +570,79 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
         }
     }
 
-    const int nrows = npar * RP;
-    const int nrt = (nrows + 15) / 16;
-    const float* rb = a.rows + (int64_t)b * a.rows_b_stride + (int64_t)h * a.rows_h_stride;
-    for (int kb = 0; kb < nrt; kb += kDenseBatch) {
-        __syncthreads();  // the previous batch is consumed (first pass: the slot table is written)
-        for (int i = threadIdx.x; i < kDenseBatch * 16 * (D / 8); i += 256) {
-            const int r = i / (D / 8), c8 = i % (D / 8);
-            const int64_t row = (int64_t)kb * 16 + r;
-            const bool ok = row < nrows && row < a.rows_limit;
-            bf16x8 vh, vl;
-            Src<float>::load(rb + (ok ? row : 0) * D + 8 * c8, ok, vh, vl);
-            *reinterpret_cast<bf16x8*>(s_rows + r * LDW + 8 * c8) = vh;
-            *reinterpret_cast<bf16x8*>(s_rows + (kDenseBatch * 16 + r) * LDW + 8 * c8) = vl;
-        }
-        __syncthreads();
-        const int kend = kb + kDenseBatch < nrt ? kb + kDenseBatch : nrt;
-        for (int k = kb; k < kend; ++k) {
-            const int rl = (k - kb) * 16 + (lane & 15);
-            bf16x8 ah[KS], al[KS];
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                ah[s] = *reinterpret_cast<const bf16x8*>(s_rows + rl * LDW + 32 * s + 8 * lg);
-                al[s] = *reinterpret_cast<const bf16x8*>(s_rows + (kDenseBatch * 16 + rl) * LDW + 32 * s + 8 * lg);
+    // one level: rows (level l-1 summaries of the np eligible parents, rows_limit of them exist)
+    // stream through LDS; write(ct, P, j, score, exists) stores candidate j of parent P for the
+    // queries of column tile ct
+    auto pass = [&](const float* rb, int64_t rows_limit, int np, auto write) {
+        const int nrows = np * RP;
+        const int nrt = (nrows + 15) / 16;
+        for (int kb = 0; kb < nrt; kb += kDenseBatch) {
+            __syncthreads();  // the previous batch is consumed (first pass: the slot table is written)
+            for (int i = threadIdx.x; i < kDenseBatch * 16 * (D / 8); i += 256) {
+                const int r = i / (D / 8), c8 = i % (D / 8);
+                const int64_t row = (int64_t)kb * 16 + r;
+                const bool ok = row < nrows && row < rows_limit;
+                bf16x8 vh, vl;
+                Src<float>::load(rb + (ok ? row : 0) * D + 8 * c8, ok, vh, vl);
+                *reinterpret_cast<bf16x8*>(s_rows + r * LDW + 8 * c8) = vh;
+                *reinterpret_cast<bf16x8*>(s_rows + (kDenseBatch * 16 + r) * LDW + 8 * c8) = vl;
             }
-            const int rfirst = k * 16 + 4 * lg;  // this lane's first row
-            const int P = rfirst / RP;           // its parent (all four rows share it)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                if (ct >= nct) break;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            __syncthreads();
+            const int kend = kb + kDenseBatch < nrt ? kb + kDenseBatch : nrt;
+            for (int k = kb; k < kend; ++k) {
+                const int rl = (k - kb) * 16 + (lane & 15);
+                bf16x8 ah[KS], al[KS];
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    acc = mfma(ah[s], qb[ct][s], acc);
-                    acc = mfma(al[s], qb[ct][s], acc);
+                    ah[s] = *reinterpret_cast<const bf16x8*>(s_rows + rl * LDW + 32 * s + 8 * lg);
+                    al[s] = *reinterpret_cast<const bf16x8*>(s_rows + (kDenseBatch * 16 + rl) * LDW + 32 * s + 8 * lg);
                 }
-                float z[4];
+                const int rfirst = k * 16 + 4 * lg;  // this lane's first row
+                const int P = rfirst / RP;           // its parent (all four rows share it)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = acc[i];
-                    if constexpr (TA == 2) v += shfl_xor(v, G);
-                    z[i] = (rfirst + i < nrows && rfirst + i < a.rows_limit) ? v * scale : -INFINITY;
-                }
-                const int slot = P < npar ? s_slot[qloc[ct] * npar + P] : 0xFF;
+                for (int ct = 0; ct < 4; ++ct) {
+                    if (ct >= nct) break;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < CPL; ++kk) {
-                    const int r0 = rfirst + kk * GB;  // first row of the candidate
-                    const bool exists = r0 < nrows && r0 < a.rows_limit;
-                    float l2 = block_score2<SK, GB, 0>(z + kk * GB, exists);
-                    l2 = sum_adjacent(l2, G);
-                    const int j = (r0 % RP) / GB;  // candidate = child j of P
-                    if (qok[ct] && head == 0 && term == 0 && exists && slot != 0xFF)
-                        a.u[(bh * a.N + t0 + qloc[ct]) * ucols + slot * GB + j] = l2 * kLn2;
+                    for (int s = 0; s < KS; ++s) {
+                        acc = mfma(ah[s], qb[ct][s], acc);
+                        acc = mfma(al[s], qb[ct][s], acc);
+                    }
+                    float z[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = acc[i];
+                        if constexpr (TA == 2) v += shfl_xor(v, G);
+                        z[i] = (rfirst + i < nrows && rfirst + i < rows_limit) ? v * scale : -INFINITY;
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < CPL; ++kk) {
+                        const int r0 = rfirst + kk * GB;  // first row of the candidate
+                        const bool exists = r0 < nrows && r0 < rows_limit;
+                        float l2 = block_score2<SK, GB, 0>(z + kk * GB, exists);
+                        l2 = sum_adjacent(l2, G);
+                        write(ct, P, (r0 % RP) / GB, l2 * kLn2, exists);  // candidate = child j of P
+                    }
                 }
             }
         }
+    };
+    // level l: candidates of the kept parents, by slot
+    pass(a.rows + (int64_t)b * a.rows_b_stride + (int64_t)h * a.rows_h_stride, a.rows_limit, npar,
+         [&](int ct, int P, int j, float v, bool exists) {
+             const int slot = P < npar ? s_slot[qloc[ct] * npar + P] : 0xFF;
+             if (qok[ct] && head == 0 && term == 0 && exists && slot != 0xFF)
+                 a.u[(bh * a.N + t0 + qloc[ct]) * ucols + slot * GB + j] = v;
+         });
+    if (a.rows2) {
+        // level l - 1 in the same pass: the children of every eligible level-l node, by node id
+        const int64_t pm2 = a.causal ? tl >> a.par2_span_log2 : a.M_par2 - 1;
+        const int npar2 = (int)((pm2 < a.M_par2 - 1 ? pm2 : a.M_par2 - 1) + 1);
+        pass(a.rows2 + (int64_t)b * a.rows2_b_stride + (int64_t)h * a.rows2_h_stride, a.rows2_limit, npar2,
+             [&](int ct, int P, int j, float v, bool exists) {
+                 if (qok[ct] && head == 0 && term == 0 && exists)
+                     a.u2[(bh * a.N + t0 + qloc[ct]) * a.u2_cols + P * GB + j] = v;
+             });
     }
 }
 

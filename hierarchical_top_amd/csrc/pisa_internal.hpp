@@ -175,6 +175,46 @@ struct ScoreArgs {
 constexpr int kDenseParents = 16;
 constexpr int64_t kDenseRows = 256;
 
+// nodes of level l (level 1 = leaf blocks of 2^c_log2 tokens) over n tokens
+inline int64_t level_nodes(int64_t n, int c_log2, int g_log2, int l)
+{
+    const int sh = c_log2 + (l - 1) * g_log2;
+    return (n + ((int64_t)1 << sh) - 1) >> sh;
+}
+// level l is scored densely (see above)
+inline bool dense_level(int64_t n, int c_log2, int g_log2, int l)
+{
+    const int g = 1 << g_log2;
+    return l >= 2 && (g == 2 || g == 4) && level_nodes(n, c_log2, g_log2, l + 1) <= kDenseParents &&
+           level_nodes(n, c_log2, g_log2, l - 1) <= kDenseRows;
+}
+// Two dense levels in a row share one pass over the queries: going down from l_top, a dense
+// level l whose next level l - 1 is dense too scores both (level l - 1 for every eligible
+// level-l node, kept by node id: its kept set is not known yet). Returns whether level l opens
+// such a pair, given that level l + 1 did not.
+inline bool dense_pair(int64_t n, int c_log2, int g_log2, int l)
+{
+    return dense_level(n, c_log2, g_log2, l) && dense_level(n, c_log2, g_log2, l - 1);
+}
+// columns of the by-node score rows of a pair's second level: every child slot of every
+// level-l node, rounded up to 4 so that rows stay 16-byte aligned
+inline int64_t dense_pair_cols(int64_t n, int c_log2, int g_log2, int l)
+{
+    return ((level_nodes(n, c_log2, g_log2, l) << g_log2) + 3) & ~(int64_t)3;
+}
+// the widest by-node score row over the dense pairs of a route from level l_top down (0: none)
+inline int64_t dense_pair_max_cols(int64_t n, int c_log2, int g_log2, int l_top)
+{
+    int64_t cols = 0;
+    for (int l = l_top; l >= 2; --l) {
+        if (!dense_pair(n, c_log2, g_log2, l)) continue;
+        const int64_t c = dense_pair_cols(n, c_log2, g_log2, l);
+        if (c > cols) cols = c;
+        --l;  // level l - 1 is the pair's second level
+    }
+    return cols;
+}
+
 struct DenseArgs {
     const void* Q;            // [B][N][H_q][d]
     int64_t N;
@@ -187,6 +227,14 @@ struct DenseArgs {
     int sk;                   // block score, as in ScoreArgs
     const int32_t* kept;      // [items][K_top] kept nodes of level l+1
     float* u;                 // [items][K_top * g]
+    // optional second level l - 1 in the same pass over the queries (rows2 != null): the
+    // candidates of every eligible level-l node, written to u2 by node id
+    const float* rows2;       // level l-2 summaries, strides and count as for rows
+    int64_t rows2_b_stride, rows2_h_stride, rows2_limit;
+    int par2_span_log2;       // log2 of the tokens spanned by a level-l node
+    int64_t M_par2;           // level-l nodes that exist
+    float* u2;                // [items][u2_cols]: column x = level l-1 node x
+    int64_t u2_cols;
 };
 
 // Upper levels whose nodes have g * g <= 16 grandchildren: one wave per chunk
@@ -225,6 +273,7 @@ struct SelectArgs {
     int win_log2;             // query window of the next level's clusters
     int32_t* idx;             // level 1: [items][K_top]
     float* score;             // level 1: [items][K_top] or null
+    int64_t u_cols;           // 0: u is [items][K_top * g] by kept slot; else [items][u_cols] by node id
 };
 
 struct LevelsArgs {
@@ -232,6 +281,7 @@ struct LevelsArgs {
     int32_t* kept[2];
     int64_t* flags;
     float* u;
+    float* u_pair;            // by-node scores of the second level of a dense pair: [items][cols]
     int32_t* counts;          // per scored level, at cnt_off[level]
     int32_t* cursor;          // same layout as counts
     int64_t cnt_total;
