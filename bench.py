@@ -1,6 +1,6 @@
 """Benchmark of PISA pyramid Top-K block selection on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick [--workload p64k|p16k]] [--no-cpu]
     python bench.py --traffic FETCH_DIR WRITE_DIR   (no GPU: counters -> profiles/traffic.json)
 
 One step = one pass of the selection path over the 262,144-token workload
@@ -16,7 +16,7 @@ Also reported (field "extra"): route-only time of the routers, the
 exhaustive BSA-style selector on the same inputs, the 16K and 64K prefill
 workloads, block-sparse attention at 64K, decode (32 sequences, 262,144
 cached tokens, 256 appended tokens: append + route microseconds per step),
-and a sweep of N = 4K .. 256K at the appendix's own selection-benchmark
+and a sweep of N = 4K .. 1M at the appendix's own selection-benchmark
 shape (32 query / 2 KV heads, d=64, g=2).
 
 Prints ONE JSON line. Only one GPU is used; --gpus above 1 exits with an error.
@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -51,8 +52,19 @@ STAGES_FUSED = ["build", "route_fused"]
 ARMED = {"build": 1, "route_fused": 1, "leaf": 1, "upper": 8, "cluster": 8, "final": 8}
 # kernel (name fragment in a rocprofv3 trace) of each single-kernel stage
 STAGE_KERNEL = {"leaf": "leaf_kernel", "build": "build_block_kernel", "route_fused": "route_query_kernel"}
+# kernel-name patterns (re.search) of the counter records: the fused router and the first stage of
+# the two-stage router are two instantiations of route_query_kernel (mode 0 and mode 1)
+KERNEL_PATTERN = {"leaf": "leaf_kernel", "build": "build_block_kernel",
+                  "route_fused": r"route_query_kernel\w*Li0ELi\d+EEEvNS_9RouteArgsE",
+                  "route_stage1": r"route_query_kernel\w*Li1ELi\d+EEEvNS_9RouteArgsE",
+                  "route_stage2": "stage2_kernel", "upper_sparse": "upper_ring_kernel",
+                  "upper_dense": "dense_kernel", "select": "select_kernel", "bsa": "bsa_tile_kernel"}
 # kernels of the 64K attention workload whose HBM traffic the counters measure (bench.py --only attn_bwd)
 ATTN_KERNEL = {"attn_fwd": "attn_cl_kernel", "attn_bwd": "attn_bwd_kernel", "dq_combine": "dq_combine_kernel"}
+# kernels of a decode step (bench.py --only decode): append the new token's pyramid path, route it,
+# attend over the selected blocks
+DECODE_KERNEL = {"decode_append": "append_kernel", "decode_route": "route_decode_kernel",
+                 "decode_attn": r"11attn_kernelI|^attn_kernel$"}
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read and 1 GiB written
 
 
@@ -145,6 +157,15 @@ STAGE_SOURCES = {
     "build": ("pyramid.hip",),
     "leaf": ("levels.hip", "levels_impl.hpp", "levels_bf16.hip", "stream.hpp"),
     "route_fused": ("route.hip", "route_impl.hpp", "route_bf16.hip"),
+    "route_stage1": ("route.hip", "route_impl.hpp", "route_bf16.hip"),
+    "route_stage2": ("route.hip", "route_impl.hpp", "route_bf16.hip"),
+    "upper_sparse": ("levels.hip", "levels_impl.hpp", "levels_bf16.hip", "stream.hpp"),
+    "upper_dense": ("levels.hip", "levels_impl.hpp", "levels_bf16.hip"),
+    "select": ("levels.hip",),
+    "bsa": ("bsa.hip",),
+    "decode_append": ("pyramid.hip",),
+    "decode_route": ("route.hip", "route_impl.hpp", "route_bf16.hip"),
+    "decode_attn": ("attn.hip",),
     "attn_fwd": ("attn_cl.hip", "attn_bwd.hpp", "stream.hpp"),
     "attn_bwd": ("attn_bwd.hip", "attn_bwd.hpp", "attn_cl.hip"),
     "dq_combine": ("attn_bwd.hip", "attn_bwd.hpp"),
@@ -201,8 +222,9 @@ def leaf_roofs(roof, w, peaks):
     """The leaf scoring against the roofs measured in the same run: its MFMA work against the
     MFMA loop and against the MFMA rate of the 1:1 MFMA + exp mix (the leaf's own mix: per 16 x 64
     logit tile 16 MFMAs and 16 wave-wide exponentials), and its exponentials (one per raw-key
-    logit of a scored leaf and head, section 3.2 eq 21) against the exp loop. The binding roof is
-    the slowest of the three floors."""
+    logit of a scored leaf and head, section 3.2 eq 21) against the exp loop; when the kernel's
+    HBM traffic per launch is known from counters (roof["traffic"]), also those bytes against
+    the copy loop. The binding roof is the slowest of these floors."""
     G = w.H_q // w.H_kv
     rw = workcount.route_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.g, w.K_top)
     s = roof["ms_per_launch"] * 1e-3
@@ -210,8 +232,13 @@ def leaf_roofs(roof, w, peaks):
     floors = {"mfma": flops / (peaks["mfma_bf16_tflops"] * 1e12),
               "exp": exps / (peaks["exp_gps"] * 1e9),
               "mfma+exp": flops / (peaks["mix_mfma_tflops"] * 1e12)}
+    moved = roof.get("traffic")
+    if moved:
+        floors["traffic"] = moved / (peaks["copy_gbs"] * 1e9)
     bind = max(floors, key=floors.get)
     return dict(algorithmic_exp=exps, achieved_exp_gps=exps / s / 1e9,
+                traffic_bytes=moved, traffic_gbs=moved / s / 1e9 if moved else None,
+                traffic_frac_of_measured_copy=moved / s / 1e9 / peaks["copy_gbs"] if moved else None,
                 exp_frac_of_derived_peak=exps / s / 1e9 / PEAK_EXP_GPS, derived_exp_peak_gps=PEAK_EXP_GPS,
                 measured_mfma_tflops=peaks["mfma_bf16_tflops"], frac_of_measured_mfma=roof["achieved"] / peaks["mfma_bf16_tflops"],
                 measured_mix_mfma_tflops=peaks["mix_mfma_tflops"],
@@ -297,24 +324,27 @@ def traffic_from_counters(fetch_dir, write_dir, workload="p256k", kernels=None):
     exactly COPY_BYTES. Writes profiles/traffic.json; returns the records."""
     fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
 
-    def avg(rows, frag, counter):
-        v = [r["c"][counter] for r in rows if frag in r["name"] and counter in r["c"]]
+    def avg(rows, pat, counter):
+        v = [r["c"][counter] for r in rows if re.search(pat, r["name"]) and counter in r["c"]]
         return (float(np.mean(v)) * 1024.0, len(v)) if v else (None, 0)
 
-    f_copy, _ = avg(fetch, "copyBuffer", "FETCH_SIZE")
-    w_copy, _ = avg(write, "copyBuffer", "WRITE_SIZE")
+    def largest(rows, counter):  # the calibration copy: the largest copy dispatch (a decode run has small ones)
+        v = [r["c"][counter] for r in rows if "copyBuffer" in r["name"] and counter in r["c"]]
+        return max(v) * 1024.0 if v else None
+
+    f_copy, w_copy = largest(fetch, "FETCH_SIZE"), largest(write, "WRITE_SIZE")
     if not f_copy or not w_copy:
         raise SystemExit("the calibration copy is missing from the counter runs")
     kf, kw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     out_file = ROOT / "profiles" / "traffic.json"
     recs = json.loads(out_file.read_text()) if out_file.exists() else {}
-    for stage, frag in (kernels or STAGE_KERNEL).items():
-        fb, nf = avg(fetch, frag, "FETCH_SIZE")
-        wb, nw = avg(write, frag, "WRITE_SIZE")
+    for stage, pat in (kernels or KERNEL_PATTERN).items():
+        fb, nf = avg(fetch, pat, "FETCH_SIZE")
+        wb, nw = avg(write, pat, "WRITE_SIZE")
         if fb is None or wb is None:
             continue
         recs["%s/%s" % (workload, stage)] = dict(
-            kernel=frag, bytes_per_launch=fb * kf + wb * kw, fetch_bytes=fb * kf, write_bytes=wb * kw,
+            kernel=pat, bytes_per_launch=fb * kf + wb * kw, fetch_bytes=fb * kf, write_bytes=wb * kw,
             dispatches=[nf, nw], scale=dict(fetch=kf, write=kw), source_hash=source_hash(stage))
     out_file.write_text(json.dumps(recs, indent=1, sort_keys=True) + "\n")
     return recs
@@ -570,19 +600,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--mode", choices=["auto", "levels", "fused", "two_stage"], default="auto")
     ap.add_argument("--quick", action="store_true", help="headline workload only (no extra workloads)")
+    ap.add_argument("--workload", choices=["p256k", "p64k", "p16k"], default="p256k",
+                    help="with --quick: the prefill workload timed (for kernel traces of the smaller ones)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle routing to time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a 1 GiB device copy (counter calibration for --traffic)")
     ap.add_argument("--only", choices=["attn_bwd", "decode"],
                     help="time one part alone (for kernel traces): the 64K attention backward, or 32 decode steps")
-    ap.add_argument("--traffic-workload", choices=["p256k", "p64k"], default="p256k",
-                    help="with --traffic: the counter runs were of the headline (p256k) or of --only attn_bwd (p64k)")
+    ap.add_argument("--traffic-workload", choices=["p256k", "p64k", "decode"], default="p256k",
+                    help="with --traffic: the counter runs were of the headline (p256k), of --only attn_bwd "
+                         "(p64k) or of --only decode (decode)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
     args = ap.parse_args()
     if args.traffic:
-        kern = ATTN_KERNEL if args.traffic_workload == "p64k" else STAGE_KERNEL
+        kern = {"p64k": ATTN_KERNEL, "decode": DECODE_KERNEL}.get(args.traffic_workload, KERNEL_PATTERN)
         print(json.dumps(traffic_from_counters(*args.traffic, workload=args.traffic_workload, kernels=kern), indent=1,
                          sort_keys=True))
         return
@@ -602,7 +635,9 @@ def main():
             copy_calibration()
         return
 
-    w = synth.workload("p256k")
+    if args.workload != "p256k" and not args.quick:
+        raise SystemExit("--workload other than p256k is for --quick runs (kernel traces)")
+    w = synth.workload(args.workload)
     log("generating", w)
     P = Prefill(w)
     torch.cuda.synchronize()
@@ -700,7 +735,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill routing 256K: pyramid build + routing of every position",
+        "config": {"workload": "prefill routing %dK: pyramid build + routing of every position" % (w.N // 1024),
                    "B": w.B, "N": w.N, "H_q": w.H_q, "H_kv": w.H_kv, "d": w.d, "C": w.C, "g": w.g,
                    "K_top": w.K_top, "causal": True, "planted_blocks_per_head": w.planted, "seed": w.seed,
                    "router": mname},
