@@ -2,7 +2,10 @@
 // Log-Linear Complexity", section 3.1 eq 6; appendix B: future tokens inside
 // a selected block are masked).
 //
-// One wave per (sequence, query row, KV head); four waves per workgroup.
+// One wave per (sequence, query row, KV head), four waves per workgroup; or,
+// when there are few rows (decode), one workgroup per (sequence, row, KV head)
+// whose four waves take every fourth selected block each and merge their
+// partial softmax states (max, sum, output) through LDS at the end (NS = 4).
 // Per selected block of C keys (C < 32 is padded to 32 with masked keys):
 //   S^T = K_blk Q^T on MFMA: A = 16 keys x d, B = d x 16 columns holding the
 //     G_Q query heads (and, for fp32 queries, their low halves). Tile rt's
@@ -16,9 +19,10 @@
 
 namespace pisa {
 
-template <int D, typename T, int G>
+template <int D, typename T, int G, int NS>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
 {
+    static_assert(NS == 1 || NS == 4, "waves per row: one, or the whole workgroup");
     constexpr int TA = Src<T>::TERMS;  // query terms (columns per head)
     constexpr int TB = Src<T>::TERMS;  // key / value / probability terms
     constexpr int KS = D / 32;
@@ -29,8 +33,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
     bf16* s_vt = reinterpret_cast<bf16*>(s_raw) + (size_t)wave * TB * D * ldv;
 
     const int64_t total = (int64_t)a.B * a.H_kv * a.N_q;
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    if (item >= total) return;
+    const int64_t item = (int64_t)blockIdx.x * (4 / NS) + wave / NS;
+    const int part = wave % NS;  // this wave's share of the row's blocks: k = part, part + NS, ...
+    if (item >= total) return;   // NS = 4: the whole workgroup (no barrier is skipped)
     const int64_t r = item % a.N_q;
     const int h = (int)((item / a.N_q) % a.H_kv);
     const int b = (int)(item / ((int64_t)a.N_q * a.H_kv));
@@ -68,7 +73,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
     const int64_t kstride = (int64_t)a.H_kv * D;
     const int nrt = Cp / 16;
 
-    for (int k = 0; k < a.K_top; ++k) {
+    for (int k = part; k < a.K_top; k += NS) {
         const int blk = sel[k];
         if (blk < 0) continue;
         const int64_t k0 = (int64_t)blk * C;
@@ -206,6 +211,63 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
+    if constexpr (NS > 1) {
+        // merge the NS waves' states: with M = the largest running max of a head, the row's
+        // sum is sum_w l_w 2^(m_w - M) and its output sum_w o_w 2^(m_w - M) (a wave that saw no
+        // visible key has m_w = -inf and weighs 0). The V^T staging area is free again.
+        __syncthreads();
+        float* s_m = reinterpret_cast<float*>(s_raw);  // [NS][16] running max per head column
+        float* s_l = s_m + NS * 16;                     // [NS][16] running sum
+        float* s_o = s_l + NS * 16;                     // [NS][16 heads][D] unnormalised output
+        if (lane < 16) {
+            s_m[part * 16 + lane] = m_run;
+            s_l[part * 16 + lane] = l_run;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int head = 4 * (lane >> 4) + i;
+            if (head < G) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) s_o[(part * 16 + head) * D + 16 * ct + (lane & 15)] = o[ct][i];
+            }
+        }
+        __syncthreads();
+        if (part != 0) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int head = (4 * (lane >> 4) + i) & 15;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NS; ++w) M = fmaxf(M, s_m[w * 16 + head]);
+            float L = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) o[ct][i] = 0.f;
+#pragma unroll
+            for (int w = 0; w < NS; ++w) {
+                const float mw = s_m[w * 16 + head];
+                const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+                L += f * s_l[w * 16 + head];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) o[ct][i] += f * s_o[(w * 16 + head) * D + 16 * ct + (lane & 15)];
+            }
+        }
+        // every lane: the merged (m, l) of head column lane % 16, as the single-wave path holds them
+        {
+            const int head = lane & 15;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NS; ++w) M = fmaxf(M, s_m[w * 16 + head]);
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < NS; ++w) {
+                const float mw = s_m[w * 16 + head];
+                L += (mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M)) * s_l[w * 16 + head];
+            }
+            m_run = M;
+            l_run = L;
+        }
+    }
+
     // normalise and store rows (heads) 4*(lane/16)+i < G
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -224,16 +286,23 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
     }
 }
 
-template <int D, typename T>
-static hipError_t attn_d(const AttnArgs& a, hipStream_t s)
+// Rows (sequence x row x KV head) below which a row gets a whole workgroup (NS = 4): with
+// one wave per row, 2,048 rows fill only two waves per CU.
+constexpr int64_t kAttnSplitRows = 2048;
+
+template <int D, typename T, int NS>
+static hipError_t attn_ns(const AttnArgs& a, hipStream_t s)
 {
     const int Cp = a.C < 32 ? 32 : a.C;
-    const size_t lds = (size_t)4 * Src<T>::TERMS * D * (Cp + 8) * 2;
+    // four waves' V^T staging; the NS = 4 merge reuses it for NS x 16 x (D + 2) floats
+    const size_t stage = (size_t)4 * Src<T>::TERMS * D * (Cp + 8) * 2;
+    const size_t merge = (size_t)NS * 16 * (D + 2) * 4;
+    const size_t lds = NS > 1 && merge > stage ? merge : stage;
     const int64_t total = (int64_t)a.B * a.H_kv * a.N_q;
-    const dim3 grid((unsigned)((total + 3) / 4));
+    const dim3 grid((unsigned)((total + 4 / NS - 1) / (4 / NS)));
 #define PISA_ATTN_G(GG)                                                                                        \
     case GG: {                                                                                                 \
-        auto k = attn_kernel<D, T, GG>;                                                                        \
+        auto k = attn_kernel<D, T, GG, NS>;                                                                    \
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
         if (e != hipSuccess) return e;                                                                         \
         hipLaunchKernelGGL(k, grid, dim3(256), lds, s, a, Cp);                                                 \
@@ -246,7 +315,7 @@ static hipError_t attn_d(const AttnArgs& a, hipStream_t s)
         PISA_ATTN_G(8)
     case 16:
         if constexpr (Src<T>::TERMS == 1) {
-            auto k = attn_kernel<D, T, 16>;
+            auto k = attn_kernel<D, T, 16, NS>;
             hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL(k, grid, dim3(256), lds, s, a, Cp);
@@ -257,6 +326,13 @@ static hipError_t attn_d(const AttnArgs& a, hipStream_t s)
         return hipErrorInvalidValue;
     }
 #undef PISA_ATTN_G
+}
+
+template <int D, typename T>
+static hipError_t attn_d(const AttnArgs& a, hipStream_t s)
+{
+    const int64_t total = (int64_t)a.B * a.H_kv * a.N_q;
+    return total < kAttnSplitRows ? attn_ns<D, T, 4>(a, s) : attn_ns<D, T, 1>(a, s);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int dtype, int d, hipStream_t s)
