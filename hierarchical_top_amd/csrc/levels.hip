@@ -108,6 +108,13 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
                 const float tv = val[j]; val[j] = v; v = tv;
             }
     };
+    int64_t F[3];
+    const int nF = forced_nodes(c, shl, causal, F);
+    // insertion-list length: the largest R = K - nF over the wave's ranked items, a wave-uniform
+    // (scalar) bound, so slots past it are skipped by scalar branches; each item then keeps the
+    // first K - nF entries of its list, which are its best K - nF candidates
+    const bool ranked = nA > K;
+    const int Rw = ballot(ranked && nF == 0) ? K : (ballot(ranked && nF == 1) ? K - 1 : (ballot(ranked && nF == 2) ? K - 2 : K - 3));
     int nkept;
     if (nA <= K) {
         // at most K_top candidates: all are kept without scoring (section 3.2)
@@ -123,8 +130,6 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
             }
         }
     } else {
-        int64_t F[3];
-        const int nF = forced_nodes(c, shl, causal, F);
         const int R = K - nF;
         float bu[KMAX];
         int bi[KMAX];
@@ -134,7 +139,7 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
         auto offer = [&](float xu, int xi) {
 #pragma unroll
             for (int q = 0; q < KMAX; ++q) {
-                if (q < R && before(xu, xi, bu[q], bi[q])) {
+                if (q < Rw && before(xu, xi, bu[q], bi[q])) {
                     const float tu = bu[q]; bu[q] = xu; xu = tu;
                     const int ti = bi[q]; bi[q] = xi; xi = ti;
                 }
