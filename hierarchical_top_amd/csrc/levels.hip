@@ -22,6 +22,9 @@ namespace pisa {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelItemsPerThread = 1;
+// cluster scatter: positions per thread (a workgroup's per-node cursor atomics are amortised
+// over kSelThreads * kScatterItemsPerThread positions, which must divide every window)
+constexpr int kScatterItemsPerThread = 4;
 
 // Eligible existing children of node P of level lp at level lp - 1, for query t.
 __device__ __forceinline__ int64_t n_children(int64_t P, int g, int64_t M_child, int64_t elig_max_child)
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a
     int* s_cnt = s_mem;
     int* s_pos = s_mem + a.M_bins;
     const int64_t bh = blockIdx.y;
-    const int64_t t0 = (int64_t)blockIdx.x * (kSelThreads * kSelItemsPerThread);
+    const int64_t t0 = (int64_t)blockIdx.x * (kSelThreads * kScatterItemsPerThread);
     const bool use_lds = a.M_bins <= kLdsBins;
     if (use_lds) {
         const int64_t cbase = ((t0 >> a.win_log2) * a.BH + bh) * a.M_bins;  // the block lies in one window
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a
         int32_t* cur = a.cursor + cbase;
         for (int64_t k = threadIdx.x; k < a.M_bins; k += kSelThreads) s_cnt[k] = 0;
         __syncthreads();
-        for (int k = 0; k < kSelItemsPerThread; ++k) {
+        for (int k = 0; k < kScatterItemsPerThread; ++k) {
             const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
             if (t >= a.N) continue;
             const int64_t i = bh * a.N + t;
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a
             s_pos[k] = v ? base_off[k] + atomicAdd(&cur[k], v) : 0;
         }
         __syncthreads();
-        for (int k = 0; k < kSelItemsPerThread; ++k) {
+        for (int k = 0; k < kScatterItemsPerThread; ++k) {
             const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
             if (t >= a.N) continue;
             const int64_t i = bh * a.N + t;
@@ -385,7 +388,7 @@ __global__ __launch_bounds__(kSelThreads) void scatter_lv_kernel(ScatterLvArgs a
             }
         }
     } else {
-        for (int k = 0; k < kSelItemsPerThread; ++k) {
+        for (int k = 0; k < kScatterItemsPerThread; ++k) {
             const int64_t t = t0 + (int64_t)k * kSelThreads + threadIdx.x;
             if (t >= a.N) continue;
             const int64_t i = bh * a.N + t;
@@ -681,7 +684,9 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         sc.kept = a.kept[cur]; sc.flags = a.flags; sc.offsets = a.offsets; sc.cursor = cursor;
         sc.entries = a.entries;
         {
-            const dim3 grid((unsigned)((N + per_blk - 1) / per_blk), (unsigned)BH);
+            const int64_t per_sc = (int64_t)kSelThreads * kScatterItemsPerThread;
+            static_assert(kSelThreads * kScatterItemsPerThread <= 4096, "a scatter block lies in one 2^12 window");
+            const dim3 grid((unsigned)((N + per_sc - 1) / per_sc), (unsigned)BH);
             const size_t lds = M_bins <= kLdsBins ? (size_t)2 * M_bins * 4 : 0;
             hipLaunchKernelGGL(scatter_lv_kernel, grid, dim3(kSelThreads), lds, s, sc);
             if ((err = hipGetLastError()) != hipSuccess) return err;
