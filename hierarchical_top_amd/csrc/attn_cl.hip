@@ -553,8 +553,8 @@ hipError_t launch_attn_cluster(AttnClArgs& a, const AttnClLayout& L, char* ws, h
     const size_t clds = L.M_blk <= kClLdsBins ? (size_t)2 * L.M_blk * 4 : 0;
     hipLaunchKernelGGL(attn_cluster_kernel, cgrid, dim3(kClThreads), clds, s, a, 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_scan_chunks(a.counts, L.n_clusters, a.qc, a.block_sums, a.offsets, a.chunk_off, a.chunk_cl, s)) !=
-        hipSuccess)
+    if ((e = launch_scan_chunks(a.counts, L.n_clusters, a.qc, a.block_sums, a.offsets, a.chunk_off, a.chunk_cl,
+                                L.max_chunks, s)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(attn_cluster_kernel, cgrid, dim3(kClThreads), clds, s, a, 1);
     return hipGetLastError();

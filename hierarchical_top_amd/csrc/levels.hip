@@ -445,8 +445,7 @@ __global__ __launch_bounds__(1024) void scan_totals_kernel(const int32_t* __rest
 __global__ __launch_bounds__(1024) void scan_final_kernel(const int32_t* __restrict__ counts, int64_t n, int qc,
                                                           const int32_t* __restrict__ sums,
                                                           int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ chunk_off,
-                                                          int32_t* __restrict__ chunk_cl)
+                                                          int32_t* __restrict__ chunk_off)
 {
     __shared__ int s_w0[16], s_w1[16], s_b[2];
     // prefix of the earlier blocks' totals
@@ -467,12 +466,28 @@ __global__ __launch_bounds__(1024) void scan_final_kernel(const int32_t* __restr
     if (i < n) {
         offsets[i] = x0;
         chunk_off[i] = x1;
-        for (int k = 0; k < nch; ++k) chunk_cl[x1 + k] = (int32_t)i;  // chunk -> cluster
     }
     if (i == n - 1) {
         offsets[n] = x0 + cnt;
         chunk_off[n] = x1 + nch;
     }
+}
+
+// Chunk -> cluster map: chunk c belongs to the last cluster whose first chunk is <= c (an empty
+// cluster shares its first-chunk offset with the next one). One thread per chunk: a cluster's
+// chunks are written in parallel however many it has.
+__global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restrict__ chunk_off, int64_t n,
+                                                        int64_t max_chunks, int32_t* __restrict__ chunk_cl)
+{
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= max_chunks || c >= chunk_off[n]) return;
+    int64_t lo = 0, hi = n;  // chunk_off[lo] <= c < chunk_off[hi]
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (chunk_off[mid] <= c) lo = mid;
+        else hi = mid;
+    }
+    chunk_cl[c] = (int32_t)lo;
 }
 
 // Output when no level is ranked (at most K_top leaf blocks): all eligible leaves.
@@ -503,14 +518,16 @@ hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s)
 }
 
 hipError_t launch_scan_chunks(const int32_t* counts, int64_t n, int qc, int32_t* block_sums, int32_t* offsets,
-                              int32_t* chunk_off, int32_t* chunk_cl, hipStream_t s)
+                              int32_t* chunk_off, int32_t* chunk_cl, int64_t max_chunks, hipStream_t s)
 {
     const unsigned nsb = (unsigned)((n + 1023) / 1024);
     hipLaunchKernelGGL(scan_totals_kernel, dim3(nsb), dim3(1024), 0, s, counts, n, qc, block_sums);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_final_kernel, dim3(nsb), dim3(1024), 0, s, counts, n, qc, block_sums, offsets, chunk_off,
-                       chunk_cl);
+    hipLaunchKernelGGL(scan_final_kernel, dim3(nsb), dim3(1024), 0, s, counts, n, qc, block_sums, offsets, chunk_off);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_map_kernel, dim3((unsigned)((max_chunks + 255) / 256)), dim3(256), 0, s, chunk_off, n,
+                       max_chunks, chunk_cl);
     return hipGetLastError();
 }
 
@@ -673,12 +690,11 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
         int32_t* cursor = a.cursor + a.cnt_off[l];
 
         stage_mark(PISA_STAGE_CLUSTER, false, s);
-        const unsigned nsb = (unsigned)((n_clusters + 1023) / 1024);
-        hipLaunchKernelGGL(scan_totals_kernel, dim3(nsb), dim3(1024), 0, s, counts, n_clusters, qc, a.block_sums);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(scan_final_kernel, dim3(nsb), dim3(1024), 0, s, counts, n_clusters, qc, a.block_sums,
-                           a.offsets, a.chunk_off, a.chunk_cl);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        // bound on the chunks: every entry in chunks of qc, plus one partial chunk per cluster
+        const int64_t max_chunks = ((int64_t)BH * N * r.K_top + qc - 1) / qc + n_clusters;
+        if ((err = launch_scan_chunks(counts, n_clusters, qc, a.block_sums, a.offsets, a.chunk_off, a.chunk_cl,
+                                      max_chunks, s)) != hipSuccess)
+            return err;
         ScatterLvArgs sc;
         sc.H = p.H; sc.K_top = r.K_top; sc.win_log2 = wl; sc.N = N; sc.M_bins = M_bins; sc.BH = BH;
         sc.kept = a.kept[cur]; sc.flags = a.flags; sc.offsets = a.offsets; sc.cursor = cursor;

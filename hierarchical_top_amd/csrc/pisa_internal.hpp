@@ -119,10 +119,10 @@ hipError_t launch_attn_clustered(AttnClArgs a, int d, char* ws, hipStream_t s);
 
 // Shared clustering steps (levels.hip): zero n ints; exclusive scans of n
 // cluster sizes into offsets, chunks of qc entries per cluster into chunk_off
-// and the chunk -> cluster map.
+// and the chunk -> cluster map (chunk_cl holds max_chunks, a bound on the chunks).
 hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_scan_chunks(const int32_t* counts, int64_t n, int qc, int32_t* block_sums, int32_t* offsets,
-                              int32_t* chunk_off, int32_t* chunk_cl, hipStream_t s);
+                              int32_t* chunk_off, int32_t* chunk_cl, int64_t max_chunks, hipStream_t s);
 
 struct BsaArgs {
     PyrArgs p;
