@@ -26,11 +26,12 @@ constexpr int kSelItemsPerThread = 1;
 // over kSelThreads * kScatterItemsPerThread positions, which must divide every window)
 constexpr int kScatterItemsPerThread = 4;
 
-// Eligible existing children of node P of level lp at level lp - 1, for query t.
-__device__ __forceinline__ int64_t n_children(int64_t P, int g, int64_t M_child, int64_t elig_max_child)
+// Eligible existing children of node P of level lp at level lp - 1, for query t. Positions,
+// node ids and counts of the level router fit 32 bits (it takes N < 2^25).
+__device__ __forceinline__ int n_children(int P, int g, int M_child, int elig_max_child)
 {
-    const int64_t lo = P * g;
-    int64_t hi = lo + g;
+    const int lo = P * g;
+    int hi = lo + g;
     if (hi > M_child) hi = M_child;
     if (hi > elig_max_child + 1) hi = elig_max_child + 1;
     return hi > lo ? hi - lo : 0;
@@ -38,11 +39,11 @@ __device__ __forceinline__ int64_t n_children(int64_t P, int g, int64_t M_child,
 
 // Forced nodes of level l for a query in leaf c (first, current and previous
 // leaf's ancestors), deduplicated; returns the count (0 without causal masking).
-__device__ __forceinline__ int forced_nodes(int64_t c, int shl, bool causal, int64_t F[3])
+__device__ __forceinline__ int forced_nodes(int c, int shl, bool causal, int F[3])
 {
     // constant indices only, so that F stays in registers
-    const int64_t fc = c >> shl;
-    const int64_t fp = c >= 1 ? (c - 1) >> shl : 0;
+    const int fc = c >> shl;
+    const int fp = c >= 1 ? (c - 1) >> shl : 0;
     const bool hc = fc != 0;
     const bool hp = c >= 1 && fp != 0 && fp != fc;
     F[0] = 0;
@@ -51,7 +52,7 @@ __device__ __forceinline__ int forced_nodes(int64_t c, int shl, bool causal, int
     return causal ? 1 + (hc ? 1 : 0) + (hp ? 1 : 0) : 0;
 }
 
-__device__ __forceinline__ bool in3(int64_t x, const int64_t F[3], int nF)
+__device__ __forceinline__ bool in3(int x, const int F[3], int nF)
 {
     return (nF > 0 && x == F[0]) || (nF > 1 && x == F[1]) || (nF > 2 && x == F[2]);
 }
@@ -67,18 +68,18 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
     const int64_t i = bh * a.N + t;
     const int K = a.K_top, g = GB ? GB : 1 << a.g_log2;
     const int l = a.level;
-    const int64_t c = t >> a.c_log2;
+    const int c = (int)(t >> a.c_log2);
     const bool causal = a.causal != 0;
     const int shl = (l - 1) * a.g_log2;
     const int span_log2 = a.c_log2 + shl;
-    const int64_t M_l = (a.N + ((int64_t)1 << span_log2) - 1) >> span_log2;
-    const int64_t elig_max = causal ? (t >> span_log2) : M_l - 1;
+    const int M_l = (int)((a.N + ((int64_t)1 << span_log2) - 1) >> span_log2);
+    const int elig_max = causal ? (int)(t >> span_log2) : M_l - 1;
 
     // kept nodes of level l + 1 (the parents of this level's candidates)
     int kin[KMAX];
 #pragma unroll
     for (int s = 0; s < KMAX; ++s) kin[s] = -1;
-    int64_t nA = 0;
+    int nA = 0;
     if (a.init) {
         nA = elig_max + 1 < M_l ? elig_max + 1 : M_l;
     } else {
@@ -111,7 +112,7 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
                 const float tv = val[j]; val[j] = v; v = tv;
             }
     };
-    int64_t F[3];
+    int F[3];
     const int nF = forced_nodes(c, shl, causal, F);
     // insertion-list length: the largest R = K - nF over the wave's ranked items, a wave-uniform
     // (scalar) bound, so slots past it are skipped by scalar branches; each item then keeps the
@@ -123,13 +124,13 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
         // at most K_top candidates: all are kept without scoring (section 3.2)
         nkept = (int)nA;
         if (a.init) {
-            for (int64_t x = 0; x < nA; ++x) put((int)x, INFINITY);
+            for (int x = 0; x < nA; ++x) put(x, INFINITY);
         } else {
 #pragma unroll
             for (int s = 0; s < KMAX; ++s) {
                 if (kin[s] < 0) continue;
-                const int64_t nc = n_children(kin[s], g, M_l, elig_max);
-                for (int64_t j = 0; j < nc; ++j) put((int)((int64_t)kin[s] * g + j), INFINITY);
+                const int nc = n_children(kin[s], g, M_l, elig_max);
+                for (int j = 0; j < nc; ++j) put(kin[s] * g + j, INFINITY);
             }
         }
     } else {
@@ -180,21 +181,21 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
 #pragma unroll
             for (int s = 0; s < KMAX; ++s) {
                 if (kin[s] < 0) continue;
-                const int64_t nc = n_children(kin[s], g, M_l, elig_max);
+                const int nc = n_children(kin[s], g, M_l, elig_max);
 #pragma unroll
                 for (int j = 0; j < GB; ++j) {
-                    const int64_t x = (int64_t)kin[s] * GB + j;
-                    if (j < nc && !in3(x, F, nF)) offer(ur[s * GB + j], (int)x);
+                    const int x = kin[s] * GB + j;
+                    if (j < nc && !in3(x, F, nF)) offer(ur[s * GB + j], x);
                 }
             }
         } else {
 #pragma unroll
             for (int s = 0; s < KMAX; ++s) {
                 if (kin[s] < 0) continue;
-                const int64_t nc = n_children(kin[s], g, M_l, elig_max);
-                for (int64_t j = 0; j < nc; ++j) {
-                    const int64_t x = (int64_t)kin[s] * g + j;
-                    if (!in3(x, F, nF)) offer(urow[s * g + j], (int)x);
+                const int nc = n_children(kin[s], g, M_l, elig_max);
+                for (int j = 0; j < nc; ++j) {
+                    const int x = kin[s] * g + j;
+                    if (!in3(x, F, nF)) offer(urow[s * g + j], x);
                 }
             }
         }
@@ -263,22 +264,22 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
     // next level: is it ranked for this item, and which kept nodes own ranked candidates?
     const int shl2 = shl - a.g_log2;
     const int span2 = a.c_log2 + shl2;
-    const int64_t M_c = (a.N + ((int64_t)1 << span2) - 1) >> span2;
-    const int64_t em_c = causal ? (t >> span2) : M_c - 1;
-    int64_t nA2 = 0;
+    const int M_c = (int)((a.N + ((int64_t)1 << span2) - 1) >> span2);
+    const int em_c = causal ? (int)(t >> span2) : M_c - 1;
+    int nA2 = 0;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
         if (j < nkept) nA2 += n_children(ids[j], g, M_c, em_c);
     uint64_t mask = 0;
     if (nA2 > K) {
-        int64_t F2[3];
+        int F2[3];
         const int nF2 = forced_nodes(c, shl2, causal, F2);
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             if (j < nkept) {
-                const int64_t P = ids[j];
-                const int64_t nc = n_children(P, g, M_c, em_c);
-                int64_t nforced = 0;
+                const int P = ids[j];
+                const int nc = n_children(P, g, M_c, em_c);
+                int nforced = 0;
 #pragma unroll
                 for (int k = 0; k < 3; ++k) nforced += (k < nF2 && F2[k] >= P * g && F2[k] < P * g + nc) ? 1 : 0;
                 if (nc > nforced) {
@@ -287,7 +288,7 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
                         // forced and current-path nodes are shared by neighbouring queries:
                         // one LDS atomic per wave when every active lane adds to the same bin
                         const uint64_t act = ballot(true);
-                        const int64_t P0 = __builtin_amdgcn_readfirstlane((int)P);
+                        const int P0 = __builtin_amdgcn_readfirstlane(P);
                         if (ballot(P == P0) == act) {
                             if (lane_id() == __builtin_ctzll(act)) atomicAdd(&s_hist[P0], __popcll(act));
                         } else {
