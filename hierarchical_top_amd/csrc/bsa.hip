@@ -17,9 +17,10 @@
 namespace pisa {
 
 constexpr int kBsaWaves = 8;
-constexpr int kBsaKMax = 8;  // largest K_top the exhaustive selector supports
+constexpr int kBsaKMax = 8;      // K_top of the MFMA-stationary kernel below (bsa_tile_kernel)
+constexpr int kBsaKMaxWide = 16;  // largest K_top of the exhaustive selector (this kernel, KM = 16)
 
-template <int D, typename T, int G>
+template <int D, typename T, int G, int KM>
 __global__ __launch_bounds__(512) void bsa_kernel(BsaArgs a)
 {
     constexpr int TA = Src<T>::TERMS;
@@ -79,12 +80,12 @@ __global__ __launch_bounds__(512) void bsa_kernel(BsaArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m2[i] = -INFINITY; s2[i] = 0.f; }
     // top lists: per lane, per held query q (NQ), KMAX entries in selection order
-    float tu[NQ][kBsaKMax];
-    int ti[NQ][kBsaKMax];
+    float tu[NQ][KM];
+    int ti[NQ][KM];
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
-        for (int j = 0; j < kBsaKMax; ++j) { tu[q][j] = -INFINITY; ti[q][j] = 0x7fffffff; }
+        for (int j = 0; j < KM; ++j) { tu[q][j] = -INFINITY; ti[q][j] = 0x7fffffff; }
     // number of ranked picks of each held query
     int rk[NQ];
 #pragma unroll
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(512) void bsa_kernel(BsaArgs a)
                             float xu = u;
                             int xi = leaf;
 #pragma unroll
-                            for (int j = 0; j < kBsaKMax; ++j) {
+                            for (int j = 0; j < KM; ++j) {
                                 if (j < rk[q] && before(xu, xi, tu[q][j], ti[q][j])) {
                                     const float t_ = tu[q][j]; tu[q][j] = xu; xu = t_;
                                     const int i_ = ti[q][j]; ti[q][j] = xi; xi = i_;
@@ -225,17 +226,17 @@ __global__ __launch_bounds__(512) void bsa_kernel(BsaArgs a)
     for (int q = 0; q < NQ; ++q) {
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
-            float ou[kBsaKMax];
-            int oi[kBsaKMax];
+            float ou[KM];
+            int oi[KM];
 #pragma unroll
-            for (int j = 0; j < kBsaKMax; ++j) { ou[j] = shfl_xor(tu[q][j], o); oi[j] = shfl_xor(ti[q][j], o); }
+            for (int j = 0; j < KM; ++j) { ou[j] = shfl_xor(tu[q][j], o); oi[j] = shfl_xor(ti[q][j], o); }
 #pragma unroll
-            for (int k = 0; k < kBsaKMax; ++k) {
+            for (int k = 0; k < KM; ++k) {
                 float xu = ou[k];
                 int xi = oi[k];
                 if (xi == 0x7fffffff) continue;
 #pragma unroll
-                for (int j = 0; j < kBsaKMax; ++j) {
+                for (int j = 0; j < KM; ++j) {
                     if (j < rk[q] && before(xu, xi, tu[q][j], ti[q][j])) {
                         const float t_ = tu[q][j]; tu[q][j] = xu; xu = t_;
                         const int i_ = ti[q][j]; ti[q][j] = xi; xi = i_;
@@ -261,13 +262,13 @@ __global__ __launch_bounds__(512) void bsa_kernel(BsaArgs a)
         if (!writer || tq >= N) continue;
         const int64_t c = tq >> p.c_log2;
         const int64_t E = a.causal ? c + 1 : M1;
-        int ids[kBsaKMax + 4];
-        float val[kBsaKMax + 4];
+        int ids[KM + 4];
+        float val[KM + 4];
 #pragma unroll
-        for (int j = 0; j < kBsaKMax + 4; ++j) { ids[j] = 0x7fffffff; val[j] = -INFINITY; }
+        for (int j = 0; j < KM + 4; ++j) { ids[j] = 0x7fffffff; val[j] = -INFINITY; }
         auto put = [&](int x, float v) {
 #pragma unroll
-            for (int j = 0; j < kBsaKMax + 4; ++j)
+            for (int j = 0; j < KM + 4; ++j)
                 if (x < ids[j]) {
                     const int i_ = ids[j]; ids[j] = x; x = i_;
                     const float v_ = val[j]; val[j] = v; v = v_;
@@ -282,12 +283,12 @@ __global__ __launch_bounds__(512) void bsa_kernel(BsaArgs a)
                 if (c - 1 >= 1) put((int)(c - 1), INFINITY);
             }
 #pragma unroll
-            for (int j = 0; j < kBsaKMax; ++j)
+            for (int j = 0; j < KM; ++j)
                 if (j < rk[q] && ti[q][j] != 0x7fffffff) put(ti[q][j], tu[q][j]);
         }
         const int64_t base = (((int64_t)b * p.H + h) * N + tq) * a.K_top;
 #pragma unroll
-        for (int j = 0; j < kBsaKMax + 4; ++j) {
+        for (int j = 0; j < KM + 4; ++j) {
             if (j < a.K_top) {
                 const bool okj = ids[j] != 0x7fffffff;
                 a.idx[base + j] = okj ? ids[j] : -1;
@@ -596,20 +597,20 @@ static hipError_t bsa_tile_launch(const BsaArgs& a, hipStream_t s)
     return e != hipSuccess ? e : hipGetLastError();
 }
 
-template <int D, typename T>
-static hipError_t bsa_d(const BsaArgs& a, hipStream_t s)
+template <int D, typename T, int KM>
+static hipError_t bsa_dk(const BsaArgs& a, hipStream_t s)
 {
     const int R = a.G * Src<T>::TERMS;
     const int64_t per_wg = (int64_t)kBsaWaves * (16 / R);
     const int64_t grid = (int64_t)a.p.B * a.p.H * ((a.N + per_wg - 1) / per_wg);
     switch (a.G) {
-    case 1: hipLaunchKernelGGL((bsa_kernel<D, T, 1>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((bsa_kernel<D, T, 2>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((bsa_kernel<D, T, 4>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((bsa_kernel<D, T, 8>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((bsa_kernel<D, T, 1, KM>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((bsa_kernel<D, T, 2, KM>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((bsa_kernel<D, T, 4, KM>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((bsa_kernel<D, T, 8, KM>), dim3((unsigned)grid), dim3(512), 0, s, a); break;
     case 16:
         if constexpr (Src<T>::TERMS == 1) {
-            hipLaunchKernelGGL((bsa_kernel<D, T, 16>), dim3((unsigned)grid), dim3(512), 0, s, a);
+            hipLaunchKernelGGL((bsa_kernel<D, T, 16, KM>), dim3((unsigned)grid), dim3(512), 0, s, a);
             break;
         }
         return hipErrorInvalidValue;
@@ -618,10 +619,16 @@ static hipError_t bsa_d(const BsaArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int D, typename T>
+static hipError_t bsa_d(const BsaArgs& a, hipStream_t s)
+{
+    return a.K_top <= kBsaKMax ? bsa_dk<D, T, kBsaKMax>(a, s) : bsa_dk<D, T, kBsaKMaxWide>(a, s);
+}
+
 hipError_t launch_bsa(const BsaArgs& a, int dtype, int d, hipStream_t s)
 {
     if (dtype == 0) return d == 64 ? bsa_d<64, float>(a, s) : bsa_d<128, float>(a, s);
-    if (a.G == 4 || a.G == 8 || a.G == 16) {  // queries stationary in MFMA registers
+    if (a.K_top <= kBsaKMax && (a.G == 4 || a.G == 8 || a.G == 16)) {  // queries stationary in MFMA registers
         if (d == 64)
             return a.G == 4 ? bsa_tile_launch<64, 4>(a, s) : (a.G == 8 ? bsa_tile_launch<64, 8>(a, s) : bsa_tile_launch<64, 16>(a, s));
         return a.G == 4 ? bsa_tile_launch<128, 4>(a, s) : (a.G == 8 ? bsa_tile_launch<128, 8>(a, s) : bsa_tile_launch<128, 16>(a, s));

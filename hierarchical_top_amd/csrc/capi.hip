@@ -728,7 +728,7 @@ pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, int32_t dt, in
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return fail(PISA_EUNSUPPORTED, "gqa_group=%d", G);
     if (dt == PISA_F32 && G > 8) return fail(PISA_EUNSUPPORTED, "f32 selection supports gqa_group <= 8");
     if (K_top < 1) return fail(PISA_EINVAL, "K_top=%d < 1", K_top);
-    if (K_top > 8) return fail(PISA_EUNSUPPORTED, "exhaustive selector supports K_top <= 8");
+    if (K_top > 16) return fail(PISA_EUNSUPPORTED, "exhaustive selector supports K_top <= 16");
     if (causal && K_top < 3) return fail(PISA_EINVAL, "causal selection needs K_top >= 3");
     if (!Q || !idx || !aligned16(Q)) return fail(PISA_EINVAL, "Q and idx must be non-NULL, Q 16-byte aligned");
     BsaArgs a;

@@ -310,7 +310,8 @@ pisa_status pisa_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
  * when at most K_top leaves are eligible. Q, idx and score as in
  * pisa_route_prefill; score holds the summed probability (+inf for blocks
  * kept without a score). The pyramid must hold a build over N.
- * Supported: K_top <= 8. Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE.
+ * Supported: K_top <= 16 (bf16 queries with G_Q >= 4 and K_top <= 8 take a faster kernel
+ * that keeps the queries in MFMA registers). Errors: PISA_EINVAL, PISA_EUNSUPPORTED, PISA_ENOSPACE.
  */
 pisa_status pisa_bsa_select(const pisa_pyramid* p, const void* Q, int32_t dt, int64_t N,
                             int32_t H_q, int32_t K_top, int32_t causal, int32_t gqa_group,

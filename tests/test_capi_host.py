@@ -190,7 +190,7 @@ def test_attention_and_bsa_validation(lib):
     assert a(FAKE, FAKE, None, pisa.BF16, 1, 10, 10, 10, 8, 2, 128, 64, FAKE, 8, 1, None, FAKE, None, None) == EINVAL
     desc = fake_pyramid(lib)
     b = lib.pisa_bsa_select
-    assert b(ctypes.byref(desc), FAKE, pisa.BF16, 4096, 16, 9, 1, 4, FAKE, None, None) == EUNSUPPORTED
+    assert b(ctypes.byref(desc), FAKE, pisa.BF16, 4096, 16, 17, 1, 4, FAKE, None, None) == EUNSUPPORTED
     assert b(ctypes.byref(desc), FAKE, pisa.BF16, 4096, 16, 2, 1, 4, FAKE, None, None) == EINVAL
     assert b(ctypes.byref(desc), FAKE, pisa.BF16, 5000, 16, 8, 1, 4, FAKE, None, None) == ENOSPACE
 

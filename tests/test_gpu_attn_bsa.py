@@ -174,6 +174,11 @@ def _bsa_compare(w, t, causal, K_top):
     ("paper_shape", True, 8, 1024),
     ("f32_g4", True, 5, None),
     ("p64k", True, 8, 2048),
+    # K_top above 8: the selector with 16-entry pick lists (fp32 G=1, bf16 G=2 and G=4, fp32 G=4)
+    ("tiny", True, 12, None),
+    ("ragged", True, 16, None),
+    ("c32_b2", True, 13, None),
+    ("f32_g4", True, 16, None),
 ])
 def test_bsa_matches_oracle(case, causal, K_top, sample):
     w = W[case]
