@@ -435,8 +435,8 @@ pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, cons
 
     if (N >= ((int64_t)1 << 25)) return fail(PISA_EUNSUPPORTED, "clustered routing needs N < 2^25");
     if (mode == PISA_ROUTE_LEVELS) {
-        if (K_top > 16 && levels_top(N, p->C, p->g, K_top) > 0)
-            return fail(PISA_EUNSUPPORTED, "level-synchronous routing ranks at most K_top = 16 blocks");
+        if (K_top > 32 && levels_top(N, p->C, p->g, K_top) > 0)
+            return fail(PISA_EUNSUPPORTED, "level-synchronous routing ranks at most K_top = 32 blocks");
         if (items * K_top > ((int64_t)1 << 31) - 1)
             return fail(PISA_EUNSUPPORTED, "B * H_kv * N * K_top exceeds 2^31 - 1");
         const size_t lds_leaf = (size_t)p->g * p->C * (p->d + 8) * 2 * (dt == PISA_F32 ? 2 : 1);

@@ -193,9 +193,11 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
             for (int s = 0; s < KMAX; ++s) {
                 if (kin[s] < 0) continue;
                 const int nc = n_children(kin[s], g, M_l, elig_max);
+                // the children's scores: by slot, or by node id on a dense pair's second level
+                const float* us = a.u_cols ? a.u + i * a.u_cols + (int64_t)kin[s] * g : urow + s * g;
                 for (int j = 0; j < nc; ++j) {
                     const int x = kin[s] * g + j;
-                    if (!in3(x, F, nF)) offer(urow[s * g + j], x);
+                    if (!in3(x, F, nF)) offer(us[j], x);
                 }
             }
         }
@@ -549,10 +551,14 @@ static hipError_t launch_select(const SelectArgs& sa, int K_top, hipStream_t s)
         if (g == 4) PISA_SEL(8, 4);
         else if (g == 2) PISA_SEL(8, 2);
         else PISA_SEL(8, 0);
-    } else {
+    } else if (K_top <= 16) {
         if (g == 4) PISA_SEL(16, 4);
         else if (g == 2) PISA_SEL(16, 2);
         else PISA_SEL(16, 0);
+    } else {
+        // K_top <= 32 (g * K_top <= 64, so g = 2): scores read as needed, which keeps the
+        // 32-entry lists in registers
+        PISA_SEL(32, 0);
     }
 #undef PISA_SEL
     return hipGetLastError();

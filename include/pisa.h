@@ -62,7 +62,7 @@ typedef enum pisa_route_mode {
     PISA_ROUTE_FUSED = 1,      /* all levels of one query in one program (per-query) */
     PISA_ROUTE_LEVELS = 2      /* all queries advance one level at a time; at every level
                                   the (query, kept node) pairs are clustered by node and
-                                  scored with the node's data staged once (K_top <= 16) */
+                                  scored with the node's data staged once (K_top <= 32) */
 } pisa_route_mode;
 
 /*

@@ -75,7 +75,7 @@ int main(void)
     EXPECT(pisa_route_decode(&p, fake, fake, PISA_BF16, NULL, 16, 8, 4, fi, NULL, NULL), PISA_EINVAL);
     EXPECT(pisa_route_decode(&p, fake, fake, PISA_BF16, (const int64_t*)fake, 16, 2, 4, fi, NULL, NULL), PISA_EINVAL);
     EXPECT(pisa_route_decode_scored(&p, fake, fake, PISA_BF16, (const int64_t*)fake, 16, 8, 4, 3, fi, NULL, NULL), PISA_EINVAL);
-    EXPECT(pisa_bsa_select(&p, fake, PISA_BF16, 4096, 16, 9, 1, 4, fi, NULL, NULL), PISA_EUNSUPPORTED);
+    EXPECT(pisa_bsa_select(&p, fake, PISA_BF16, 4096, 16, 17, 1, 4, fi, NULL, NULL), PISA_EUNSUPPORTED);
     EXPECT(pisa_bsa_select(&p, NULL, PISA_BF16, 4096, 16, 8, 1, 4, fi, NULL, NULL), PISA_EINVAL);
     EXPECT(pisa_sparse_attn_workspace(1, 4096, 4096, 16, 4, 128, 64, 8, NULL), PISA_EINVAL);
     EXPECT(pisa_sparse_attn_bwd_workspace(1, 4096, 4096, 16, 3, 128, 64, 8, &n), PISA_EINVAL);

@@ -42,6 +42,9 @@ CASES = {
     "paper64k": synth.paper_shape(65536, seed=27),
     # ragged length: sparse levels 3 and 2 with tail nodes missing grandchildren, two-head groups
     "ragged_big": synth.Workload("rbig", 1, 70001, 4, 2, 128, 64, 4, 8, "bf16", 0, 25, False),
+    # g=2 with K_top above 16 (level nodes 625, 313, 157, 79, 40, 20, 10, ...): at K_top=18 the top
+    # ranked level is scored densely and the rest sparsely, at K_top=32 every upper level sparsely
+    "g2_wide": synth.Workload("g2w", 1, 20000, 8, 2, 128, 32, 2, 8, "bf16", 0, 28, False),
 }
 
 
@@ -111,11 +114,11 @@ def _positions(w, sample):
     ("sparse64k", 8, True, 600),
     ("ragged_big", 8, True, 600),
     ("paper64k", 8, True, 600),
+    ("g2_wide", 18, True, 600),
+    ("g2_wide", 32, True, 600),
 ])
 def test_route_matches_oracle(mode, case, K_top, causal, sample):
     w = CASES[case]
-    if mode == "levels" and 16 < K_top < -(-w.N // w.C):
-        pytest.skip("the level-synchronous router ranks at most 16 blocks")
     print("case", case, "mode", mode, "K_top", K_top, "causal", causal, flush=True)
     Q, K = _inputs(w)
     t = _positions(w, sample)
@@ -125,7 +128,11 @@ def test_route_matches_oracle(mode, case, K_top, causal, sample):
     for b in range(w.B):
         gi = idx[b][:, t].transpose(1, 0, 2)
         gs = score[b][:, t].transpose(1, 0, 2)
+        # the share of items whose oracle route has a cut within the band grows with K_top: at
+        # g=2 and K_top > 16 about five levels of ~60 candidates are ranked and the oracle's own
+        # near-tie share on g2_wide is 0.24 (K_top=18) and 0.26 (K_top=32)
         stats = compare(gi, gs, orc[b], t, w.C, K_top, causal=causal, M1=M1,
+                        max_near_tie_frac=0.35 if K_top > 16 else 0.25,
                         reach=route_reach(opyr, Q[b, t].float().numpy(), b, t, K_top, causal))
         print(case, mode, b, stats)
 
