@@ -224,7 +224,8 @@ def leaf_roofs(roof, w, peaks):
     logit tile 16 MFMAs and 16 wave-wide exponentials), and its exponentials (one per raw-key
     logit of a scored leaf and head, section 3.2 eq 21) against the exp loop; when the kernel's
     HBM traffic per launch is known from counters (roof["traffic"]), also those bytes against
-    the copy loop. The binding roof is the slowest of these floors."""
+    the gather loop (almost all of them are gathered 1 KiB query rows) and, for reference, the
+    copy loop. The binding roof is the slowest of these floors."""
     G = w.H_q // w.H_kv
     rw = workcount.route_work(w.B, w.N, w.H_kv, G, w.d, w.C, w.g, w.K_top)
     s = roof["ms_per_launch"] * 1e-3
@@ -234,11 +235,12 @@ def leaf_roofs(roof, w, peaks):
               "mfma+exp": flops / (peaks["mix_mfma_tflops"] * 1e12)}
     moved = roof.get("traffic")
     if moved:
-        floors["traffic"] = moved / (peaks["copy_gbs"] * 1e9)
+        floors["traffic"] = moved / (peaks["gather_gbs"] * 1e9)
     bind = max(floors, key=floors.get)
     return dict(algorithmic_exp=exps, achieved_exp_gps=exps / s / 1e9,
                 traffic_bytes=moved, traffic_gbs=moved / s / 1e9 if moved else None,
                 traffic_frac_of_measured_copy=moved / s / 1e9 / peaks["copy_gbs"] if moved else None,
+                traffic_frac_of_measured_gather=moved / s / 1e9 / peaks["gather_gbs"] if moved else None,
                 exp_frac_of_derived_peak=exps / s / 1e9 / PEAK_EXP_GPS, derived_exp_peak_gps=PEAK_EXP_GPS,
                 measured_mfma_tflops=peaks["mfma_bf16_tflops"], frac_of_measured_mfma=roof["achieved"] / peaks["mfma_bf16_tflops"],
                 measured_mix_mfma_tflops=peaks["mix_mfma_tflops"],
@@ -261,6 +263,9 @@ def unit_peaks(reps: int = 5):
     for f in ("pisa_peak_exp", "pisa_peak_mfma", "pisa_peak_mix"):
         getattr(L, f).argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.pisa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.pisa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.pisa_peak_gather.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_uint32, ctypes.c_void_p]
     blocks, iters = 2048, 4096                      # 8 waves per SIMD
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
@@ -279,6 +284,14 @@ def unit_peaks(reps: int = 5):
     dst = torch.empty_like(src)
     ms_copy = time_fn(lambda: run(lambda: L.pisa_peak_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, st)), reps)
     ok = bool(torch.equal(src, dst))
+    def read4():  # four back-to-back passes over the 1 GiB buffer (larger than the 256 MB MALL)
+        for _ in range(4):
+            run(lambda: L.pisa_peak_read(src.data_ptr(), COPY_BYTES, out.data_ptr(), st))
+    ms_read = time_fn(read4, reps)
+    rows_per_wave = 512                             # 2048 x 4 waves x 512 rows of 1 KiB = 4 GiB
+    ms_gather = time_fn(lambda: run(lambda: L.pisa_peak_gather(src.data_ptr(), COPY_BYTES, out.data_ptr(), blocks,
+                                                               rows_per_wave, 12345, st)), reps)
+    gathered = blocks * 4 * rows_per_wave * 1024
     del src, dst, out
     torch.cuda.empty_cache()
     return dict(exp_gps=exps / (ms_exp * 1e-3) / 1e9,
@@ -287,9 +300,13 @@ def unit_peaks(reps: int = 5):
                 mix_exp_gps=mfmas * 64 / (ms_mix * 1e-3) / 1e9,
                 mix_over_mfma_time=ms_mix / ms_mfma,
                 copy_gbs=2 * COPY_BYTES / (ms_copy * 1e-3) / 1e9, copy_verified=ok,
+                read_gbs=4 * COPY_BYTES / (ms_read * 1e-3) / 1e9,
+                gather_gbs=gathered / (ms_gather * 1e-3) / 1e9,
                 how="exp: 8 independent chains x <- 2^-x per thread; mfma: 8 independent accumulators per wave; "
                     "mix: the two interleaved 1:1 in every wave; copy: 1 GiB read + 1 GiB written, 16-byte "
-                    "accesses; %d workgroups of 256 threads" % blocks)
+                    "accesses; read: the same 1 GiB read four times over; gather: 4 GiB of 1 KiB rows at hashed positions "
+                    "of that 1 GiB (one row per wave and load: the routers' per-entry query gathers); "
+                    "%d workgroups of 256 threads" % blocks)
 
 
 def copy_calibration():
@@ -357,7 +374,7 @@ def sample_positions(N, C, n):
 
 def cpu_baseline(P: Prefill, budget_s: float):
     """The oracle on the host cores: full pyramid build, then routing of a growing
-    evenly spaced sample of positions until about budget_s seconds of routing."""
+    evenly spaced sample of positions until one sample takes at least 0.8 * budget_s seconds."""
     import oracle  # test infrastructure: only this leg of the benchmark calls it
     w = P.w
     threads = max(1, min(len(os.sched_getaffinity(0)), 16))
@@ -373,9 +390,9 @@ def cpu_baseline(P: Prefill, budget_s: float):
         t0 = time.perf_counter()
         orc = oracle.route(opyr, Qs, [0] * len(t), t, w.K_top, causal=True, threads=threads)
         dt = time.perf_counter() - t0
-        if dt >= budget_s / 4 or n >= w.N:
+        if dt >= 0.8 * budget_s or n >= w.N:
             break
-        n = min(w.N, int(n * max(2.0, 0.5 * budget_s / max(dt, 1e-3))))
+        n = min(w.N, int(n * min(8.0, max(1.25, budget_s / max(dt, 1e-3)))))
     # routing cost per query position, weighted to the full sequence by the scored work
     full = workcount.route_work(w.B, w.N, w.H_kv, w.H_q // w.H_kv, w.d, w.C, w.g, w.K_top)
     samp = workcount.route_work(w.B, w.N, w.H_kv, w.H_q // w.H_kv, w.d, w.C, w.g, w.K_top, positions=t)
@@ -718,6 +735,8 @@ def main():
             extra[name] = prefill_extra(name, reps, with_attn=attn)
         log("extra decode")
         extra["decode"] = decode_bench(256)
+        # the decode router only reads: its gathered bytes against this run's read loop
+        extra["decode"]["route_frac_of_measured_read"] = extra["decode"]["route_hbm_gbs"] / peaks["read_gbs"]
         extra["paper_shape_sweep"] = dict(
             shape="B=1, H_q=32, H_kv=2, d=64, C=64, g=2, K_top=8, causal, random bf16 Q/K (seed 40)",
             by_N=paper_sweep(check=not args.no_cpu))

@@ -93,6 +93,55 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const uint4* __restrict_
     for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) dst[i] = src[i];
 }
 
+// Every thread folds its 16-byte pieces of src[0, n) (grid-stride) into one word.
+__global__ __launch_bounds__(kThreads) void read_kernel(const uint4* __restrict__ src, size_t n, float* out)
+{
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    uint32_t acc = 0;
+    size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {  // four loads in flight per thread
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n; i += stride) {
+        const uint4 a = src[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    out[blockIdx.x * kThreads + threadIdx.x] = (float)(acc & 0xffffu);
+}
+
+// 32-bit integer hash (the "lowbias32" xorshift-multiply mix published by C. Wellons).
+__device__ __forceinline__ uint32_t mix32(uint32_t x)
+{
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+// Every wave reads rows_per_wave rows of 1 KiB (64 lanes x 16 bytes), each row drawn by
+// hashing (seed, wave, k) into [0, nrows), eight rows in flight at a time.
+__global__ __launch_bounds__(kThreads) void gather_kernel(const uint4* __restrict__ src, uint32_t nrows,
+                                                          int rows_per_wave, uint32_t seed, float* out)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    uint32_t acc = 0;
+    for (int k = 0; k < rows_per_wave; k += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t r = mix32(seed ^ mix32(wave * (uint32_t)rows_per_wave + (uint32_t)(k + u))) % nrows;
+            v[u] = src[(size_t)r * 64 + lane];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    out[blockIdx.x * kThreads + threadIdx.x] = (float)(acc & 0xffffu);
+}
+
 int launched(void) { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
 }  // namespace
@@ -117,6 +166,25 @@ int pisa_peak_mix(float* out, int32_t blocks, int32_t iters, void* stream)
 {
     if (!out || blocks < 1 || iters < 1) return -1;
     hipLaunchKernelGGL(mix_loop_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, out, iters);
+    return launched();
+}
+
+int pisa_peak_read(const void* src, size_t bytes, float* out, void* stream)
+{
+    if (!src || !out || bytes == 0 || (bytes & 15) || ((uintptr_t)src & 15)) return -1;
+    hipLaunchKernelGGL(read_kernel, dim3(2048), dim3(kThreads), 0, (hipStream_t)stream, (const uint4*)src, bytes / 16,
+                       out);
+    return launched();
+}
+
+int pisa_peak_gather(const void* src, size_t bytes, float* out, int32_t blocks, int32_t rows_per_wave,
+                     uint32_t seed, void* stream)
+{
+    if (!src || !out || bytes < 1024 || (bytes >> 10) > 0xffffffffu || ((uintptr_t)src & 15) || blocks < 1 ||
+        rows_per_wave < 8 || (rows_per_wave & 7))
+        return -1;
+    hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, (const uint4*)src,
+                       (uint32_t)(bytes >> 10), rows_per_wave, seed, out);
     return launched();
 }
 

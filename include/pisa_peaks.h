@@ -21,6 +21,15 @@
  *                   exponentials of the leaf scoring of a 16 x 64 logit tile).
  *   pisa_peak_copy: dst[i] = src[i] for bytes (a multiple of 16, 16-byte
  *                   aligned pointers) with 16-byte loads and stores.
+ *   pisa_peak_read: reads src[0, bytes) once with 16-byte loads (bytes a
+ *                   multiple of 16, src 16-byte aligned); out holds 2048 * 256
+ *                   floats.
+ *   pisa_peak_gather: every wave reads rows_per_wave (a multiple of 8, >= 8)
+ *                   rows of 1 KiB at hashed positions among the bytes / 1024
+ *                   whole rows of src (16-byte aligned, bytes >= 1024 and
+ *                   below 2^42): blocks * 4 * rows_per_wave KiB read, the
+ *                   access pattern of the routers' per-entry query gathers
+ *                   (G_Q = 4 heads of d = 128 bf16 per entry).
  */
 #ifndef PISA_PEAKS_H
 #define PISA_PEAKS_H
@@ -36,6 +45,9 @@ int pisa_peak_exp(float* out, int32_t blocks, int32_t iters, void* stream);
 int pisa_peak_mfma(float* out, int32_t blocks, int32_t iters, void* stream);
 int pisa_peak_mix(float* out, int32_t blocks, int32_t iters, void* stream);
 int pisa_peak_copy(const void* src, void* dst, size_t bytes, void* stream);
+int pisa_peak_read(const void* src, size_t bytes, float* out, void* stream);
+int pisa_peak_gather(const void* src, size_t bytes, float* out, int32_t blocks, int32_t rows_per_wave,
+                     uint32_t seed, void* stream);
 
 #ifdef __cplusplus
 }

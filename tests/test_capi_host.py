@@ -42,6 +42,18 @@ def test_library_exports_every_declared_function(lib):
     assert lib.pisa_abi_version() == 1
 
 
+def test_peaks_library_exports_every_declared_function():
+    """The unit-throughput loops timed beside the kernels (include/pisa_peaks.h)."""
+    from hierarchical_top_amd import build
+    if not build.PEAKS_LIB.exists():
+        pytest.skip("libpisa_peaks.so is not built")
+    text = re.sub(r"/\*.*?\*/", "", (ROOT / "include" / "pisa_peaks.h").read_text(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(pisa_peak_[a-z0-9_]+)\s*\(", text)))
+    assert {"pisa_peak_copy", "pisa_peak_read", "pisa_peak_gather"} <= set(names)
+    peaks = ctypes.CDLL(str(build.PEAKS_LIB))
+    assert [n for n in names if not hasattr(peaks, n)] == []
+
+
 def test_status_strings(lib):
     for s in (OK, EINVAL, EUNSUPPORTED, ENOSPACE, -4):
         assert lib.pisa_status_str(s)
