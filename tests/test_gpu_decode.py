@@ -72,6 +72,31 @@ def test_decode_small_ragged_lengths():
     assert lens[0] == N0 + steps and checked == steps * B
 
 
+@pytest.mark.parametrize("g,K_top", [(4, 16), (2, 32)])
+def test_decode_wide_candidate_lists(g, K_top):
+    """g * K_top = 64 candidates per level (one per lane of the decode program), d=128, C=64,
+    four sequences of ragged lengths (one below K_top leaf blocks: every leaf kept)."""
+    B, H_q, H, d, C = 4, 8, 2, 128, 64
+    lens = [5000, 4097, 1300, 700]
+    cap = max(lens)
+    gen = torch.Generator().manual_seed(47 + g)
+    K = torch.randn(B, cap, H, d, generator=gen).to(torch.bfloat16).cuda()
+    q = torch.randn(B, H_q, d, generator=gen).to(torch.bfloat16).cuda()
+    pyr = pisa.Pyramid(B, H, d, C, g, cap)
+    seqlen = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    for b in range(B):  # one build per length: sequence b's pyramid covers its own prefix
+        one = pisa.Pyramid(1, H, d, C, g, cap)
+        one.build(K[b:b + 1].contiguous(), lens[b])
+        for l in range(1, len(oracle.levels(lens[b], C, g))):
+            pyr.level(l)[b].copy_(one.level(l)[0])
+    print("g", g, "K_top", K_top, "lens", lens, flush=True)
+    idx, score = pisa.route_decode(pyr, q, K, seqlen, K_top, with_score=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        st, _ = _check_route(K, q, b, lens[b], C, g, K_top, idx, score)
+        print("seq", b, st)
+
+
 @pytest.mark.parametrize("kind", ["mean", "mean_var"])
 def test_decode_pisa1_pisa2_scores(kind):
     """The decode router with the PISA-1 / PISA-2 block scores (section 4.4) against the

@@ -149,6 +149,7 @@ def test_route_matches_oracle(mode, case, K_top, causal, sample):
     ("p16k", 8, True, None),
     ("sparse64k", 8, True, 600),      # sparse upper levels
     ("ragged_big", 8, True, 600),     # tail nodes missing grandchildren at sparse levels
+    ("g2_wide", 32, True, 600),       # g=2, 64 candidates per item at every ranked level
 ])
 def test_route_pisa1_pisa2_match_oracle(kind, case, K_top, causal, sample, mode):
     """PISA-1 (mean logit) and PISA-2 (mean + half the variance) block scores of section 4.4,
