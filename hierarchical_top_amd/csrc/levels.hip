@@ -204,10 +204,16 @@ __device__ __forceinline__ void select_item(const SelectArgs& a, int64_t bh, int
 #pragma unroll
         for (int k = 0; k < 3; ++k)
             if (k < nF) put((int)F[k], INFINITY);
+        // a candidate whose score is NaN (non-finite inputs) never enters the list, so fewer
+        // than R picks are possible only then: keep the real ones and pad with -1
+        int npick = 0;
 #pragma unroll
         for (int q = 0; q < KMAX; ++q)
-            if (q < R) put(bi[q], bu[q]);
-        nkept = K;
+            if (q < R && bi[q] != 0x7fffffff) {
+                put(bi[q], bu[q]);
+                ++npick;
+            }
+        nkept = nF + npick;
     }
 
     if (l == 1) {

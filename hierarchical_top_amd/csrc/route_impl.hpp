@@ -344,10 +344,13 @@ struct RouteQuery {
                 }
                 __syncthreads();
                 const float u = scored ? s_u[rk] : 0.f;
-                key = forced ? INFINITY : (scored ? u : -INFINITY);
-                int sid = cid >= 0 ? cid : (0x7fffffff - lane);
-                rank_sort(key, sid, ballot(cid >= 0));
-                nkept = a.K_top;
+                // a NaN score (non-finite inputs) drops its candidate, as in the other selects
+                const bool live = cid >= 0 && !(scored && !(u == u));
+                key = forced ? INFINITY : (scored && live ? u : -INFINITY);
+                int sid = live ? cid : (0x7fffffff - lane);
+                const uint64_t lv = ballot(live);
+                rank_sort(key, sid, lv);
+                nkept = __popcll(lv) < a.K_top ? __popcll(lv) : a.K_top;
                 cid = lane < nkept ? sid : -1;
                 if (lane >= nkept) key = -INFINITY;
                 __syncthreads();  // s_sid / s_u are rewritten at the next level

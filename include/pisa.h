@@ -30,6 +30,10 @@
  *   Other shapes return PISA_EUNSUPPORTED.
  * - Calls do not share mutable state; two calls may run concurrently on
  *   different streams if they do not write the same buffers.
+ * - Selection is defined for finite inputs. With NaN or inf in Q or K every
+ *   router still returns valid rows (ascending, causal, -1 padded, forced
+ *   blocks present); a candidate whose score is NaN is never picked, so a row
+ *   may then hold fewer than K_top blocks.
  */
 #ifndef PISA_H
 #define PISA_H
