@@ -183,7 +183,7 @@ int levels_top(int64_t N, int C, int g, int K_top)
 }
 
 struct LevelsLayout {
-    size_t kept0, kept1, flags, u, u_pair, counts, offsets, chunk_off, chunk_cl, block_sums, entries, total;
+    size_t kept0, kept1, flags, u, u_pair, counts, offsets, chunk_off, chunk_cl, block_sums, entries, rows_hl, total;
     int64_t cnt_total, max_clusters;
     int64_t cnt_off[PISA_MAX_LEVELS + 2];
     int l_top;
@@ -222,6 +222,8 @@ LevelsLayout levels_layout(const pisa_pyramid* p, int64_t N, int K_top)
     w.chunk_cl = o; o = al(o + (size_t)(items * K_top / pisa::kRegChunk + w.max_clusters + 1) * 4);
     w.block_sums = o; o = al(o + (size_t)2 * (w.max_clusters / 1024 + 2) * 4);
     w.entries = o; o = al(o + (size_t)items * K_top * 4);
+    // the upper levels' summaries as two bf16 terms (pisa::split_layout): 4 bytes per value
+    w.rows_hl = o; o = al(o + (size_t)pisa::split_layout(N, c_log2, g_log2, w.l_top, BH, p->d, nullptr) * 2);
     w.total = o;
     return w;
 }
@@ -465,6 +467,7 @@ pisa_status pisa_route_prefill_scored(const pisa_pyramid* p, const void* Q, cons
         la.chunk_cl = (int32_t*)(base + w.chunk_cl);
         la.block_sums = (int32_t*)(base + w.block_sums);
         la.entries = (int32_t*)(base + w.entries);
+        la.rows_hl = base + w.rows_hl;
         la.l_top = w.l_top;
         hipError_t e = launch_levels(la, dti, p->d, st);
         return e == hipSuccess ? ok() : hip_fail(e, "pisa_route_prefill (levels)");

@@ -570,6 +570,38 @@ static hipError_t launch_select(const SelectArgs& sa, int K_top, hipStream_t s)
     return hipGetLastError();
 }
 
+// Split of the summaries of levels l_lo .. l_hi into the two bf16 terms the MFMA operands take
+// (split_layout): one thread per 8 values, in level order. The dense and sparse upper-level
+// kernels then read both terms with plain loads instead of splitting the same rows in every
+// workgroup.
+struct SplitArgs {
+    PyrArgs p;
+    int l_lo, l_hi;
+    int64_t nodes[PISA_MAX_LEVELS + 2];   // nodes of level l over the routed tokens
+    int64_t first[PISA_MAX_LEVELS + 2];   // first 8-value piece of level l; first[l_hi + 1] = total
+    int64_t off[PISA_MAX_LEVELS + 2];     // bf16 element offset of level l in out
+    void* out;
+};
+
+__global__ __launch_bounds__(256) void split_kernel(SplitArgs a)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.first[a.l_hi + 1]) return;
+    int l = a.l_lo;
+    while (l < a.l_hi && i >= a.first[l + 1]) ++l;
+    const int d8 = a.p.d >> 3;
+    const int64_t k = i - a.first[l];
+    const int64_t row = k / d8;  // over [B * H][nodes]
+    const int c8 = (int)(k - row * d8);
+    const int64_t bh = row / a.nodes[l], r = row - bh * a.nodes[l];
+    const float* src = a.p.buf + a.p.off[l] + (bh * a.p.M_cap[l] + r) * a.p.d + 8 * c8;
+    bf16* dst = reinterpret_cast<bf16*>(a.out) + a.off[l] + row * 2 * a.p.d + 8 * c8;
+    bf16x8 hi, lo;
+    split8(load8f(src), hi, lo);
+    *reinterpret_cast<bf16x8*>(dst) = hi;
+    *reinterpret_cast<bf16x8*>(dst + a.p.d) = lo;
+}
+
 hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
 {
     const RouteArgs& r = a.r;
@@ -594,6 +626,32 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
     hipLaunchKernelGGL(fill_zero_lv_kernel, dim3(256), dim3(256), 0, s, a.counts, 2 * a.cnt_total);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     stage_mark(PISA_STAGE_CLUSTER, true, s);
+
+    // the summaries the upper levels score against, as two bf16 terms (split_layout)
+    int64_t hl_off[PISA_MAX_LEVELS + 2] = {};
+    split_layout(N, p.c_log2, p.g_log2, a.l_top, BH, d, hl_off);
+    auto hl_rows = [&](int lv) { return reinterpret_cast<const uint16_t*>(a.rows_hl) + hl_off[lv]; };
+    auto hl_h_stride = [&](int lv) { return nodes_n(N, p.c_log2, p.g_log2, lv) * 2 * d; };
+    if (a.l_top >= 2) {
+        SplitArgs sp;
+        memset(&sp, 0, sizeof(sp));
+        sp.p = p;
+        sp.l_lo = 1;
+        sp.l_hi = a.l_top - 1;
+        int64_t pieces = 0;
+        for (int lv = 1; lv <= sp.l_hi; ++lv) {
+            sp.nodes[lv] = nodes_n(N, p.c_log2, p.g_log2, lv);
+            sp.first[lv] = pieces;
+            sp.off[lv] = hl_off[lv];
+            pieces += BH * sp.nodes[lv] * (d / 8);
+        }
+        sp.first[sp.l_hi + 1] = pieces;
+        sp.out = a.rows_hl;
+        stage_mark(PISA_STAGE_UPPER, false, s);
+        hipLaunchKernelGGL(split_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, sp);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        stage_mark(PISA_STAGE_UPPER, true, s);
+    }
 
     // the level above the first ranked one: every eligible node is kept
     int cur = 0;
@@ -644,9 +702,9 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
             memset(&da, 0, sizeof(da));
             da.Q = r.Q; da.N = N; da.B = p.B; da.H = p.H; da.H_q = r.H_q; da.G = r.G; da.K_top = r.K_top; da.g = p.g;
             da.causal = r.causal;
-            da.rows = p.buf + p.off[l - 1];
-            da.rows_b_stride = (int64_t)p.H * p.M_cap[l - 1] * d;
-            da.rows_h_stride = p.M_cap[l - 1] * d;
+            da.rows_hl = hl_rows(l - 1);
+            da.rows_hl_h_stride = hl_h_stride(l - 1);
+            da.rows_hl_b_stride = (int64_t)p.H * da.rows_hl_h_stride;
             da.rows_limit = nodes_n(N, p.c_log2, p.g_log2, l - 1);
             da.par_span_log2 = p.c_log2 + l * p.g_log2;
             da.M_par = nodes_n(N, p.c_log2, p.g_log2, l + 1);
@@ -655,9 +713,9 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
             da.u = a.u;
             if (dense_pair(N, p.c_log2, p.g_log2, l)) {
                 // level l - 1 rides along: rows of level l - 2, parents = level-l nodes
-                da.rows2 = p.buf + p.off[l - 2];
-                da.rows2_b_stride = (int64_t)p.H * p.M_cap[l - 2] * d;
-                da.rows2_h_stride = p.M_cap[l - 2] * d;
+                da.rows2_hl = hl_rows(l - 2);
+                da.rows2_hl_h_stride = hl_h_stride(l - 2);
+                da.rows2_hl_b_stride = (int64_t)p.H * da.rows2_hl_h_stride;
                 da.rows2_limit = nodes_n(N, p.c_log2, p.g_log2, l - 2);
                 da.par2_span_log2 = p.c_log2 + (l - 1) * p.g_log2;
                 da.M_par2 = nodes_n(N, p.c_log2, p.g_log2, l);
@@ -739,6 +797,9 @@ hipError_t launch_levels(const LevelsArgs& a, int dtype, int d, hipStream_t s)
             sc2.row_stride = d;
             sc2.rows_limit = nodes_n(N, p.c_log2, p.g_log2, l - 1);
             sc2.rc = p.g;
+            sc2.rows_hl = hl_rows(l - 1);
+            sc2.rows_hl_h_stride = hl_h_stride(l - 1);
+            sc2.rows_hl_b_stride = (int64_t)p.H * sc2.rows_hl_h_stride;
         }
         sc2.qc = qc;
         sc2.n_clusters = n_clusters;

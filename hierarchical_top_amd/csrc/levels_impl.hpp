@@ -504,7 +504,7 @@ __global__ __launch_bounds__(64 * kRegWaves) void score_reg_kernel(ScoreArgs a)
 // nodes) stream through LDS in batches of 4 row tiles as two bf16 terms; a row
 // tile holds 16 / g^2 parents whose g children are the candidates. A per-query
 // table maps each parent to its slot in the query's kept list (0xFF = not
-// kept); only kept parents' candidates are written to u. With rows2 set, the
+// kept); only kept parents' candidates are written to u. With rows2_hl set, the
 // workgroup then scores level l - 1 from the query tiles it already holds: the
 // children of every eligible level-l node, written to u2 by node id (the kept
 // level-l nodes are chosen after this kernel).
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
     // one level: rows (level l-1 summaries of the np eligible parents, rows_limit of them exist)
     // stream through LDS; write(ct, P, j, score, exists) stores candidate j of parent P for the
     // queries of column tile ct
-    auto pass = [&](const float* rb, int64_t rows_limit, int np, auto write) {
+    auto pass = [&](const bf16* rh, int64_t rows_limit, int np, auto write) {
         const int nrows = np * RP;
         const int nrt = (nrows + 15) / 16;
         for (int kb = 0; kb < nrt; kb += kDenseBatch) {
@@ -582,8 +582,9 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
                 const int r = i / (D / 8), c8 = i % (D / 8);
                 const int64_t row = (int64_t)kb * 16 + r;
                 const bool ok = row < nrows && row < rows_limit;
-                bf16x8 vh, vl;
-                Src<float>::load(rb + (ok ? row : 0) * D + 8 * c8, ok, vh, vl);
+                // the row's two terms, split once per call (split_kernel)
+                const bf16* hp = rh + (ok ? row : 0) * (2 * D) + 8 * c8;
+                const bf16x8 vh = ok ? load8h(hp) : zero8h(), vl = ok ? load8h(hp + D) : zero8h();
                 *reinterpret_cast<bf16x8*>(s_rows + r * LDW + 8 * c8) = vh;
                 *reinterpret_cast<bf16x8*>(s_rows + (kDenseBatch * 16 + r) * LDW + 8 * c8) = vl;
             }
@@ -628,17 +629,20 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a)
         }
     };
     // level l: candidates of the kept parents, by slot
-    pass(a.rows + (int64_t)b * a.rows_b_stride + (int64_t)h * a.rows_h_stride, a.rows_limit, npar,
+    pass(reinterpret_cast<const bf16*>(a.rows_hl) + (int64_t)b * a.rows_hl_b_stride + (int64_t)h * a.rows_hl_h_stride,
+         a.rows_limit, npar,
          [&](int ct, int P, int j, float v, bool exists) {
              const int slot = P < npar ? s_slot[qloc[ct] * npar + P] : 0xFF;
              if (qok[ct] && head == 0 && term == 0 && exists && slot != 0xFF)
                  a.u[(bh * a.N + t0 + qloc[ct]) * ucols + slot * GB + j] = v;
          });
-    if (a.rows2) {
+    if (a.rows2_hl) {
         // level l - 1 in the same pass: the children of every eligible level-l node, by node id
         const int64_t pm2 = a.causal ? tl >> a.par2_span_log2 : a.M_par2 - 1;
         const int npar2 = (int)((pm2 < a.M_par2 - 1 ? pm2 : a.M_par2 - 1) + 1);
-        pass(a.rows2 + (int64_t)b * a.rows2_b_stride + (int64_t)h * a.rows2_h_stride, a.rows2_limit, npar2,
+        pass(reinterpret_cast<const bf16*>(a.rows2_hl) + (int64_t)b * a.rows2_hl_b_stride +
+                 (int64_t)h * a.rows2_hl_h_stride,
+             a.rows2_limit, npar2,
              [&](int ct, int P, int j, float v, bool exists) {
                  if (qok[ct] && head == 0 && term == 0 && exists)
                      a.u2[(bh * a.N + t0 + qloc[ct]) * a.u2_cols + P * GB + j] = v;
@@ -987,10 +991,14 @@ __global__ __launch_bounds__(256) void upper_ring_kernel(ScoreArgs a)
     {
         const int r = lane & 15;
         const bool ok = r < lim_rows;
-        const float* rp = reinterpret_cast<const float*>(a.rows) + (int64_t)b * a.rows_b_stride +
-                          (int64_t)h * a.rows_h_stride + (row0 + (ok ? r : 0)) * a.row_stride + 8 * lg;
+        // P's grandchildren as two bf16 terms, split once per call (split_kernel)
+        const bf16* rp = reinterpret_cast<const bf16*>(a.rows_hl) + (int64_t)b * a.rows_hl_b_stride +
+                         (int64_t)h * a.rows_hl_h_stride + (row0 + (ok ? r : 0)) * (2 * D) + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) Src<float>::load(rp + 32 * s, ok, ah[s], al[s]);
+        for (int s = 0; s < KS; ++s) {
+            ah[s] = ok ? load8h(rp + 32 * s) : zero8h();
+            al[s] = ok ? load8h(rp + D + 32 * s) : zero8h();
+        }
     }
     // the A rows are in flight ahead of the ring's first fetches: a wait for a tile (exact count
     // of the fetches issued after it) also covers every older load

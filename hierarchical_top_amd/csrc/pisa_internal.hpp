@@ -164,6 +164,10 @@ struct ScoreArgs {
     const int32_t* chunk_cl;  // [chunks] cluster of each chunk
     const int32_t* entries;   // (t << 6) | slot
     float* u;                 // [B][H][N][K_top * g]
+    // the rows of an upper level as two bf16 terms (split_layout), read by upper_ring_kernel:
+    // row r of (b, h) at rows_hl + b * rows_hl_b_stride + h * rows_hl_h_stride + r * 2 d
+    const void* rows_hl;
+    int64_t rows_hl_b_stride, rows_hl_h_stride;
 };
 
 // Dense scoring of an upper level: every query tile scores the children of
@@ -215,12 +219,29 @@ inline int64_t dense_pair_max_cols(int64_t n, int c_log2, int g_log2, int l_top)
     return cols;
 }
 
+// The level router splits the fp32 summaries of levels 1 .. l_top - 1 once per call into two
+// bf16 terms (hi = the value rounded to bf16, lo = the rest rounded to bf16, as the MFMA
+// operands take them): level l holds rows [B * H][nodes(n, l)][hi d | lo d] at off[l] bf16
+// elements, each level 256-byte aligned. Returns the total bf16 elements (0 below l_top = 2).
+inline int64_t split_layout(int64_t n, int c_log2, int g_log2, int l_top, int64_t BH, int d, int64_t* off)
+{
+    int64_t e = 0;
+    for (int l = 1; l < l_top; ++l) {
+        if (off) off[l] = e;
+        e += BH * level_nodes(n, c_log2, g_log2, l) * 2 * d;
+        e = (e + 127) & ~(int64_t)127;
+    }
+    return e;
+}
+
 struct DenseArgs {
     const void* Q;            // [B][N][H_q][d]
     int64_t N;
     int B, H, H_q, G, K_top, g, causal;
-    const float* rows;        // level l-1 summaries of (b, h) at rows + b * rows_b_stride + h * rows_h_stride
-    int64_t rows_b_stride, rows_h_stride;
+    // level l-1 summaries of (b, h) as two bf16 terms (split_layout): row r at
+    // rows_hl + b * rows_hl_b_stride + h * rows_hl_h_stride + r * 2 d (bf16 elements)
+    const void* rows_hl;
+    int64_t rows_hl_b_stride, rows_hl_h_stride;
     int64_t rows_limit;       // level l-1 nodes that exist
     int par_span_log2;        // log2 of the tokens spanned by a level-(l+1) node
     int64_t M_par;            // level l+1 nodes that exist
@@ -229,8 +250,8 @@ struct DenseArgs {
     float* u;                 // [items][K_top * g]
     // optional second level l - 1 in the same pass over the queries (rows2 != null): the
     // candidates of every eligible level-l node, written to u2 by node id
-    const float* rows2;       // level l-2 summaries, strides and count as for rows
-    int64_t rows2_b_stride, rows2_h_stride, rows2_limit;
+    const void* rows2_hl;     // level l-2 summaries, layout as for rows_hl
+    int64_t rows2_hl_b_stride, rows2_hl_h_stride, rows2_limit;
     int par2_span_log2;       // log2 of the tokens spanned by a level-l node
     int64_t M_par2;           // level-l nodes that exist
     float* u2;                // [items][u2_cols]: column x = level l-1 node x
@@ -291,6 +312,7 @@ struct LevelsArgs {
     int32_t* chunk_cl;        // [max chunks]
     int32_t* block_sums;      // scan partials: 2 * (max clusters / 1024 + 1)
     int32_t* entries;
+    void* rows_hl;            // the summaries of levels 1 .. l_top - 1 as two bf16 terms (split_layout)
     int l_top;                // highest scored level (0: nothing is scored)
 };
 
