@@ -81,39 +81,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
         if (a.causal && kend > pos + 1) kend = pos + 1;
         if (kend <= k0) continue;  // no visible key in this block (uniform across the wave)
 
-        // Stage V^T: lane = key (lanes >= Cp idle); pairs of lanes write packed dwords.
-        {
-            const int key = lane;
-            const bool kok = key < Cp && k0 + key < kend;
-            const T* vp = vbase + (kok ? (k0 + key) : 0) * kstride;
+        // The block's loads are issued together, each at an address in the sequence (a masked
+        // key reads row 0): the K rows of the four 16-key tiles first, so that the S products
+        // wait for them only, then (bf16) the V rows, which go to LDS after the softmax; fp32
+        // values, two terms each, are loaded after the softmax to stay within the registers.
+        // A masked key's S entry is replaced by -inf (a select: whatever row 0 holds cannot leak)
+        // and its V row is written as zeros.
+        bf16x8 kh[4][KS], kl[4][KS];
 #pragma unroll
-            for (int j = 0; j < D / 8; ++j) {
-                bf16x8 vh, vl;
-                Src<T>::load(vp + 8 * j, kok, vh, vl);
+        for (int rt = 0; rt < 4; ++rt) {
+            const int rr = lane & 15;
+            const int key = 32 * (rt >> 1) + 8 * (rr >> 2) + 4 * (rt & 1) + (rr & 3);
+            const bool kok = rt < nrt && k0 + key < kend && key < C;
+            const T* kp = kbase + (kok ? (k0 + key) : 0) * kstride + 8 * (lane >> 4);
 #pragma unroll
-                for (int tp = 0; tp < TB; ++tp) {
-                    const bf16x8 v = tp == 0 ? vh : vl;
-                    const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
-                    uint32_t pw[4];
+            for (int s = 0; s < KS; ++s) Src<T>::load(kp + 32 * s, true, kh[rt][s], kl[rt][s]);
+        }
+        // V: lane = key (lanes >= Cp load row 0 and write nothing)
+        bf16x8 vh[D / 8], vl[D / 8];
+        const T* vp = vbase + ((lane < Cp && k0 + lane < kend) ? (k0 + lane) : 0) * kstride;
+        if constexpr (TB == 1) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) pw[q] = (uint32_t)__shfl_xor((int)w[q], 1, 64);
-                    if (key < Cp) {
-                        bf16* plane = s_vt + (size_t)tp * D * ldv;
-                        const bool even = (key & 1) == 0;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            // even lane: element 2q of itself (low) and of key+1 (high), row 8j+2q
-                            // odd lane : element 2q+1 of key-1 (low) and of itself (high), row 8j+2q+1
-                            const uint32_t mine = even ? (w[q] & 0xffffu) : (w[q] >> 16);
-                            const uint32_t other = even ? (pw[q] & 0xffffu) : (pw[q] >> 16);
-                            const uint32_t dw = even ? (mine | (other << 16)) : (other | (mine << 16));
-                            const int row = 8 * j + 2 * q + (even ? 0 : 1);
-                            const int c0 = even ? key : key - 1;
-                            *reinterpret_cast<uint32_t*>(plane + row * ldv + c0) = dw;
-                        }
-                    }
-                }
-            }
+            for (int j = 0; j < D / 8; ++j) Src<T>::load(vp + 8 * j, true, vh[j], vl[j]);
         }
 
         // S^T tiles
@@ -121,17 +110,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             if (rt < nrt) {
-                const int rr = lane & 15;
-                const int key = 32 * (rt >> 1) + 8 * (rr >> 2) + 4 * (rt & 1) + (rr & 3);
-                const bool kok = k0 + key < kend && key < C;
-                const T* kp = kbase + (kok ? (k0 + key) : 0) * kstride + 8 * (lane >> 4);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    bf16x8 kh, kl;
-                    Src<T>::load(kp + 32 * s, kok, kh, kl);
-                    acc = mfma(kh, qb[s], acc);
-                    if constexpr (TB == 2) acc = mfma(kl, qb[s], acc);
+                    acc = mfma(kh[rt][s], qb[s], acc);
+                    if constexpr (TB == 2) acc = mfma(kl[rt][s], qb[s], acc);
                 }
                 // output rows 4*(lane/16)+i are keys of this tile
 #pragma unroll
@@ -177,6 +160,39 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, int Cp)
             const float f = __shfl(fac, 4 * (lane >> 4) + i, 64);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) o[ct][i] *= f;
+        }
+        if constexpr (TB == 2) {
+#pragma unroll
+            for (int j = 0; j < D / 8; ++j) Src<T>::load(vp + 8 * j, true, vh[j], vl[j]);
+        }
+        // Stage V^T (V^T[d][key]): pairs of lanes write packed dwords; a masked key's half is 0.
+        {
+            const bool even = (lane & 1) == 0;
+            const int c0 = even ? lane : lane - 1;
+            const uint32_t mine_ok = k0 + lane < kend ? 0xffffu : 0u;
+            const uint32_t other_ok = k0 + (lane ^ 1) < kend ? 0xffffu : 0u;
+#pragma unroll
+            for (int j = 0; j < D / 8; ++j) {
+#pragma unroll
+                for (int tp = 0; tp < TB; ++tp) {
+                    const bf16x8 v = tp == 0 ? vh[j] : vl[j];
+                    const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+                    uint32_t pw[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) pw[q] = (uint32_t)__shfl_xor((int)w[q], 1, 64);
+                    bf16* plane = s_vt + (size_t)tp * D * ldv;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        // even lane: element 2q of itself (low) and of key+1 (high), row 8j+2q
+                        // odd lane : element 2q+1 of key-1 (low) and of itself (high), row 8j+2q+1
+                        const uint32_t mine = (even ? (w[q] & 0xffffu) : (w[q] >> 16)) & mine_ok;
+                        const uint32_t other = (even ? (pw[q] & 0xffffu) : (pw[q] >> 16)) & other_ok;
+                        const uint32_t dw = even ? (mine | (other << 16)) : (other | (mine << 16));
+                        const int row = 8 * j + 2 * q + (even ? 0 : 1);
+                        if (lane < Cp) *reinterpret_cast<uint32_t*>(plane + row * ldv + c0) = dw;
+                    }
+                }
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
