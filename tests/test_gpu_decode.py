@@ -97,6 +97,37 @@ def test_decode_wide_candidate_lists(g, K_top):
         print("seq", b, st)
 
 
+@pytest.mark.parametrize("g,K_top,C,lens", [
+    (2, 8, 64, [20000, 9000, 2500, 600]),   # six ranked levels at 20000; 600: only the leaf
+    (8, 8, 32, [40000, 12000, 3000]),      # 64 candidates of 8 children per ranked upper level
+    (16, 4, 16, [30000, 5000]),            # g = 16: a candidate's 16 children fill one tile
+])
+def test_decode_branching_factors(g, K_top, C, lens):
+    """The decode router against the oracle for branching factors 2, 8 and 16 (the other
+    decode tests take g = 4 or g = 2 with K_top = 32), leaf blocks of 16, 32 and 64 keys, and
+    lengths from one ranked level (the leaf) to six."""
+    B, H_q, H, d = len(lens), 8, 2, 128
+    cap = max(lens)
+    gen = torch.Generator().manual_seed(53 + g)
+    K = torch.randn(B, cap, H, d, generator=gen).to(torch.bfloat16).cuda()
+    q = torch.randn(B, H_q, d, generator=gen).to(torch.bfloat16).cuda()
+    pyr = pisa.Pyramid(B, H, d, C, g, cap)
+    seqlen = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    for b in range(B):
+        one = pisa.Pyramid(1, H, d, C, g, cap)
+        one.build(K[b:b + 1].contiguous(), lens[b])
+        for l in range(1, len(oracle.levels(lens[b], C, g))):
+            pyr.level(l)[b].copy_(one.level(l)[0])
+    print("g", g, "K_top", K_top, "C", C, "lens", lens, flush=True)
+    idx, score = pisa.route_decode(pyr, q, K, seqlen, K_top, with_score=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        M = oracle.levels(lens[b], C, g)
+        ranked = [l for l in range(1, len(M)) if M[l] > K_top]
+        st, _ = _check_route(K, q, b, lens[b], C, g, K_top, idx, score)
+        print("seq", b, "ranked levels", ranked, st)
+
+
 @pytest.mark.parametrize("kind", ["mean", "mean_var"])
 def test_decode_pisa1_pisa2_scores(kind):
     """The decode router with the PISA-1 / PISA-2 block scores (section 4.4) against the
