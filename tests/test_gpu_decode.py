@@ -179,6 +179,33 @@ def test_decode_first_level_growth_and_short_sequences():
             _check_route(K, q, b, n, C, g, K_top, idx, score)
 
 
+@pytest.mark.parametrize("C,g,N0,dtype", [
+    (16, 2, 8192 - 6, torch.bfloat16),     # ten levels, eleven from 8193 on
+    (16, 16, 65536 - 6, torch.bfloat16),   # g = 16: four levels, five from 65537 on
+    (32, 8, 131072 - 6, torch.bfloat16),   # g = 8: the sixth level appears at 131073
+    (64, 4, 4096 - 6, torch.float32),      # fp32 keys
+])
+def test_append_equals_rebuild_deep_pyramids(C, g, N0, dtype):
+    """Appending tokens one at a time across a level-count boundary leaves every level equal,
+    bit for bit, to a fresh build: branching factors 2, 16 and 8 with paths of up to eleven
+    levels, and fp32 keys."""
+    B, H, d, steps = 2, 2, 64, 12
+    cap = N0 + steps
+    gen = torch.Generator().manual_seed(61 + g)
+    K = torch.randn(B, cap, H, d, generator=gen).to(dtype).cuda()
+    pyr = pisa.Pyramid(B, H, d, C, g, cap)
+    pyr.build(K, N0)
+    print("C", C, "g", g, "levels at", N0, len(oracle.levels(N0, C, g)) - 1, "at", cap,
+          len(oracle.levels(cap, C, g)) - 1, flush=True)
+    for n in range(N0 + 1, cap + 1):
+        pyr.append(K, torch.full((B,), n, dtype=torch.int64, device="cuda"))
+        if n in (N0 + 1, N0 + 6, N0 + 7, cap):
+            torch.cuda.synchronize()
+            for b in range(B):
+                err = _rebuild_equal(pyr, K, b, n)
+                assert err is None, "n=%d b=%d: %s" % (n, b, err)
+
+
 def test_decode_full_size_sampled():
     """The decode workload (32 sequences, 262144-token caches, 32 / 8 heads, d=128,
     C=64, g=4, K_top=8): three appended tokens; sequences 0, 17, 31 checked
